@@ -1,0 +1,363 @@
+"""Pins of the fp64 CPU oracle against what the pages and the mathematics fix.
+
+Each check is something other than the oracle itself: the dense softmax
+attention definition evaluated with a library matmul, the skip criterion of
+the BLASST pages evaluated non-incrementally (closed form of the running
+max), the dropped-mass bound that follows from the criterion, a hand-worked
+example with closed-form outputs, and invariants (monotonicity in lambda,
+GQA = MHA with repeated KV, split merge = single pass over the kept keys).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bruteforce import (block_decisions, dense_probs, masked_softmax_attention,
+                        prefill_mask, scores)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(rng, *shape, std=1.0):
+    return rng.standard_normal(shape) * std
+
+
+def _prefill_case(seed, B=1, Hq=2, Hkv=1, L=200, d=16, dv=12, qstd=1.5, blocky=0):
+    """Gaussian q, k, v; with ``blocky`` > 0 the keys of every run of ``blocky``
+    positions are scaled by one factor in [0.05, 1] (the first run by 2), which
+    makes whole blocks cold or hot as the skip test needs."""
+    rng = np.random.default_rng(seed)
+    q = _rand(rng, B, Hq, L, d, std=qstd)
+    k = _rand(rng, B, Hkv, L, d, std=qstd)
+    v = _rand(rng, B, Hkv, L, dv)
+    if blocky:
+        nb = -(-L // blocky)
+        f = rng.uniform(0.05, 1.0, size=(B, Hkv, nb))
+        f[..., 0] = 2.0
+        k = k * np.repeat(f, blocky, axis=2)[..., :L, None]
+    return q, k, v
+
+
+def _lam_at(gap, qtl):
+    """A lambda that puts ln(lambda) at quantile ``qtl`` of the finite gaps."""
+    fg = gap[np.isfinite(gap)]
+    return float(min(0.999, math.exp(np.quantile(fg, qtl) + 1e-6)))
+
+
+# ---------------------------------------------------------------- dense limit
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("L,tq,bk", [(200, 64, 64), (130, 32, 64), (64, 64, 64), (1, 64, 64), (97, 16, 8)])
+def test_prefill_lambda0_is_dense_softmax(causal, L, tq, bk):
+    """lambda = 0 never skips: the oracle must be plain softmax attention (<= 1e-10)."""
+    q, k, v = _prefill_case(7 + L, B=2, Hq=4, Hkv=2, L=L)
+    r = oracle.prefill(q, k, v, causal=causal, lam=0.0, tile_q=tq, block_k=bk)
+    scale = 1 / math.sqrt(q.shape[-1])
+    mask = prefill_mask(L, causal)
+    for b in range(2):
+        for h in range(4):
+            S = scores(q[b, h], k[b, h // 2], scale)
+            ref = masked_softmax_attention(S, mask, v[b, h // 2])
+            np.testing.assert_allclose(r["o"][b, h], ref, rtol=0, atol=1e-10)
+    assert r["skipped"] == 0
+    assert np.all((r["skip"] == 0) | (r["skip"] == 255))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40])
+def test_decode_lambda0_is_dense_softmax(splits):
+    rng = np.random.default_rng(11 + splits)
+    B, Hq, Hkv, Lmax, d, dv = 3, 6, 2, 300, 20, 10
+    q = _rand(rng, B, Hq, d, std=1.5)
+    k = _rand(rng, B, Hkv, Lmax, d, std=1.5)
+    v = _rand(rng, B, Hkv, Lmax, dv)
+    lens = np.array([300, 1, 129])
+    r = oracle.decode(q, k, v, lens, lam=0.0, block_k=64, num_splits=splits)
+    scale = 1 / math.sqrt(d)
+    for b in range(B):
+        for h in range(Hq):
+            S = scores(q[b, h][None], k[b, h // 3], scale)
+            mask = np.arange(Lmax)[None] < lens[b]
+            ref = masked_softmax_attention(S, mask, v[b, h // 3])[0]
+            np.testing.assert_allclose(r["o"][b, h], ref, rtol=0, atol=1e-10)
+    assert r["skipped"] == 0
+
+
+# ------------------------------------------------------------ skip decisions
+def _prefill_brute_decisions(q, k, lam, causal, tq, bk):
+    B, Hq, L, d = q.shape
+    G = Hq // k.shape[1]
+    nqt, nkb = -(-L // tq), -(-L // bk)
+    skip = np.zeros((B, Hq, nqt, nkb), np.uint8)
+    gap = np.zeros((B, Hq, nqt, nkb))
+    mask = prefill_mask(L, causal)
+    scale = 1 / math.sqrt(d)
+    cols = [(j * bk, min(L, (j + 1) * bk)) for j in range(nkb)]
+    for b in range(B):
+        for h in range(Hq):
+            S = scores(q[b, h], k[b, h // G], scale)
+            for t in range(nqt):
+                rows = slice(t * tq, min(L, (t + 1) * tq))
+                s, g = block_decisions(S[rows], mask[rows], None, cols, lam)
+                skip[b, h, t] = s
+                gap[b, h, t] = g
+    return skip, gap
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_decisions_match_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(40, 260))
+    tq = int(rng.choice([16, 32, 64]))
+    bk = int(rng.choice([8, 16, 32]))
+    causal = bool(seed % 2)
+    q, k, v = _prefill_case(seed, B=1, Hq=2, Hkv=1, L=L, d=8, dv=4, qstd=2.0, blocky=bk)
+    # lambda at a random quantile of the brute-force gaps, so that both outcomes occur
+    _, g0 = _prefill_brute_decisions(q, k, 0.0, causal, tq, bk)
+    fg = g0[np.isfinite(g0)]
+    lam = float(min(0.999, math.exp(np.quantile(fg, rng.uniform(0.2, 0.8)) + 1e-6)))
+    r = oracle.prefill(q, k, v, causal=causal, lam=lam, tile_q=tq, block_k=bk)
+    skip, gap = _prefill_brute_decisions(q, k, lam, causal, tq, bk)
+    fin = np.isfinite(gap)
+    np.testing.assert_allclose(r["gap"][fin], gap[fin], rtol=0, atol=1e-9)
+    assert np.array_equal(np.isfinite(r["gap"]), fin)
+    assert np.array_equal(r["gap"][~fin], gap[~fin])
+    near = np.abs(gap - math.log(lam)) < 1e-9
+    assert np.array_equal(r["skip"][~near], skip[~near])
+    assert r["skipped"] > 0  # the cases do exercise skipping
+    assert r["visited"] == int((skip != 255).sum())
+    assert r["skipped"] == int((skip == 1).sum())
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_decisions_match_bruteforce(seed):
+    rng = np.random.default_rng(300 + seed)
+    B, Hq, Hkv, Lmax, d, dv, bk = 2, 8, 2, int(rng.integers(70, 400)), 8, 6, 16
+    splits = int(rng.integers(1, 5))
+    q = _rand(rng, B, Hq, d, std=2.0)
+    k = _rand(rng, B, Hkv, Lmax, d, std=2.0)
+    v = _rand(rng, B, Hkv, Lmax, dv)
+    lens = rng.integers(1, Lmax + 1, size=B)
+    lam = float(10 ** rng.uniform(-5, -0.5))
+    r = oracle.decode(q, k, v, lens, lam=lam, block_k=bk, num_splits=splits)
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(d)
+    nkb = -(-Lmax // bk)
+    for b in range(B):
+        nkb_b = -(-int(lens[b]) // bk)
+        per = -(-nkb_b // splits)
+        for g in range(Hkv):
+            S = scores(q[b, g * G:(g + 1) * G], k[b, g], scale)
+            mask = np.broadcast_to(np.arange(Lmax)[None] < lens[b], S.shape)
+            exp_skip = [255] * nkb
+            exp_gap = [-math.inf] * nkb
+            for s in range(splits):
+                jb, je = s * per, min(nkb_b, (s + 1) * per)
+                if jb >= je:
+                    continue
+                cols = [(j * bk, min(Lmax, (j + 1) * bk)) for j in range(jb, je)]
+                sk, gp = block_decisions(S, mask, None, cols, lam)
+                exp_skip[jb:je] = sk
+                exp_gap[jb:je] = gp
+            exp_gap = np.array(exp_gap)
+            fin = np.isfinite(exp_gap)
+            np.testing.assert_allclose(r["gap"][b, g][fin], exp_gap[fin], rtol=0, atol=1e-9)
+            assert np.array_equal(r["gap"][b, g][~fin], exp_gap[~fin])
+            near = np.abs(exp_gap - math.log(lam)) < 1e-9
+            assert np.array_equal(r["skip"][b, g][~near], np.array(exp_skip, np.uint8)[~near])
+
+
+# ----------------------------------------------------- outputs of kept keys
+def _kept_mask_prefill(skip, L, tq, bk, causal):
+    """Visible and executed entries, for each (b, h): [L, L]."""
+    B, Hq, nqt, nkb = skip.shape
+    base = prefill_mask(L, causal)
+    out = np.zeros((B, Hq, L, L), bool)
+    for t in range(nqt):
+        for j in range(nkb):
+            ex = skip[:, :, t, j] == 0
+            out[:, :, t * tq:(t + 1) * tq, j * bk:(j + 1) * bk] = ex[:, :, None, None]
+    return out & base[None, None]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_output_is_softmax_over_executed_keys(seed):
+    """A skipped block changes nothing: O equals softmax attention over executed keys (<= 1e-12)."""
+    rng = np.random.default_rng(500 + seed)
+    L, tq, bk = 192, 32, 16
+    causal = seed % 2 == 0
+    q, k, v = _prefill_case(seed + 50, B=1, Hq=2, Hkv=2, L=L, d=8, dv=5, qstd=2.0, blocky=bk)
+    r0 = oracle.prefill(q, k, v, causal=causal, lam=0.0, tile_q=tq, block_k=bk)
+    lam = _lam_at(r0["gap"], rng.uniform(0.3, 0.8))
+    r = oracle.prefill(q, k, v, causal=causal, lam=lam, tile_q=tq, block_k=bk)
+    assert r["skipped"] > 0
+    kept = _kept_mask_prefill(r["skip"], L, tq, bk, causal)
+    scale = 1 / math.sqrt(8)
+    for h in range(2):
+        S = scores(q[0, h], k[0, h], scale)
+        ref = masked_softmax_attention(S, kept[0, h], v[0, h])
+        np.testing.assert_allclose(r["o"][0, h], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_decode_output_is_softmax_over_executed_keys(splits):
+    """Split partials merged by log-sum-exp equal one softmax over the union of executed keys."""
+    rng = np.random.default_rng(700 + splits)
+    B, Hq, Hkv, Lmax, d, dv, bk = 2, 4, 1, 512, 8, 7, 32
+    q = _rand(rng, B, Hq, d, std=2.0)
+    k = _rand(rng, B, Hkv, Lmax, d, std=2.0)
+    v = _rand(rng, B, Hkv, Lmax, dv)
+    lens = np.array([512, 333])
+    r0 = oracle.decode(q, k, v, lens, lam=0.0, block_k=bk, num_splits=splits)
+    lam = _lam_at(r0["gap"], 0.6)
+    r = oracle.decode(q, k, v, lens, lam=lam, block_k=bk, num_splits=splits)
+    assert r["skipped"] > 0
+    scale = 1 / math.sqrt(d)
+    for b in range(B):
+        ex = np.repeat(r["skip"][b, 0] == 0, bk)[:Lmax] & (np.arange(Lmax) < lens[b])
+        S = scores(q[b], k[b, 0], scale)
+        ref = masked_softmax_attention(S, np.broadcast_to(ex, S.shape), v[b, 0])
+        np.testing.assert_allclose(r["o"][b], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- mass bound
+@pytest.mark.parametrize("seed", range(6))
+def test_dropped_mass_bound(seed):
+    """Per row, the dense-softmax mass of skipped keys is < lambda * (number of skipped keys)."""
+    rng = np.random.default_rng(900 + seed)
+    L, tq, bk, d = 256, 32, 16, 8
+    q, k, v = _prefill_case(seed + 90, B=1, Hq=1, Hkv=1, L=L, d=d, dv=3, qstd=2.0, blocky=bk)
+    r0 = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=tq, block_k=bk)
+    lam = _lam_at(r0["gap"], rng.uniform(0.3, 0.9))
+    r = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=tq, block_k=bk)
+    assert r["skipped"] > 0
+    S = scores(q[0, 0], k[0, 0], 1 / math.sqrt(d))
+    base = prefill_mask(L, True)
+    p = dense_probs(S, base)
+    kept = _kept_mask_prefill(r["skip"], L, tq, bk, True)[0, 0]
+    dropped = base & ~kept
+    mass = (p * dropped).sum(axis=1)
+    nskip = dropped.sum(axis=1)
+    assert np.all(mass <= lam * nskip + 1e-15)
+    # and O is within the corresponding bound of dense attention
+    dense = masked_softmax_attention(S, base, v[0, 0])
+    err = np.abs(r["o"][0, 0] - dense).max(axis=1)
+    span = v[0, 0].max(axis=0) - v[0, 0].min(axis=0)
+    assert np.all(err <= mass * span.max() + 1e-12)
+
+
+# ------------------------------------------------------------- invariants
+def test_skip_set_monotone_in_lambda():
+    q, k, v = _prefill_case(3, B=1, Hq=2, Hkv=1, L=256, d=8, dv=4, qstd=2.0, blocky=16)
+    prev = None
+    for lam in [0.0, 1e-6, 1e-4, 1e-3, 1e-2, 0.1, 0.5, 0.999]:
+        r = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=32, block_k=16)
+        s = r["skip"] == 1
+        if prev is not None:
+            assert np.all(s >= prev)
+        prev = s
+    assert prev.any()
+
+
+def test_first_block_always_executed():
+    q, k, v = _prefill_case(5, B=1, Hq=1, Hkv=1, L=200, d=8, dv=4, qstd=2.0)
+    r = oracle.prefill(q, k, v, causal=True, lam=0.999999, tile_q=32, block_k=16)
+    assert np.all(r["skip"][..., 0] == 0)
+    assert np.all(np.isposinf(r["gap"][..., 0]))
+    rng = np.random.default_rng(2)
+    qd = _rand(rng, 2, 2, 8, std=2)
+    kd = _rand(rng, 2, 1, 300, 8, std=2)
+    vd = _rand(rng, 2, 1, 300, 3)
+    rd = oracle.decode(qd, kd, vd, [300, 300], lam=0.999999, block_k=16, num_splits=4)
+    nkb = 19  # ceil(300/16); per split = 5 blocks
+    for s in range(4):
+        assert np.all(rd["skip"][:, 0, s * 5] == 0)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    q, k, v = _prefill_case(9, B=1, Hq=4, Hkv=2, L=150, d=8, dv=6, qstd=2.0)
+    r1 = oracle.prefill(q, k, v, causal=True, lam=0.01, tile_q=32, block_k=16)
+    r2 = oracle.prefill(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), causal=True,
+                        lam=0.01, tile_q=32, block_k=16)
+    assert np.array_equal(r1["o"], r2["o"])
+    assert np.array_equal(r1["skip"], r2["skip"])
+
+
+def test_causal_unvisited_blocks():
+    """Causal tiles never visit blocks strictly above the diagonal."""
+    q, k, v = _prefill_case(4, B=1, Hq=1, Hkv=1, L=256, d=8, dv=4)
+    r = oracle.prefill(q, k, v, causal=True, lam=0.01, tile_q=64, block_k=32)
+    for t in range(4):
+        for j in range(8):
+            visited = j * 32 <= t * 64 + 63
+            assert (r["skip"][0, 0, t, j] != 255) == visited
+
+
+def test_input_validation():
+    q, k, v = _prefill_case(1, L=16)
+    for bad in [-0.1, 1.0, float("nan")]:
+        with pytest.raises(ValueError):
+            oracle.prefill(q, k, v, lam=bad)
+    with pytest.raises(ValueError):
+        oracle.decode(q[:, :, 0], k, v, [0], lam=0.1)
+
+
+# ------------------------------------------------------ hand-worked example
+def test_worked_example_closed_form():
+    """Hand-built cases whose scores, gaps, decisions and outputs are closed forms."""
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        examples = json.load(f)["examples"]
+    for ex in examples:
+        bk = ex["block_k"]
+        kv = np.array(ex["key_values"], dtype=np.float64)  # scalar keys, d = 1
+        L = kv.size
+        q = np.array([[[ex["query"]]]])            # [B=1, Hq=1, d=1]
+        k = kv.reshape(1, 1, L, 1)
+        v = np.zeros((1, 1, L, 1))
+        v[0, 0, ex["value_one_at"], 0] = 1.0       # V is the indicator of one key
+        for case in ex["cases"]:
+            r = oracle.decode(q, k, v, [L], scale=1.0, lam=case["lambda"], block_k=bk)
+            assert list(r["skip"][0, 0]) == case["skip"], case
+            assert np.array_equal(r["gap"][0, 0][1:], np.array(ex["gaps_after_first"]))
+            # O = e^{s*} / sum over executed keys of e^{s}, with the key scores known exactly
+            s = kv * ex["query"]
+            ex_keys = np.repeat(np.array(case["skip"]) == 0, bk)
+            expect = math.exp(s[ex["value_one_at"]]) / np.exp(s[ex_keys]).sum()
+            assert abs(r["o"][0, 0, 0] - expect) < 1e-14
+
+
+# --------------------------------------------------------------- calibration
+def test_lambda_for_target_hits_target_exactly():
+    q, k, v = _prefill_case(21, B=1, Hq=2, Hkv=1, L=512, d=8, dv=4, qstd=2.0, blocky=16)
+    r0 = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=32, block_k=16)
+    vis = r0["skip"] != 255
+    gaps = r0["gap"][vis]
+    N = gaps.size
+    for target in [0.3, 0.5, 0.7]:
+        lam, reached = oracle.lambda_for_target(gaps, target)
+        assert 0 < lam < 1
+        r = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=32, block_k=16)
+        frac = r["skipped"] / r["visited"]
+        assert r["visited"] == N
+        assert abs(frac - reached) < 1e-12
+        assert abs(frac - target) <= 1.0 / N + 1e-12
+        # ln(lambda) separates the ceil(target*N) smallest gaps from the rest with margin on both sides
+        sg = np.sort(gaps)
+        kk = math.ceil(target * N)
+        assert sg[kk - 1] < math.log(lam) < sg[kk]
+
+
+def test_fit_a_recovers_planted_a():
+    Ls = np.array([4096, 8192, 16384, 32768, 65536])
+    a = 37.5
+    assert abs(oracle.fit_a(a / Ls, Ls) - a) < 1e-9 * a
+    noisy = a / Ls * np.exp(np.array([0.1, -0.1, 0.05, -0.05, 0.0]))
+    assert abs(oracle.fit_a(noisy, Ls) - a) < 1e-9 * a  # log-noise averaging to 0
+
+
+def test_lambda_from_table():
+    t, a = [0.3, 0.5, 0.7], [2.0, 8.0, 32.0]
+    assert abs(oracle.lambda_from_table(t, a, 0.5, 1000) - 8.0 / 1000) < 1e-15
+    assert abs(oracle.lambda_from_table(t, a, 0.6, 1000) - 16.0 / 1000) < 1e-15  # geometric midpoint
+    assert abs(oracle.lambda_from_table(t, a, 0.4, 2000) - 4.0 / 2000) < 1e-15
