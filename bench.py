@@ -1,0 +1,262 @@
+"""Benchmark of the BLASST block-skipping attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Step = one blasst_prefill call on the GQA causal prefill workload
+(B=1, Hq=32, Hkv=8, L=8192, d=128, bf16, query tile 128, key block 64) at the
+lambda that the library's own calibration search gives for 70% block
+sparsity on that input.  ``value`` is the dense-equivalent throughput
+4*B*Hq*L^2*d/2 / time, in TFLOP/s.  The same run also measures
+  * the same prefill at the 50% lambda and with lambda = 0 (the dense kernel),
+    for speedups over the library's own dense path;
+  * the GQA decode workload (148 sequences, Hq=32, Hkv=8, 32768 cached tokens,
+    d=128, bf16 cache, block 64) at the 70% and 50% lambdas and lambda = 0:
+    microseconds per decode step and HBM GB/s on the bytes actually loaded;
+  * the fp64 CPU oracle on a bounded sample of the prefill workload.
+Inputs are seeded synthetic segment-center tensors generated on the device.
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import long_context_fa_amd as bl  # noqa: E402
+from long_context_fa_amd import inputs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, steps, warmup):
+    """Average ms per call over ``steps`` calls, timed with events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in ev]
+    return float(np.mean(per)), float(np.median(per)), per
+
+
+def prefill_workload(seed=1001):
+    B, Hq, Hkv, L, d = 1, 32, 8, 8192, 128
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda", seed=seed)
+    return (B, Hq, Hkv, L, d), (q, k, v)
+
+
+def decode_workload(seed=1002):
+    B, Hq, Hkv, L, d = 148, 32, 8, 32768, 128
+    q, kc, vc, lens = inputs.decode_inputs(B, Hq, Hkv, L, d, n_random=8, device="cuda", seed=seed)
+    return (B, Hq, Hkv, L, d), (q, kc, vc, lens)
+
+
+def calibrate_prefill(q, k, v, targets):
+    B, Hq, L, _ = q.shape
+    gap = torch.empty(B, Hq, -(-L // 128), -(-L // 64), dtype=torch.float32, device="cuda")
+    bl.blasst_prefill(q, k, v, causal=True, lam=0.0, tile_q=128, gap_map=gap)
+    g = gap.cpu().numpy().ravel()
+    return {t: bl.blasst_calibrate_search(g, t) for t in targets}
+
+
+def calibrate_decode(q, kc, vc, lens, S, targets):
+    B, Hkv, L = q.shape[0], kc.shape[1], kc.shape[2]
+    gap = torch.empty(B, Hkv, -(-L // 64), dtype=torch.float32, device="cuda")
+    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap)
+    g = gap.cpu().numpy().ravel()
+    return {t: bl.blasst_calibrate_search(g, t) for t in targets}
+
+
+def counts(fn_with_counters):
+    cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+    fn_with_counters(cnt)
+    torch.cuda.synchronize()
+    c = cnt.cpu().numpy()
+    return int(c[0]), int(c[1])
+
+
+def cpu_baseline_prefill(q, k, v, lam, budget_s=20.0):
+    """The fp64 oracle on a bounded sample of query tiles of the prefill workload."""
+    import oracle
+
+    B, Hq, L, d = q.shape
+    tile = 128
+    nqt = L // tile
+    threads = min(16, len(os.sched_getaffinity(0)))
+    f = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    qh, kh, vh = f(q), f(k), f(v)
+    rng = np.random.default_rng(7)
+    all_units = [(b, h, t) for b in range(B) for h in range(Hq) for t in range(nqt)]
+    order = rng.permutation(len(all_units))
+    done_flops, done_s, n_units = 0.0, 0.0, 0
+    batch = threads
+    while done_s < budget_s * 0.5 and n_units < len(all_units):
+        mask = np.zeros((B, Hq, nqt), np.uint8)
+        picks = [all_units[i] for i in order[n_units:n_units + batch]]
+        batch = len(picks)
+        flops = 0.0
+        for (b, h, t) in picks:
+            mask[b, h, t] = 1
+            r0 = t * tile
+            flops += 4.0 * d * sum(r + 1 for r in range(r0, r0 + tile))  # dense-equivalent
+        t0 = time.perf_counter()
+        oracle.prefill(qh, kh, vh, causal=True, lam=lam, tile_q=tile, block_k=64, unit_mask=mask,
+                       nthreads=threads, want_maps=False)
+        dt = time.perf_counter() - t0
+        done_flops += flops
+        done_s += dt
+        n_units += batch
+        log(f"  cpu oracle: {n_units} units, {done_s:.1f} s")
+        if done_s + 2 * dt > budget_s:
+            break
+        batch *= 2
+    return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_units} random query tiles (128 rows) of the 1x32/8x8192x128 prefill at the "
+                      f"70% lambda, {done_s:.1f} s of fp64 work on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the method has no multi-GPU path here; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    steps, warmup = args.steps, args.warmup
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ------------------------------------------------------------ prefill
+    (B, Hq, Hkv, L, d), (q, k, v) = prefill_workload()
+    cal = calibrate_prefill(q, k, v, [0.5, 0.7])
+    lam70, reach70 = cal[0.7]
+    lam50, reach50 = cal[0.5]
+    log(f"prefill lambda70={lam70:.4g} (gap-map sparsity {reach70:.4f}) lambda50={lam50:.4g} ({reach50:.4f})")
+    out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
+
+    def pf(lam, cnt=None):
+        return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
+
+    dense_flops = 4.0 * B * Hq * L * L * d / 2
+    res = {}
+    for name, lam in [("s70", lam70), ("s50", lam50), ("dense", 0.0)]:
+        mean_ms, med_ms, _ = time_calls(pf(lam), steps, warmup)
+        vis, skp = counts(lambda c: pf(lam, c)())
+        res[name] = {"lambda": lam, "ms": mean_ms, "ms_median": med_ms, "visited": vis, "skipped": skp,
+                     "sparsity": skp / vis if vis else 0.0,
+                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12}
+        log(f"prefill {name}: {mean_ms:.4f} ms, sparsity {res[name]['sparsity']:.4f}, "
+            f"{res[name]['dense_equiv_tflops']:.1f} dense-equiv TFLOP/s")
+    bc, br = 64, 128
+    exec70 = res["s70"]["visited"] - res["s70"]["skipped"]
+    mfma_flops70 = res["s70"]["visited"] * 2.0 * br * bc * d + exec70 * 2.0 * br * bc * d
+    achieved = mfma_flops70 / (res["s70"]["ms"] * 1e-3) / 1e12
+    prefill = {
+        "lambda70": lam70, "sparsity70": res["s70"]["sparsity"], "ms70": res["s70"]["ms"],
+        "lambda50": lam50, "sparsity50": res["s50"]["sparsity"], "ms50": res["s50"]["ms"],
+        "ms_dense": res["dense"]["ms"],
+        "dense_equiv_tflops_dense_path": res["dense"]["dense_equiv_tflops"],
+        "speedup70_vs_dense": res["dense"]["ms"] / res["s70"]["ms"],
+        "speedup50_vs_dense": res["dense"]["ms"] / res["s50"]["ms"],
+        "mfma_util_executed70": achieved / PEAK_BF16_TFLOPS,
+        "mfma_util_dense": dense_flops / (res["dense"]["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+
+    # ------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
+        S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
+        work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+        dout = torch.empty(DB, DHq, Dd, dtype=torch.bfloat16, device="cuda")
+        dcal = calibrate_decode(dq, kc, vc, lens, S, [0.5, 0.7])
+
+        def dc(lam, cnt=None):
+            return lambda: bl.blasst_decode(dq, kc, vc, lens, lam=lam, num_splits=S, out=dout,
+                                            workspace=work, counters=cnt)
+
+        dres = {}
+        for name, lam in [("s70", dcal[0.7][0]), ("s50", dcal[0.5][0]), ("dense", 0.0)]:
+            mean_ms, med_ms, _ = time_calls(dc(lam), steps, warmup)
+            vis, skp = counts(lambda c: dc(lam, c)())
+            blk = 64 * Dd * 2
+            loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
+            if S > 1:
+                loaded += 2 * DB * DHq * S * (Dd + 2) * 4
+            dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "bytes": loaded,
+                          "gbps": loaded / (mean_ms * 1e-3) / 1e9}
+            log(f"decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
+                f"{dres[name]['gbps']:.0f} GB/s on loaded bytes")
+        decode = {
+            "workload": "GQA decode B=148 Hq=32 Hkv=8 L=32768 d=128 bf16, block 64, one query token per sequence",
+            "num_splits": S,
+            "us_per_step70": dres["s70"]["us"], "sparsity70": dres["s70"]["sparsity"],
+            "us_per_step50": dres["s50"]["us"], "sparsity50": dres["s50"]["sparsity"],
+            "us_per_step_dense": dres["dense"]["us"],
+            "speedup70_vs_dense": dres["dense"]["us"] / dres["s70"]["us"],
+            "speedup50_vs_dense": dres["dense"]["us"] / dres["s50"]["us"],
+            "roofline": {"bound": "hbm", "achieved": dres["s70"]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": dres["s70"]["gbps"] / PEAK_HBM_GBS, "traffic": None},
+        }
+        del dq, kc, vc, work, dout
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(q, k, v, lam70)
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s dense-equivalent on {cpu['cores']} threads")
+
+    line = {
+        "metric": "prefill dense-equiv TFLOP/s + decode us/step at ~70% block skip vs lambda=0",
+        "value": res["s70"]["dense_equiv_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": res["s70"]["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "GQA causal prefill B=1 Hq=32 Hkv=8 L=8192 d=128 bf16, query tile 128, "
+                               "key block 64, lambda calibrated for 70% block sparsity",
+                   "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
+        "prefill": prefill,
+        "decode": decode,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * blasst.h -- C ABI of the MI355X (gfx950) block-skipping attention library
+ * (libblasst.so).
+ *
+ * The method: "BLASST: Dynamic BLocked Attention Sparsity via Softmax
+ * Thresholding" (gist.science/pt/paper/2512.12087, section 2 "Metodologia:
+ * BLASST"; the same in gist.science/hi/paper/2512.12087, section 2).  A
+ * FlashAttention-style blockwise online-softmax forward pass keeps a running
+ * row max m; for every key block it forms the block-local row max m~ and skips
+ * the block when m~ - m < ln(lambda).  A skipped block does no exponential, no
+ * V-block load and no P.V product.  The threshold follows lambda = a / L, with
+ * a fitted per target sparsity (page 1 "Calibração Automática"; BLASST reading
+ * notes, papers.lqhl.me/papers/BLASST-MLSys26, "关键观察" observation 2).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are described by blasst_tensor: a DEVICE pointer, an element type
+ *    and strides IN ELEMENTS for the batch, head and token dimensions; the
+ *    last (feature) dimension is always contiguous.  Every device buffer is
+ *    allocated and owned by the caller; the library never allocates device
+ *    memory and keeps no pointer after a call returns.
+ *  - Calls are asynchronous: they validate their arguments on the host,
+ *    enqueue kernels on the given HIP stream (a hipStream_t passed as void*;
+ *    NULL = the default stream) and return.  Outputs are valid once the stream
+ *    has been synchronised.
+ *  - Validation happens before any launch, so a call that returns an error
+ *    has written nothing.  blasst_last_error() then holds a message naming the
+ *    offending argument (per calling thread).
+ *  - "Query tile" and "key block": decisions are taken per (query tile, key
+ *    block) pair.  A query tile skips a key block only if EVERY valid row of
+ *    the tile meets the criterion (the pages decide per block, see the BLASST
+ *    reading notes, "设计取舍": block rather than token granularity).
+ *  - Skip map entries: 0 = executed, 1 = skipped, 255 = not visited (no
+ *    unmasked (row, key) entry in the pair).  Gap map entries: the tile gap
+ *    g = max over valid rows of (m~ - m) in natural-log units of the scaled
+ *    scores; +inf for a unit's first visited block (m = -inf there); -inf for
+ *    pairs that are not visited.  Every entry of both maps is written.
+ *  - Counters (optional, device, two uint64): [0] += visited pairs,
+ *    [1] += skipped pairs.  They are accumulated atomically; the caller zeroes
+ *    them.  Block sparsity = counters[1] / counters[0].
+ *  - Arithmetic: bf16 inputs, fp32 scores and accumulation; the skip test is
+ *    evaluated in fp32 on the scaled scores (scale applied in fp32, never folded
+ *    into the bf16 query).
+ */
+#ifndef BLASST_H
+#define BLASST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLASST_ABI_VERSION 1
+
+typedef enum {
+    BLASST_OK = 0,
+    BLASST_ERR_INVALID_ARG = 1, /* bad pointer, size, stride, lambda, ... */
+    BLASST_ERR_UNSUPPORTED = 2, /* valid request with no compiled kernel (head dim, tile, dtype) */
+    BLASST_ERR_WORKSPACE = 3,   /* workspace missing or smaller than blasst_decode_plan() asked */
+    BLASST_ERR_LAUNCH = 4       /* the HIP runtime refused the launch */
+} blasst_status;
+
+typedef enum { BLASST_BF16 = 0, BLASST_FP32 = 1 } blasst_dtype;
+
+typedef struct {
+    void *ptr;          /* device pointer to element [0,0,0,0] */
+    blasst_dtype dtype;
+    int64_t sb, sh, st; /* strides in elements: batch, head, token (token unused for 3-D tensors) */
+} blasst_tensor;
+
+/* ------------------------------------------------------------------ prefill
+ * blasst_prefill(Q, K, V, causal, lambda, tile sizes): the blockwise skip
+ * forward for a whole sequence (Lq = Lk = L; with causal masking query i sees
+ * keys 0..i).  Query head h reads KV head h / (Hq / Hkv) (MHA when Hq = Hkv,
+ * GQA, MQA when Hkv = 1).  Key blocks are visited in ascending order.
+ *
+ *   q  [B, Hq, L, d]   bf16          k [B, Hkv, L, d]  bf16
+ *   v  [B, Hkv, L, dv] bf16          o [B, Hq, L, dv]  fp32 or bf16 (written)
+ *   d = dv in {64, 128}; tile_q in {64, 128}; block_k = 64.
+ *   scale   : multiplies q.k; <= 0 selects 1/sqrt(d).
+ *   lambda  : in [0, 1).  0 disables skipping and runs the dense kernel.
+ *   skip_map: optional device uint8 [B, Hq, nQT, nKB], nQT = ceil(L/tile_q),
+ *             nKB = ceil(L/block_k), contiguous.
+ *   gap_map : optional device float [B, Hq, nQT, nKB], contiguous.
+ *   counters: optional device uint64 [2].
+ * Errors: INVALID_ARG for null q/k/v/o, L < 0, B < 0, Hq or Hkv <= 0,
+ * Hq % Hkv != 0, lambda outside [0,1) or NaN, a non-positive stride or a
+ * pointer not aligned to 16 bytes with a token stride not a multiple of 8
+ * elements; UNSUPPORTED for other d, dv, tile or dtype; LAUNCH if HIP fails.
+ * L = 0 or B = 0 is a valid no-op.
+ */
+typedef struct {
+    blasst_tensor q, k, v, o;
+    int64_t B, Hq, Hkv, L, d, dv;
+    int causal;
+    double scale;
+    double lambda;
+    int tile_q;
+    int block_k;
+    uint8_t *skip_map;
+    float *gap_map;
+    unsigned long long *counters;
+} blasst_prefill_params;
+
+blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream);
+
+/* ------------------------------------------------------------------- decode
+ * blasst_decode(q, KV cache, seq lens, lambda): one query token per sequence
+ * against a KV cache.  A query tile is the group of G = Hq / Hkv query heads
+ * that share one KV head (GQA; MQA when Hkv = 1; MHA when G = 1); MLA in its
+ * absorbed form is Hkv = 1 with a latent cache whose first dv columns are the
+ * values (pass v_cache.ptr == k_cache.ptr with the same strides).
+ *
+ * Split-K: the nkb = ceil(seq_len/block_k) key blocks of a sequence are cut
+ * into num_splits contiguous runs of ceil(nkb/num_splits) blocks; each run is
+ * processed from m = -inf (so its first block is always executed) and the run
+ * partials are merged with the log-sum-exp rule.  Decisions therefore depend
+ * on num_splits; the value used is reported by blasst_decode_plan().
+ *
+ *   q       [B, Hq, dqk] bf16 (sb, sh)       o [B, Hq, dv] fp32 or bf16 (sb, sh)
+ *   k_cache [B, Hkv, Lmax, dqk] bf16         v_cache [B, Hkv, Lmax, dv] bf16
+ *   seq_lens: device int32 [B], each in 1..Lmax (the kernel clamps other
+ *             values into 0..Lmax; a length of 0 yields O = 0).
+ *   Supported: (dqk = dv in {64, 128}, G in 1..16) and the latent form
+ *   (dqk = 576, dv = 512, Hkv = 1, G = 128, v aliasing k).  block_k = 64.
+ *   num_splits: 0 lets the library choose; otherwise 1..nKB.
+ *   skip_map / gap_map: optional device [B, Hkv, nKB], nKB = ceil(Lmax/64).
+ */
+typedef struct {
+    blasst_tensor q, k_cache, v_cache, o;
+    const int32_t *seq_lens;
+    int64_t B, Hq, Hkv, Lmax, dqk, dv;
+    double scale;
+    double lambda;
+    int block_k;
+    int num_splits;
+    uint8_t *skip_map;
+    float *gap_map;
+    unsigned long long *counters;
+} blasst_decode_params;
+
+/* Host-only: the split count a call with *p will use and the device workspace
+ * (bytes) it needs; either output pointer may be NULL.  Same validation as
+ * blasst_decode. */
+blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_used,
+                                 size_t *workspace_bytes);
+
+/* workspace: caller-owned device buffer of at least the planned size (may be
+ * NULL when the planned size is 0).  Calls that share one workspace must be
+ * ordered on one stream. */
+blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes,
+                            void *hip_stream);
+
+/* ---------------------------------------------------------------- calibrate
+ * blasst_calibrate(target_sparsity, L) -> lambda = a(target) / L.  The table
+ * holds a fitted per target sparsity (strictly increasing targets, a > 0); ln a
+ * is interpolated linearly in the target between rows.  Host only.
+ * Errors: INVALID_ARG for a null or empty table, non-increasing targets,
+ * a <= 0, L <= 0, a target outside [targets[0], targets[n-1]], or a result
+ * lambda >= 1.
+ */
+typedef struct {
+    int n;
+    const double *target;
+    const double *a;
+} blasst_calib_table;
+
+blasst_status blasst_calibrate(const blasst_calib_table *table, double target_sparsity, int64_t L,
+                               double *lambda_out);
+
+/* The calibration search at one length, host only.  gaps: host copy of a gap
+ * map (entries of -inf, i.e. unvisited pairs, are ignored).  Because the
+ * running max never depends on the decisions, the sparsity at lambda is the
+ * fraction of gaps below ln(lambda); the returned lambda puts ln(lambda)
+ * halfway between the k-th and (k+1)-th smallest gap, k = ceil(target * N).
+ * *reached_out (optional) gets the sparsity that lambda gives on these gaps;
+ * when the target needs lambda >= 1 the largest lambda below 1 is returned and
+ * *reached_out says what it reaches.  INVALID_ARG for null pointers, n < 1,
+ * no visited pair, or a target outside [0, 1]. */
+blasst_status blasst_calibrate_search(const float *gaps, int64_t n, double target,
+                                      double *lambda_out, double *reached_out);
+
+/* Fit of the law lambda = a / L over n lengths: ln a = mean(ln(lambda_i * L_i)).
+ * INVALID_ARG for null pointers, n < 1, lambda_i outside (0, 1) or L_i <= 0. */
+blasst_status blasst_calibrate_fit(const double *lambda_at_L, const int64_t *L, int n, double *a_out);
+
+/* ------------------------------------------------------------------ helpers */
+const char *blasst_status_str(blasst_status s); /* static string, never NULL */
+const char *blasst_last_error(void);            /* message of this thread's last failed call */
+int blasst_abi_version(void);                   /* BLASST_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLASST_H */

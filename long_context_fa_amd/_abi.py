@@ -1,0 +1,255 @@
+"""ctypes marshalling for libblasst.so (mirrors include/blasst.h).
+
+Argument marshalling only: tensors become (device pointer, dtype, strides);
+the library validates, plans and launches.  Nothing here computes any part of
+the attention.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libblasst.so"
+
+BLASST_OK = 0
+_BF16, _FP32 = 0, 1
+
+
+class BlasstError(RuntimeError):
+    """A non-OK blasst_status, with the library's message."""
+
+    def __init__(self, status, func):
+        self.status = status
+        lib = load_library()
+        msg = lib.blasst_last_error().decode()
+        name = lib.blasst_status_str(status).decode()
+        super().__init__(f"{func}: {name} ({status}): {msg}")
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int),
+                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("st", ctypes.c_int64)]
+
+
+class _PrefillParams(ctypes.Structure):
+    _fields_ = [("q", _Tensor), ("k", _Tensor), ("v", _Tensor), ("o", _Tensor),
+                ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("L", ctypes.c_int64), ("d", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("causal", ctypes.c_int), ("scale", ctypes.c_double), ("lam", ctypes.c_double),
+                ("tile_q", ctypes.c_int), ("block_k", ctypes.c_int),
+                ("skip_map", ctypes.c_void_p), ("gap_map", ctypes.c_void_p),
+                ("counters", ctypes.c_void_p)]
+
+
+class _DecodeParams(ctypes.Structure):
+    _fields_ = [("q", _Tensor), ("k_cache", _Tensor), ("v_cache", _Tensor), ("o", _Tensor),
+                ("seq_lens", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("Lmax", ctypes.c_int64), ("dqk", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("scale", ctypes.c_double), ("lam", ctypes.c_double),
+                ("block_k", ctypes.c_int), ("num_splits", ctypes.c_int),
+                ("skip_map", ctypes.c_void_p), ("gap_map", ctypes.c_void_p),
+                ("counters", ctypes.c_void_p)]
+
+
+class _CalibTable(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("target", ctypes.POINTER(ctypes.c_double)),
+                ("a", ctypes.POINTER(ctypes.c_double))]
+
+
+_lib = None
+
+
+def library_path():
+    return os.environ.get("BLASST_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libblasst.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m long_context_fa_amd.build` "
+                          "(the attention has no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    st = ctypes.c_int
+    lib.blasst_prefill.restype = st
+    lib.blasst_prefill.argtypes = [ctypes.POINTER(_PrefillParams), ctypes.c_void_p]
+    lib.blasst_decode_plan.restype = st
+    lib.blasst_decode_plan.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.blasst_decode.restype = st
+    lib.blasst_decode.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]
+    lib.blasst_calibrate.restype = st
+    lib.blasst_calibrate.argtypes = [ctypes.POINTER(_CalibTable), ctypes.c_double, ctypes.c_int64,
+                                     ctypes.POINTER(ctypes.c_double)]
+    lib.blasst_calibrate_search.restype = st
+    lib.blasst_calibrate_search.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_double,
+                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.blasst_calibrate_fit.restype = st
+    lib.blasst_calibrate_fit.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                         ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.blasst_status_str.restype = ctypes.c_char_p
+    lib.blasst_status_str.argtypes = [ctypes.c_int]
+    lib.blasst_last_error.restype = ctypes.c_char_p
+    lib.blasst_last_error.argtypes = []
+    lib.blasst_abi_version.restype = ctypes.c_int
+    lib.blasst_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _FP32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _tensor(t, three_d=False):
+    if t is None:
+        return _Tensor(None, _BF16, 0, 0, 0)
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    if three_d:
+        return _Tensor(t.data_ptr(), _dtype_code(t), t.stride(0), t.stride(1), 0)
+    return _Tensor(t.data_ptr(), _dtype_code(t), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    """A hipStream_t: a torch stream, a raw handle (int), or None = torch's current stream."""
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, func):
+    if status != BLASST_OK:
+        raise BlasstError(status, func)
+
+
+def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, scale=None, out=None,
+                   out_dtype=torch.float32, skip_map=None, gap_map=None, counters=None, stream=None):
+    """Block-skipping prefill: q [B,Hq,L,d], k [B,Hkv,L,d], v [B,Hkv,L,dv] (bf16, device).
+
+    Returns O [B,Hq,L,dv] (``out`` if given).  Optional outputs: ``skip_map``
+    uint8 and ``gap_map`` float32 of shape [B,Hq,ceil(L/tile_q),ceil(L/block_k)],
+    ``counters`` uint64-compatible int64 tensor of 2 elements (visited, skipped),
+    accumulated (zero it first).
+    """
+    B, Hq, L, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    if out is None:
+        out = torch.empty(B, Hq, L, dv, dtype=out_dtype, device=q.device)
+    p = _PrefillParams(_tensor(q), _tensor(k), _tensor(v), _tensor(out), B, Hq, Hkv, L, d, dv,
+                       int(bool(causal)), float(scale) if scale is not None else 0.0, float(lam),
+                       int(tile_q), int(block_k), _ptr(skip_map), _ptr(gap_map), _ptr(counters))
+    _check(load_library().blasst_prefill(ctypes.byref(p), _stream(stream, q.device)), "blasst_prefill")
+    return out
+
+
+def _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
+                   skip_map, gap_map, counters):
+    B, Hq, dqk = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dv = out.shape[2] if out is not None else (v_cache.shape[3] if v_cache is not None else dqk)
+    return _DecodeParams(_tensor(q, True), _tensor(k_cache), _tensor(v_cache), _tensor(out, True),
+                         _ptr(seq_lens), B, Hq, Hkv, Lmax, dqk, dv,
+                         float(scale) if scale is not None else 0.0, float(lam), int(block_k),
+                         int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters))
+
+
+def blasst_decode_plan(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
+                       dv=None, out_dtype=torch.float32):
+    """(num_splits the call will use, workspace bytes it needs)."""
+    B, Hq, _ = q.shape
+    dv = dv if dv is not None else v_cache.shape[3]
+    p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, None,
+                       None, None, None)
+    # the planner reads no device memory: describe O [B,Hq,dv] at q's (aligned) address
+    p.o = _Tensor(q.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _FP32, Hq * dv, dv, 0)
+    p.dv = dv
+    ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+    _check(load_library().blasst_decode_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)),
+           "blasst_decode_plan")
+    return ns.value, ws.value
+
+
+def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
+                  dv=None, out=None, out_dtype=torch.float32, workspace=None, skip_map=None,
+                  gap_map=None, counters=None, stream=None):
+    """Block-skipping decode: q [B,Hq,dqk], caches [B,Hkv,Lmax,*] (bf16, device), seq_lens int32 [B].
+
+    For the latent (MLA) form pass ``v_cache = k_cache`` and ``dv=512``.
+    ``workspace`` (uint8 device tensor) is allocated here when not given.
+    Returns O [B,Hq,dv].
+    """
+    B, Hq, _ = q.shape
+    dv = dv if dv is not None else v_cache.shape[3]
+    if out is None:
+        out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
+    p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
+                       skip_map, gap_map, counters)
+    lib = load_library()
+    if workspace is None:
+        ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+        _check(lib.blasst_decode_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)), "blasst_decode_plan")
+        workspace = torch.empty(max(ws.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.blasst_decode(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                             _stream(stream, q.device)), "blasst_decode")
+    return out
+
+
+def blasst_calibrate(targets, a, target, L):
+    """lambda = a(target) / L from a calibration table (ln a linear in the target)."""
+    n = len(targets)
+    t = (ctypes.c_double * n)(*[float(x) for x in targets])
+    aa = (ctypes.c_double * n)(*[float(x) for x in a])
+    table = _CalibTable(n, t, aa)
+    out = ctypes.c_double(0.0)
+    _check(load_library().blasst_calibrate(ctypes.byref(table), float(target), int(L), ctypes.byref(out)),
+           "blasst_calibrate")
+    return out.value
+
+
+def blasst_calibrate_search(gaps, target):
+    """lambda reaching ``target`` sparsity on a gap map (host float32 array-like)."""
+    import numpy as np
+    g = np.ascontiguousarray(np.asarray(gaps, dtype=np.float32).ravel())
+    lam, reached = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(load_library().blasst_calibrate_search(g.ctypes.data, g.size, float(target), ctypes.byref(lam),
+                                                  ctypes.byref(reached)), "blasst_calibrate_search")
+    return lam.value, reached.value
+
+
+def blasst_calibrate_fit(lambdas, lengths):
+    """a of the law lambda = a / L, fitted as ln a = mean(ln(lambda_i L_i))."""
+    n = len(lambdas)
+    lam = (ctypes.c_double * n)(*[float(x) for x in lambdas])
+    ls = (ctypes.c_int64 * n)(*[int(x) for x in lengths])
+    out = ctypes.c_double(0.0)
+    _check(load_library().blasst_calibrate_fit(lam, ls, n, ctypes.byref(out)), "blasst_calibrate_fit")
+    return out.value
+
+
+def blasst_status_str(status):
+    return load_library().blasst_status_str(int(status)).decode()
+
+
+def blasst_last_error():
+    return load_library().blasst_last_error().decode()
+
+
+def blasst_abi_version():
+    return load_library().blasst_abi_version()

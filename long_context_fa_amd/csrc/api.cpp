@@ -1,0 +1,363 @@
+// api.cpp -- the C ABI of libblasst.so: argument validation, planning and
+// dispatch to the HIP kernels.  Declarations and the full contract are in
+// include/blasst.h.
+#include "blasst.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+blasst_status fail(blasst_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A bf16/fp32 tensor whose feature rows are loaded 16 bytes at a time.
+blasst_status check_tensor(const blasst_tensor &t, const char *name, bool three_d, bool allow_fp32)
+{
+    if (t.ptr == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "%s: null pointer", name);
+    if (t.dtype != BLASST_BF16 && !(allow_fp32 && t.dtype == BLASST_FP32))
+        return fail(BLASST_ERR_UNSUPPORTED, "%s: unsupported dtype %d", name, (int)t.dtype);
+    if (t.sb < 0 || t.sh < 0 || (!three_d && t.st <= 0))
+        return fail(BLASST_ERR_INVALID_ARG, "%s: negative or zero stride", name);
+    if (!aligned16(t.ptr))
+        return fail(BLASST_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", name);
+    const int64_t unit = t.dtype == BLASST_BF16 ? 8 : 4; // elements per 16 bytes
+    if (t.sb % unit || t.sh % unit || (!three_d && t.st % unit))
+        return fail(BLASST_ERR_INVALID_ARG, "%s: strides must be multiples of 16 bytes", name);
+    return BLASST_OK;
+}
+
+blasst_status check_lambda(double lambda)
+{
+    if (!(lambda >= 0.0 && lambda < 1.0))
+        return fail(BLASST_ERR_INVALID_ARG, "lambda must be in [0, 1) (got %g)", lambda);
+    return BLASST_OK;
+}
+
+float log2_lambda(double lambda)
+{
+    return lambda == 0.0 ? -INFINITY : (float)std::log2(lambda);
+}
+
+} // namespace
+
+extern "C" {
+
+const char *blasst_status_str(blasst_status s)
+{
+    switch (s) {
+    case BLASST_OK: return "ok";
+    case BLASST_ERR_INVALID_ARG: return "invalid argument";
+    case BLASST_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BLASST_ERR_WORKSPACE: return "workspace missing or too small";
+    case BLASST_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char *blasst_last_error(void) { return g_last_error; }
+
+int blasst_abi_version(void) { return BLASST_ABI_VERSION; }
+
+blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
+{
+    if (p == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
+    if (p->B < 0 || p->L < 0)
+        return fail(BLASST_ERR_INVALID_ARG, "B and L must be >= 0");
+    if (p->Hq <= 0 || p->Hkv <= 0 || p->Hq % p->Hkv != 0)
+        return fail(BLASST_ERR_INVALID_ARG, "need Hq, Hkv > 0 and Hq %% Hkv == 0 (Hq=%lld Hkv=%lld)",
+                    (long long)p->Hq, (long long)p->Hkv);
+    if (blasst_status s = check_lambda(p->lambda))
+        return s;
+    if (std::isnan(p->scale) || std::isinf(p->scale))
+        return fail(BLASST_ERR_INVALID_ARG, "scale must be finite");
+    if (blasst_status s = check_tensor(p->q, "q", false, false))
+        return s;
+    if (blasst_status s = check_tensor(p->k, "k", false, false))
+        return s;
+    if (blasst_status s = check_tensor(p->v, "v", false, false))
+        return s;
+    if (blasst_status s = check_tensor(p->o, "o", false, true))
+        return s;
+    if (p->d != p->dv || (p->d != 64 && p->d != 128))
+        return fail(BLASST_ERR_UNSUPPORTED, "prefill supports d = dv in {64, 128} (got d=%lld dv=%lld)",
+                    (long long)p->d, (long long)p->dv);
+    if (p->tile_q != 64 && p->tile_q != 128)
+        return fail(BLASST_ERR_UNSUPPORTED, "tile_q must be 64 or 128 (got %d)", p->tile_q);
+    if (p->block_k != 64)
+        return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
+    const int64_t nqt = (p->L + p->tile_q - 1) / p->tile_q;
+    const int64_t nkb = (p->L + p->block_k - 1) / p->block_k;
+    if (p->L > (int64_t)1 << 30 || nqt * p->Hq * p->B > (int64_t)1 << 31)
+        return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (p->B == 0 || p->L == 0)
+        return BLASST_OK;
+
+    blasst::PrefillArgs a{};
+    a.q = (const uint16_t *)p->q.ptr;
+    a.k = (const uint16_t *)p->k.ptr;
+    a.v = (const uint16_t *)p->v.ptr;
+    a.o = p->o.ptr;
+    a.q_sb = p->q.sb; a.q_sh = p->q.sh; a.q_st = p->q.st;
+    a.k_sb = p->k.sb; a.k_sh = p->k.sh; a.k_st = p->k.st;
+    a.v_sb = p->v.sb; a.v_sh = p->v.sh; a.v_st = p->v.st;
+    a.o_sb = p->o.sb; a.o_sh = p->o.sh; a.o_st = p->o.st;
+    a.B = (int)p->B; a.Hq = (int)p->Hq; a.Hkv = (int)p->Hkv; a.L = (int)p->L;
+    a.nqt = (int)nqt; a.nkb = (int)nkb;
+    const double scale = p->scale > 0 ? p->scale : 1.0 / std::sqrt((double)p->d);
+    a.scale_log2 = (float)(scale * kLog2e);
+    a.lnlam2 = log2_lambda(p->lambda);
+    a.skip_map = p->skip_map;
+    a.gap_map = p->gap_map;
+    a.counters = p->counters;
+    const bool skip = p->lambda > 0.0;
+    hipError_t e = blasst::launch_prefill(a, (int)p->d, p->tile_q, p->causal != 0, skip,
+                                          p->o.dtype == BLASST_BF16, (hipStream_t)hip_stream);
+    if (e == hipErrorInvalidValue)
+        return fail(BLASST_ERR_UNSUPPORTED, "no prefill kernel for this configuration");
+    if (e != hipSuccess)
+        return fail(BLASST_ERR_LAUNCH, "prefill launch failed: %s", hipGetErrorString(e));
+    return BLASST_OK;
+}
+
+namespace {
+
+enum DecodeKind { KIND_NONE, KIND_GQA, KIND_MLA };
+
+DecodeKind decode_kind(const blasst_decode_params *p)
+{
+    const int64_t G = p->Hq / p->Hkv;
+    if (p->dqk == p->dv && (p->dqk == 64 || p->dqk == 128) && G <= 16)
+        return KIND_GQA;
+    if (p->dqk == 576 && p->dv == 512 && p->Hkv == 1 && G == 128)
+        return KIND_MLA;
+    return KIND_NONE;
+}
+
+blasst_status validate_decode(const blasst_decode_params *p)
+{
+    if (p == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
+    if (p->B < 0 || p->Lmax <= 0)
+        return fail(BLASST_ERR_INVALID_ARG, "need B >= 0 and Lmax > 0");
+    if (p->Hq <= 0 || p->Hkv <= 0 || p->Hq % p->Hkv != 0)
+        return fail(BLASST_ERR_INVALID_ARG, "need Hq, Hkv > 0 and Hq %% Hkv == 0");
+    if (blasst_status s = check_lambda(p->lambda))
+        return s;
+    if (std::isnan(p->scale) || std::isinf(p->scale))
+        return fail(BLASST_ERR_INVALID_ARG, "scale must be finite");
+    if (p->seq_lens == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "seq_lens: null pointer");
+    if (blasst_status s = check_tensor(p->q, "q", true, false))
+        return s;
+    if (blasst_status s = check_tensor(p->k_cache, "k_cache", false, false))
+        return s;
+    if (blasst_status s = check_tensor(p->v_cache, "v_cache", false, false))
+        return s;
+    if (blasst_status s = check_tensor(p->o, "o", true, true))
+        return s;
+    if (p->block_k != 64)
+        return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
+    const DecodeKind kind = decode_kind(p);
+    if (kind == KIND_NONE)
+        return fail(BLASST_ERR_UNSUPPORTED,
+                    "decode supports dqk = dv in {64,128} with Hq/Hkv <= 16, or dqk=576, dv=512, Hkv=1, Hq=128");
+    if (kind == KIND_MLA && p->v_cache.ptr != p->k_cache.ptr)
+        return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs v_cache to alias k_cache");
+    const int64_t nkb = (p->Lmax + 63) / 64;
+    if (p->num_splits < 0 || p->num_splits > nkb)
+        return fail(BLASST_ERR_INVALID_ARG, "num_splits must be in 0..ceil(Lmax/64)");
+    if (p->Lmax > (int64_t)1 << 30 || p->B > 65535 || p->Hkv > 65535)
+        return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+    return BLASST_OK;
+}
+
+int choose_splits(const blasst_decode_params *p)
+{
+    const int64_t nkb = (p->Lmax + 63) / 64;
+    if (p->num_splits > 0)
+        return p->num_splits;
+    const int64_t units = p->B * p->Hkv;
+    // Aim for >= 1024 workgroups (4 per compute unit), keep >= 16 blocks a split.
+    int s = 1;
+    while (units * s < 1024 && nkb / (2 * s) >= 16)
+        s *= 2;
+    return s;
+}
+
+size_t workspace_for(const blasst_decode_params *p, int S)
+{
+    if (S <= 1)
+        return 0;
+    const int64_t G = p->Hq / p->Hkv;
+    const int64_t units = p->B * p->Hkv * S * G;
+    return (size_t)units * (size_t)(p->dv + 2) * sizeof(float) + 256;
+}
+
+} // namespace
+
+blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_used, size_t *workspace_bytes)
+{
+    if (blasst_status s = validate_decode(p))
+        return s;
+    const int S = choose_splits(p);
+    if (num_splits_used)
+        *num_splits_used = S;
+    if (workspace_bytes)
+        *workspace_bytes = workspace_for(p, S);
+    return BLASST_OK;
+}
+
+blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    if (blasst_status s = validate_decode(p))
+        return s;
+    const int S = choose_splits(p);
+    const size_t need = workspace_for(p, S);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(BLASST_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned16(workspace))
+        return fail(BLASST_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    if (p->B == 0)
+        return BLASST_OK;
+
+    blasst::DecodeArgs a{};
+    a.q = (const uint16_t *)p->q.ptr;
+    a.k = (const uint16_t *)p->k_cache.ptr;
+    a.v = (const uint16_t *)p->v_cache.ptr;
+    a.o = p->o.ptr;
+    a.q_sb = p->q.sb; a.q_sh = p->q.sh;
+    a.k_sb = p->k_cache.sb; a.k_sh = p->k_cache.sh; a.k_st = p->k_cache.st;
+    a.v_sb = p->v_cache.sb; a.v_sh = p->v_cache.sh; a.v_st = p->v_cache.st;
+    a.o_sb = p->o.sb; a.o_sh = p->o.sh;
+    a.seq_lens = p->seq_lens;
+    a.B = (int)p->B; a.Hq = (int)p->Hq; a.Hkv = (int)p->Hkv; a.G = (int)(p->Hq / p->Hkv);
+    a.Lmax = (int)p->Lmax; a.nkb = (int)((p->Lmax + 63) / 64); a.num_splits = S;
+    const double scale = p->scale > 0 ? p->scale : 1.0 / std::sqrt((double)p->dqk);
+    a.scale_log2 = (float)(scale * kLog2e);
+    a.lnlam2 = log2_lambda(p->lambda);
+    if (S > 1) {
+        const int64_t units = p->B * p->Hkv * S * a.G;
+        a.part_o = (float *)workspace;
+        a.part_ml = a.part_o + units * p->dv;
+    }
+    a.skip_map = p->skip_map;
+    a.gap_map = p->gap_map;
+    a.counters = p->counters;
+    hipError_t e = blasst::launch_decode(a, (int)p->dqk, (int)p->dv, p->lambda > 0.0, p->o.dtype == BLASST_BF16,
+                                         (hipStream_t)hip_stream);
+    if (e == hipErrorInvalidValue)
+        return fail(BLASST_ERR_UNSUPPORTED, "no decode kernel for this configuration");
+    if (e != hipSuccess)
+        return fail(BLASST_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+    return BLASST_OK;
+}
+
+// ------------------------------------------------------------- calibration
+blasst_status blasst_calibrate(const blasst_calib_table *t, double target, int64_t L, double *lambda_out)
+{
+    if (t == nullptr || lambda_out == nullptr || t->target == nullptr || t->a == nullptr || t->n < 1)
+        return fail(BLASST_ERR_INVALID_ARG, "calibration table or output missing");
+    for (int i = 0; i < t->n; ++i) {
+        if (!(t->a[i] > 0.0) || std::isinf(t->a[i]))
+            return fail(BLASST_ERR_INVALID_ARG, "table a[%d] must be positive and finite", i);
+        if (i > 0 && !(t->target[i] > t->target[i - 1]))
+            return fail(BLASST_ERR_INVALID_ARG, "table targets must be strictly increasing");
+    }
+    if (L <= 0)
+        return fail(BLASST_ERR_INVALID_ARG, "L must be positive");
+    if (!(target >= t->target[0] && target <= t->target[t->n - 1]))
+        return fail(BLASST_ERR_INVALID_ARG, "target %g outside the calibrated range [%g, %g]", target,
+                    t->target[0], t->target[t->n - 1]);
+    int i = 0;
+    while (i + 1 < t->n && target > t->target[i + 1])
+        ++i;
+    double lna;
+    if (i + 1 >= t->n || target == t->target[i]) {
+        lna = std::log(t->a[i]);
+    } else {
+        const double w = (target - t->target[i]) / (t->target[i + 1] - t->target[i]);
+        lna = (1.0 - w) * std::log(t->a[i]) + w * std::log(t->a[i + 1]);
+    }
+    const double lam = std::exp(lna) / (double)L;
+    if (!(lam < 1.0))
+        return fail(BLASST_ERR_INVALID_ARG, "lambda = a/L = %g is not below 1", lam);
+    *lambda_out = lam;
+    return BLASST_OK;
+}
+
+blasst_status blasst_calibrate_search(const float *gaps, int64_t n, double target, double *lambda_out,
+                                      double *reached_out)
+{
+    if (gaps == nullptr || lambda_out == nullptr || n < 1)
+        return fail(BLASST_ERR_INVALID_ARG, "gaps/lambda_out missing or n < 1");
+    if (!(target >= 0.0 && target <= 1.0))
+        return fail(BLASST_ERR_INVALID_ARG, "target must be in [0, 1]");
+    std::vector<double> g;
+    g.reserve((size_t)n);
+    for (int64_t i = 0; i < n; ++i)
+        if (gaps[i] != -INFINITY && !std::isnan(gaps[i]))
+            g.push_back((double)gaps[i]);
+    const int64_t N = (int64_t)g.size();
+    if (N == 0)
+        return fail(BLASST_ERR_INVALID_ARG, "no visited pair in the gap map");
+    std::sort(g.begin(), g.end());
+    const int64_t k = std::min<int64_t>(N, std::max<int64_t>(0, (int64_t)std::ceil(target * (double)N)));
+    double thr; // ln(lambda)
+    if (k == 0)
+        thr = -INFINITY;
+    else if (k == N || std::isinf(g[(size_t)k]))
+        thr = g[(size_t)k - 1] + 1.0;
+    else
+        thr = 0.5 * (g[(size_t)k - 1] + g[(size_t)k]);
+    if (!(thr < 0.0))
+        thr = -0x1p-40; // lambda must stay below 1
+    const double lam = std::exp(thr);
+    if (reached_out) {
+        int64_t below = 0;
+        for (double x : g)
+            below += x < thr;
+        *reached_out = (double)below / (double)N;
+    }
+    *lambda_out = lam;
+    return BLASST_OK;
+}
+
+blasst_status blasst_calibrate_fit(const double *lambda_at_L, const int64_t *L, int n, double *a_out)
+{
+    if (lambda_at_L == nullptr || L == nullptr || a_out == nullptr || n < 1)
+        return fail(BLASST_ERR_INVALID_ARG, "inputs missing or n < 1");
+    double sum = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (!(lambda_at_L[i] > 0.0 && lambda_at_L[i] < 1.0) || L[i] <= 0)
+            return fail(BLASST_ERR_INVALID_ARG, "need 0 < lambda < 1 and L > 0 (entry %d)", i);
+        sum += std::log(lambda_at_L[i] * (double)L[i]);
+    }
+    *a_out = std::exp(sum / n);
+    return BLASST_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,396 @@
+// decode.hip -- split-K decode attention with BLASST block skipping, gfx950.
+//
+// Method: "BLASST: Dynamic BLocked Attention Sparsity via Softmax
+// Thresholding" (gist.science/pt/paper/2512.12087, section 2 and section 3
+// "Decode (limitado por memória)"): decode is memory bound, so the saving
+// that matters is the V-block load from HBM that a skipped block never
+// issues.  The Hindi explainer (gist.science/hi/paper/2512.12087, section 2,
+// "kernel optimisation") adds "batched load scheduling": several Q.K products
+// are computed before deciding which V blocks to fetch, to avoid pipeline
+// bubbles from conditional loads.
+//
+// Here a workgroup (4 waves) owns one (split, KV head, sequence) unit and walks
+// its key blocks in batches of 4, one block per wave:
+//  1. every wave loads its block's K straight into MFMA operand registers and
+//     computes S^T = K q^T (16x16x32 bf16 MFMA; the G <= 16 query heads that
+//     share the KV head are the 16 columns, padded with zeros);
+//  2. the 4 block maxima are exchanged through LDS and every wave evaluates
+//     the 4 decisions in order.  The running max never depends on earlier
+//     decisions (a skipped block has m~ < m + ln(lambda) <= m), so the
+//     decision of block i uses the exclusive prefix max of the block maxima;
+//  3. a wave whose block is executed loads V, stores it transposed in its own
+//     LDS slice and accumulates O^T += V^T P^T; a skipped block issues no V
+//     load at all.  The next batch's K loads are already in flight.
+// Each wave keeps its own online-softmax state; the 4 states are merged with
+// the log-sum-exp rule at the end, and across splits by the combine kernel.
+#include "device.h"
+#include "kernels.h"
+
+namespace blasst {
+
+namespace {
+
+constexpr int BC = 64;
+constexpr int NWD = 4; // waves per decode workgroup = blocks per batch
+
+template <int D, bool SKIP, bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_gqa_kernel(const DecodeArgs a)
+{
+    constexpr int VP = BC + 4;    // V^T pitch (elements)
+    constexpr int NS = D / 32;    // 32-wide k-steps of the QK product
+    constexpr int NDT = D / 16;   // 16-row d tiles of O^T
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[NWD][D * VP];
+    __shared__ float mblk[NWD][16];
+    __shared__ float mw_s[NWD][16], lw_s[NWD][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = lane & 15, grp = lane >> 4;
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int S = a.num_splits, G = a.G;
+    const bool want_maps = a.skip_map != nullptr || a.gap_map != nullptr;
+
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
+    const int nkb_b = (len + BC - 1) / BC;
+    const int per = (nkb_b + S - 1) / S;
+    const int jb = s * per;
+    const int je = (jb + per < nkb_b) ? jb + per : nkb_b;
+
+    const uint16_t *kp = a.k + b * a.k_sb + g * a.k_sh;
+    const uint16_t *vp = a.v + b * a.v_sb + g * a.v_sh;
+
+    // q^T as the B operand: lane (n, grp) holds q[head n][32 st + 8 grp .. +7].
+    bf16x8 qf[NS];
+    {
+        const uint16_t *qp = a.q + b * a.q_sb + (int64_t)(g * G + n) * a.q_sh;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            u32x4 u = {0, 0, 0, 0};
+            if (n < G)
+                u = *(const u32x4 *)(qp + 32 * st + 8 * grp);
+            qf[st] = as_bf16x8(u);
+        }
+    }
+
+    // K operand of S^T = K q^T for one 64-key block: tile kt = 16 keys,
+    // lane (m = key, grp) holds K[key][32 st + 8 grp .. +7].
+    u32x4 kr[4][NS];
+    auto load_k = [&](int j) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int key = j * BC + 16 * kt + n;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                u32x4 u = {0, 0, 0, 0};
+                if (j < je && key < len)
+                    u = *(const u32x4 *)(kp + (int64_t)key * a.k_st + 32 * st + 8 * grp);
+                kr[kt][st] = u;
+            }
+        }
+    };
+
+    f32x4 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = f32x4{};
+    float m2 = neg_inf(); // this wave's running max for head n (base 2)
+    float lsum = 0.f;     // this lane's partial running sum for head n
+    float pmax = neg_inf(); // exclusive prefix max of block maxima (decisions)
+    int n_skipped = 0;
+
+    // V load mapping: lane owns key quad (vq + 4 i) and 16-byte group vdg.
+    constexpr int DG = D / 8;
+    constexpr int VQ = 16 * DG / 64; // key quads per lane (4 for D=128)
+    const int vdg = lane % DG;
+    const int vq0 = lane / DG;
+    constexpr int QSTEP = 64 / DG;
+
+    int j0 = jb;
+    if (j0 < je)
+        load_k(j0 + w);
+    for (; j0 < je; j0 += NWD) {
+        const int j = j0 + w; // this wave's block
+        f32x4 sc[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            sc[kt] = f32x4{};
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+                sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
+        }
+        if (j0 + NWD < je)
+            load_k(j0 + NWD + w); // next batch in flight
+
+        // Mask keys past the sequence (and the whole block if j >= je).
+        const int k0 = j * BC;
+        if (j >= je || k0 + BC > len) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = k0 + 16 * kt + 4 * grp + r;
+                    if (j >= je || key >= len)
+                        sc[kt][r] = neg_inf();
+                }
+        }
+        float mt = neg_inf();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mt = fmaxf(mt, sc[kt][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mt2 = mt * a.scale_log2;
+        if (grp == 0)
+            mblk[w][n] = mt2;
+        __syncthreads();
+
+        // Decisions of the batch, in block order, identical in every wave.
+        bool my_skip = false;
+        int batch_skipped = 0;
+#pragma unroll
+        for (int i = 0; i < NWD; ++i) {
+            if (j0 + i >= je)
+                break;
+            const float mb = mblk[i][n];
+            const bool valid_head = n < G;
+            const float dgap = (!valid_head || mb == neg_inf()) ? neg_inf() : mb - pmax;
+            bool skip_i = false;
+            if (SKIP)
+                skip_i = __all(!(dgap >= a.lnlam2)) != 0;
+            if (want_maps) {
+                const float gg = wave_max(dgap);
+                if (w == 0 && lane == 0) {
+                    const int64_t idx = (int64_t)(b * a.Hkv + g) * a.nkb + j0 + i;
+                    if (a.skip_map)
+                        a.skip_map[idx] = skip_i ? 1 : 0;
+                    if (a.gap_map)
+                        a.gap_map[idx] = gg * 0.69314718055994531f;
+                }
+            }
+            pmax = fmaxf(pmax, mb);
+            if (i == w)
+                my_skip = skip_i;
+            batch_skipped += skip_i ? 1 : 0;
+        }
+        n_skipped += batch_skipped;
+
+        if (j < je && !my_skip) {
+            // V for an executed block only.
+            u32x4 vr[VQ][4];
+#pragma unroll
+            for (int qi = 0; qi < VQ; ++qi)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int key = k0 + 4 * (vq0 + QSTEP * qi) + k;
+                    u32x4 u = {0, 0, 0, 0};
+                    if (key < len)
+                        u = *(const u32x4 *)(vp + (int64_t)key * a.v_st + 8 * vdg);
+                    vr[qi][k] = u;
+                }
+            // Online-softmax update with this wave's running max.
+            const float mnew = fmaxf(m2, mt2);
+            const float msafe = mnew == neg_inf() ? 0.f : mnew;
+            const float alpha = exp2_hw(m2 - msafe);
+            float rs = 0.f;
+            bf16x8 pf[2];
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                f32x8 pv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p0 = exp2_hw(__builtin_fmaf(sc[2 * u2][r], a.scale_log2, -msafe));
+                    const float p1 = exp2_hw(__builtin_fmaf(sc[2 * u2 + 1][r], a.scale_log2, -msafe));
+                    pv[r] = p0;
+                    pv[r + 4] = p1;
+                    rs += p0 + p1;
+                }
+                pf[u2] = cvt_bf16x8(pv);
+            }
+            lsum = alpha * lsum + rs;
+            m2 = mnew;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                o[dt] *= alpha;
+            // Transposing store into this wave's V^T slice.
+            uint16_t *vt = Vt[w];
+#pragma unroll
+            for (int qi = 0; qi < VQ; ++qi) {
+                const int kq = vq0 + QSTEP * qi;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sh = (e & 1) * 16, ix = e >> 1;
+                    const uint32_t x0 = (vr[qi][0][ix] >> sh) & 0xffffu, x1 = (vr[qi][1][ix] >> sh) & 0xffffu;
+                    const uint32_t x2 = (vr[qi][2][ix] >> sh) & 0xffffu, x3 = (vr[qi][3][ix] >> sh) & 0xffffu;
+                    const u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
+                    *(u32x2 *)(vt + (8 * vdg + e) * VP + 4 * kq) = pk;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // O^T += V^T P^T: two k-steps of 32 keys.
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const uint16_t *row = vt + (16 * dt + n) * VP + 32 * u2 + 4 * grp;
+                    const u32x2 lo = *(const u32x2 *)row;
+                    const u32x2 hi = *(const u32x2 *)(row + 16);
+                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                    o[dt] = mfma16(as_bf16x8(va), pf[u2], o[dt]);
+                }
+        }
+        __syncthreads(); // mblk reuse; V^T slice reuse
+    }
+
+    // Merge the 4 wave states (log-sum-exp), then write O or the split partial.
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (grp == 0) {
+        mw_s[w][n] = m2;
+        lw_s[w][n] = l;
+    }
+    __syncthreads();
+    float M = neg_inf();
+#pragma unroll
+    for (int i = 0; i < NWD; ++i)
+        M = fmaxf(M, mw_s[i][n]);
+    const float Msafe = M == neg_inf() ? 0.f : M;
+    float ltot = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWD; ++i)
+        ltot += lw_s[i][n] * exp2_hw(mw_s[i][n] - Msafe);
+    const float cw = exp2_hw(m2 - Msafe);
+    // Stage the scaled wave accumulators as fp32 [wave][head][D] (reuses Vt).
+    float *stage = (float *)&Vt[0][0];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        *(f32x4 *)(stage + (w * 16 + n) * D + 16 * dt + 4 * grp) = o[dt] * cw;
+    __syncthreads();
+    // Every thread sums 4 waves for (head, d) pairs of the G valid heads.
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int hd = idx / D, d = idx % D;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < NWD; ++i)
+            acc += stage[(i * 16 + hd) * D + d];
+        float Mh = neg_inf(), lh = 0.f;
+#pragma unroll
+        for (int i = 0; i < NWD; ++i)
+            Mh = fmaxf(Mh, mw_s[i][hd]);
+        const float Mhs = Mh == neg_inf() ? 0.f : Mh;
+#pragma unroll
+        for (int i = 0; i < NWD; ++i)
+            lh += lw_s[i][hd] * exp2_hw(mw_s[i][hd] - Mhs);
+        if (S == 1) {
+            const float val = lh > 0.f ? acc / lh : 0.f;
+            const int64_t off = (int64_t)b * a.o_sb + (int64_t)(g * G + hd) * a.o_sh + d;
+            if (OUT_BF16)
+                ((__bf16 *)a.o)[off] = (__bf16)val;
+            else
+                ((float *)a.o)[off] = val;
+        } else {
+            const int64_t pu = ((int64_t)(b * a.Hkv + g) * S + s) * G + hd;
+            a.part_o[pu * D + d] = acc;
+            if (d == 0) {
+                a.part_ml[2 * pu] = Mh;
+                a.part_ml[2 * pu + 1] = lh;
+            }
+        }
+    }
+    (void)ltot;
+
+    if (tid == 0) {
+        if (want_maps && s == S - 1)
+            for (int j = nkb_b; j < a.nkb; ++j) {
+                const int64_t idx = (int64_t)(b * a.Hkv + g) * a.nkb + j;
+                if (a.skip_map)
+                    a.skip_map[idx] = 255;
+                if (a.gap_map)
+                    a.gap_map[idx] = neg_inf();
+            }
+        if (a.counters && je > jb) {
+            atomicAdd(a.counters, (unsigned long long)(je - jb));
+            atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
+        }
+    }
+}
+
+// Log-sum-exp merge of split partials: one workgroup per (query head, seq).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a, int dv)
+{
+    const int hq = blockIdx.x, b = blockIdx.y;
+    const int G = a.G, g = hq / G, hd = hq % G, S = a.num_splits;
+    const int64_t pu0 = ((int64_t)(b * a.Hkv + g) * S) * G + hd;
+    float M = neg_inf();
+    for (int s = 0; s < S; ++s) {
+        const float ls = a.part_ml[2 * (pu0 + (int64_t)s * G) + 1];
+        const float ms = a.part_ml[2 * (pu0 + (int64_t)s * G)];
+        if (ls > 0.f)
+            M = fmaxf(M, ms);
+    }
+    const float Ms = M == neg_inf() ? 0.f : M;
+    for (int d = threadIdx.x; d < dv; d += blockDim.x) {
+        float num = 0.f, den = 0.f;
+        for (int s = 0; s < S; ++s) {
+            const int64_t pu = pu0 + (int64_t)s * G;
+            const float ls = a.part_ml[2 * pu + 1];
+            if (!(ls > 0.f))
+                continue;
+            const float wgt = exp2_hw(a.part_ml[2 * pu] - Ms);
+            num += wgt * a.part_o[pu * dv + d];
+            den += wgt * ls;
+        }
+        const float val = den > 0.f ? num / den : 0.f;
+        const int64_t off = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + d;
+        if (OUT_BF16)
+            ((__bf16 *)a.o)[off] = (__bf16)val;
+        else
+            ((float *)a.o)[off] = val;
+    }
+}
+
+template <int D, bool SKIP, bool OUT_BF16>
+hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16>), dim3(a.num_splits, a.Hkv, a.B), dim3(256), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.num_splits == 1)
+        return e;
+    hipLaunchKernelGGL((decode_combine_kernel<OUT_BF16>), dim3(a.Hq, a.B), dim3(D < 256 ? D : 256), 0, stream, a,
+                       D);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16, hipStream_t stream)
+{
+    if (a.B == 0)
+        return hipSuccess;
+    if (dqk == dv && a.G <= 16) {
+        if (dqk == 128) {
+            if (skip)
+                return out_bf16 ? launch_gqa<128, true, true>(a, stream) : launch_gqa<128, true, false>(a, stream);
+            return out_bf16 ? launch_gqa<128, false, true>(a, stream) : launch_gqa<128, false, false>(a, stream);
+        }
+        if (dqk == 64) {
+            if (skip)
+                return out_bf16 ? launch_gqa<64, true, true>(a, stream) : launch_gqa<64, true, false>(a, stream);
+            return out_bf16 ? launch_gqa<64, false, true>(a, stream) : launch_gqa<64, false, false>(a, stream);
+        }
+    }
+    if (dqk == 576 && dv == 512 && a.G == 128)
+        return launch_mla(a, skip, out_bf16, stream);
+    return hipErrorInvalidValue;
+}
+
+} // namespace blasst

@@ -1,0 +1,47 @@
+// kernels.h -- internal launch interface between the C-ABI layer and the
+// HIP kernels of libblasst.so (not installed, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blasst {
+
+struct PrefillArgs {
+    const uint16_t *q, *k, *v; // bf16 bit patterns
+    void *o;
+    int64_t q_sb, q_sh, q_st, k_sb, k_sh, k_st, v_sb, v_sh, v_st, o_sb, o_sh, o_st;
+    int B, Hq, Hkv, L, nqt, nkb;
+    float scale_log2; // scale * log2(e): scores are kept in base-2 units
+    float lnlam2;     // log2(lambda), -inf for lambda = 0
+    uint8_t *skip_map;
+    float *gap_map;
+    unsigned long long *counters;
+};
+
+// Launches the prefill kernel for (d, tile_q, causal, skip, out dtype).
+// Returns hipErrorInvalidValue if no kernel is compiled for the combination.
+hipError_t launch_prefill(const PrefillArgs &a, int d, int tile_q, bool causal, bool skip,
+                          bool out_bf16, hipStream_t stream);
+
+struct DecodeArgs {
+    const uint16_t *q, *k, *v;
+    void *o;
+    int64_t q_sb, q_sh, k_sb, k_sh, k_st, v_sb, v_sh, v_st, o_sb, o_sh;
+    const int32_t *seq_lens;
+    int B, Hq, Hkv, G, Lmax, nkb, num_splits;
+    float scale_log2;
+    float lnlam2;
+    float *part_o;  // [B][Hkv][S][G][dv] fp32 (num_splits > 1)
+    float *part_ml; // [B][Hkv][S][G][2]  fp32 (max in log2 units, sum)
+    uint8_t *skip_map;
+    float *gap_map;
+    unsigned long long *counters;
+};
+
+// GQA/MQA/MHA decode (dqk = dv in {64, 128}, G <= 16) and latent (MLA) decode
+// (dqk 576, dv 512, G 128).  The combine kernel runs when num_splits > 1.
+hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16,
+                         hipStream_t stream);
+
+} // namespace blasst

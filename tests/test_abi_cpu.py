@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, rejects invalid arguments with the documented codes before any launch,
+and its host-only calibration calls agree with the oracle."""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_context_fa_amd as bl
+from long_context_fa_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "blasst.h")).read()
+    declared = set(re.findall(r"\b(blasst_[a-z_]+)\s*\(", header))
+    assert {"blasst_prefill", "blasst_decode", "blasst_decode_plan", "blasst_calibrate",
+            "blasst_calibrate_search", "blasst_calibrate_fit", "blasst_status_str",
+            "blasst_last_error", "blasst_abi_version"} <= declared
+    lib = bl.load_library()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert bl.blasst_abi_version() == 1
+    for s in range(5):
+        assert bl.blasst_status_str(s) != "unknown status"
+    assert bl.blasst_status_str(99) == "unknown status"
+
+
+def _bf16(*shape):
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def _prefill_err(**kw):
+    q, k, v = _bf16(1, 2, 128, 128), _bf16(1, 1, 128, 128), _bf16(1, 1, 128, 128)
+    args = dict(q=q, k=k, v=v, causal=True, lam=0.01, tile_q=128, block_k=64, stream=0)
+    args.update(kw)
+    with pytest.raises(bl.BlasstError) as ei:
+        bl.blasst_prefill(**args)
+    return ei.value.status
+
+
+@pytest.mark.parametrize("lam", [-0.1, 1.0, 1.5, float("nan")])
+def test_prefill_rejects_lambda(lam):
+    assert _prefill_err(lam=lam) == 1
+
+
+def test_prefill_rejects_shapes_and_tiles():
+    assert _prefill_err(k=_bf16(1, 3, 128, 128), v=_bf16(1, 3, 128, 128)) == 1  # Hq % Hkv
+    assert _prefill_err(tile_q=32) == 2
+    assert _prefill_err(block_k=32) == 2
+    q, k, v = _bf16(1, 2, 128, 96), _bf16(1, 1, 128, 96), _bf16(1, 1, 128, 96)
+    assert _prefill_err(q=q, k=k, v=v) == 2  # d = 96 not compiled
+    assert _prefill_err(q=torch.zeros(1, 2, 128, 128, dtype=torch.float32)) == 2  # fp32 q
+    qs = _bf16(1, 2, 128, 136)[..., :128]  # token stride 136: fine (multiple of 8)
+    qb = _bf16(1, 2, 128, 132)[..., :128]  # token stride 132: not 16-byte aligned rows
+    assert _prefill_err(q=qb) == 1
+    assert qs.stride(2) == 136
+
+
+def test_prefill_error_message_names_argument():
+    _prefill_err(lam=2.0)
+    assert "lambda" in bl.blasst_last_error()
+
+
+def _decode_err(**kw):
+    q = _bf16(2, 8, 128)
+    kc, vc = _bf16(2, 2, 256, 128), _bf16(2, 2, 256, 128)
+    lens = torch.full((2,), 256, dtype=torch.int32)
+    args = dict(q=q, k_cache=kc, v_cache=vc, seq_lens=lens, lam=0.01, stream=0,
+                workspace=torch.zeros(16, dtype=torch.uint8))
+    args.update(kw)
+    with pytest.raises(bl.BlasstError) as ei:
+        bl.blasst_decode(**args)
+    return ei.value.status
+
+
+def test_decode_rejects():
+    assert _decode_err(lam=1.0) == 1
+    assert _decode_err(seq_lens=None) == 1
+    assert _decode_err(num_splits=9) == 1          # more splits than blocks (4)
+    assert _decode_err(block_k=128) == 2
+    assert _decode_err(q=_bf16(2, 6, 128), k_cache=_bf16(2, 4, 256, 128), v_cache=_bf16(2, 4, 256, 128)) == 1
+    # latent form needs V to alias K
+    q = _bf16(1, 128, 576)
+    kc = _bf16(1, 1, 256, 576)
+    assert _decode_err(q=q, k_cache=kc, v_cache=_bf16(1, 1, 256, 576), dv=512,
+                       seq_lens=torch.full((1,), 256, dtype=torch.int32)) == 2
+    # more splits than one: workspace too small
+    assert _decode_err(num_splits=4, workspace=torch.zeros(16, dtype=torch.uint8)) == 3
+
+
+def test_decode_plan_host_only():
+    q = _bf16(148, 32, 128)
+    kc = _bf16(1, 8, 64, 128).expand(148, 8, 64, 128)  # plan reads no memory; shapes only
+    lens = torch.full((148,), 64, dtype=torch.int32)
+    S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=0.01)
+    assert S == 1 and ws == 0
+    q1 = _bf16(1, 32, 128)
+    kc1 = _bf16(1, 8, 32768, 128)
+    S, ws = bl.blasst_decode_plan(q1, kc1, kc1, torch.full((1,), 32768, dtype=torch.int32), lam=0.01)
+    assert S > 1 and ws >= 1 * 8 * S * 4 * (128 + 2) * 4
+    S2, _ = bl.blasst_decode_plan(q1, kc1, kc1, torch.full((1,), 32768, dtype=torch.int32), lam=0.01,
+                                  num_splits=7)
+    assert S2 == 7
+
+
+# ------------------------------------------------------ calibration (host C)
+def test_calibrate_matches_oracle():
+    targets, a = [0.3, 0.5, 0.7, 0.8], [3.0, 40.0, 900.0, 4000.0]
+    for target in [0.3, 0.41, 0.5, 0.66, 0.7, 0.79, 0.8]:
+        for L in [4096, 8192, 32768, 65536]:
+            lam = bl.blasst_calibrate(targets, a, target, L)
+            ref = oracle.lambda_from_table(targets, a, target, L)
+            assert abs(lam - ref) <= 1e-13 * ref
+
+
+def test_calibrate_rejects():
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_calibrate([0.3, 0.5], [3.0, 40.0], 0.9, 4096)   # outside the table
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_calibrate([0.5, 0.3], [3.0, 40.0], 0.4, 4096)   # not increasing
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_calibrate([0.5], [5000.0], 0.5, 4096)           # lambda >= 1
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_calibrate_fit([0.0], [100])
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_calibrate_search([-np.inf, -np.inf], 0.5)
+
+
+def test_calibrate_search_matches_oracle_quantile():
+    rng = np.random.default_rng(5)
+    gaps = rng.normal(-8, 4, size=5000).astype(np.float32)
+    gaps[:50] = np.inf            # first blocks
+    gaps[-300:] = -np.inf         # unvisited pairs are ignored
+    vis = gaps[gaps != -np.inf].astype(np.float64)
+    for target in [0.0, 0.1, 0.3, 0.5, 0.7, 0.8, 0.95]:
+        lam, reached = bl.blasst_calibrate_search(gaps, target)
+        lam_o, reached_o = oracle.lambda_for_target(vis, target)
+        assert abs(lam - lam_o) <= 1e-12 * max(lam_o, 1e-300)
+        assert reached == reached_o
+        assert abs(reached - target) <= 1 / vis.size + 1e-12 or target > 0.9
+
+
+def test_calibrate_fit_matches_oracle():
+    Ls = [4096, 8192, 16384, 32768, 65536]
+    lams = [1.1e-3, 6e-4, 2.7e-4, 1.4e-4, 6.9e-5]
+    assert abs(bl.blasst_calibrate_fit(lams, Ls) - oracle.fit_a(lams, Ls)) < 1e-12

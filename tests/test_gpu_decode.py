@@ -1,0 +1,106 @@
+"""GPU parity of blasst_decode (HIP, gfx950) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_fa_amd as bl
+import oracle
+from long_context_fa_amd import inputs
+from parity import (check_decisions, check_output, f64, gpu_decode, lambda_for, say,
+                    SPARSITY_ABS)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=False):
+    B, Hq, dqk = q.shape
+    Hkv = kc.shape[1]
+    say(f"[decode] {what}: q{tuple(q.shape)} cache{tuple(kc.shape)} lam={lam:.4g} splits={splits}")
+    o, skip, gap, cnt = gpu_decode(q, kc, vc, lens, lam=lam, num_splits=splits, dv=dv)
+    S_used, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=lam, num_splits=splits, dv=dv)
+    if unit_mask is None:
+        kk = f64(kc)
+        vv = kk[..., :dv] if mla else f64(vc)
+        ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S_used)
+        sel_u = np.ones((B, Hkv), bool)
+    else:
+        # copy only the sampled sequences to the host
+        bs = sorted({b for b, _ in unit_mask})
+        sub = {b: i for i, b in enumerate(bs)}
+        kk = f64(kc[bs])
+        vv = kk[..., :dv] if mla else f64(vc[bs])
+        m = np.zeros((len(bs), Hkv), np.uint8)
+        for b, g in unit_mask:
+            m[sub[b], g] = 1
+        ref_sub = oracle.decode(f64(q[bs]), kk, vv, lens[bs].cpu().numpy(), lam=lam, block_k=64,
+                                num_splits=S_used, unit_mask=m)
+        sel_u = np.zeros((B, Hkv), bool)
+        ref = {"skip": np.full(skip.shape, 255, np.uint8), "gap": np.full(gap.shape, -np.inf),
+               "o": np.zeros(o.shape), "visited": ref_sub["visited"], "skipped": ref_sub["skipped"]}
+        for b, g in unit_mask:
+            sel_u[b, g] = True
+            ref["skip"][b, g] = ref_sub["skip"][sub[b], g]
+            ref["gap"][b, g] = ref_sub["gap"][sub[b], g]
+        G = Hq // Hkv
+        for b in bs:
+            ref["o"][b] = ref_sub["o"][sub[b]]
+    nb = check_decisions(skip.cpu().numpy()[sel_u], gap.cpu().numpy()[sel_u], ref["skip"][sel_u],
+                         ref["gap"][sel_u], lam)
+    G = Hq // Hkv
+    rows = np.repeat(sel_u, G, axis=1)
+    check_output(o.cpu().numpy()[rows], ref["o"][rows], what)
+    gs = skip.cpu().numpy()[sel_u]
+    g_frac = (gs == 1).sum() / max(1, (gs != 255).sum())
+    r_frac = ref["skipped"] / max(1, ref["visited"])
+    say(f"  splits {S_used}; sparsity gpu {g_frac:.4f} oracle {r_frac:.4f}; band {nb}")
+    assert abs(g_frac - r_frac) <= SPARSITY_ABS
+    if unit_mask is None:
+        assert cnt[0] == ref["visited"] and abs(cnt[1] - ref["skipped"]) <= nb
+    return cnt, S_used
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 16])
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 4), (128, 1), (128, 16), (64, 8)])
+def test_parity_ragged(d, G, splits):
+    B, Hkv, Lmax = 3, 2, 1000
+    q, kc, vc, _ = inputs.decode_inputs(B, G * Hkv, Hkv, Lmax, d, device=DEV, seed=11 + d + G + splits)
+    lens = torch.tensor([1000, 1, 333], dtype=torch.int32, device=DEV)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=splits)
+    lam, _ = lambda_for(gap0, 0.6)
+    _run(q, kc, vc, lens, lam=lam, splits=splits, what=f"ragged d={d} G={G}")
+
+
+def test_dense_decode_matches_oracle():
+    q, kc, vc, lens = inputs.decode_inputs(2, 8, 2, 4096, 128, device=DEV, seed=5)
+    cnt, _ = _run(q, kc, vc, lens, lam=0.0, splits=4, what="dense")
+    assert cnt[1] == 0
+
+
+def test_parity_gqa_decode_full_length():
+    """4 sequences of the 32K GQA decode shape (32/8 heads, d 128), every unit checked."""
+    q, kc, vc, lens = inputs.decode_inputs(4, 32, 8, 32768, 128, n_random=8, device=DEV, seed=1002)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=1)
+    lam, reached = lambda_for(gap0, 0.7)
+    cnt, _ = _run(q, kc, vc, lens, lam=lam, splits=1, what="4x32/8x32768x128")
+    assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
+
+
+def test_parity_gqa_decode_148_sequences_sampled():
+    """The full 148-sequence, 32K, 32/8-head decode step; oracle on sampled units."""
+    q, kc, vc, lens = inputs.decode_inputs(148, 32, 8, 32768, 128, n_random=8, device=DEV, seed=1002)
+    S, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=0.01)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=S)
+    lam, reached = lambda_for(gap0, 0.7)
+    units = [(0, 0), (17, 3), (63, 7), (100, 5), (147, 2), (147, 7)]
+    cnt, _ = _run(q, kc, vc, lens, lam=lam, splits=S, what="148x32/8x32768x128", unit_mask=units)
+    assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
+
+
+def test_bf16_output_and_determinism():
+    q, kc, vc, lens = inputs.decode_inputs(3, 8, 2, 2048, 128, device=DEV, seed=9)
+    o1, s1, g1, _ = gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=2)
+    o2, s2, g2, _ = gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=2)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(g1, g2)
+    o3, _, _, _ = gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=2, out_dtype=torch.bfloat16)
+    assert torch.equal(o3.float(), o1.to(torch.bfloat16).float())
