@@ -18,9 +18,11 @@
 //     the 4 decisions in order.  The running max never depends on earlier
 //     decisions (a skipped block has m~ < m + ln(lambda) <= m), so the
 //     decision of block i uses the exclusive prefix max of the block maxima;
-//  3. a wave whose block is executed loads V, stores it transposed in its own
-//     LDS slice and accumulates O^T += V^T P^T; a skipped block issues no V
-//     load at all.  The next batch's K loads are already in flight.
+//  3. a wave whose block is executed copies V global -> LDS into its own slice
+//     (global_load_lds, no registers), then issues the next batch's K loads,
+//     computes the exponentials while both are in flight, and accumulates
+//     O^T += V^T P^T with the V^T operand taken by the gfx950 transpose read.
+//     A skipped block issues no V load at all.
 // Each wave keeps its own online-softmax state; the 4 states are merged with
 // the log-sum-exp rule at the end, and across splits by the combine kernel.
 #include "device.h"
@@ -37,14 +39,20 @@ template <int D, bool SKIP, bool OUT_BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_kernel(const DecodeArgs a)
 {
-    constexpr int VP = BC + 4;    // V^T pitch (elements)
-    constexpr int NS = D / 32;    // 32-wide k-steps of the QK product
-    constexpr int NDT = D / 16;   // 16-row d tiles of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[NWD][D * VP];
-    __shared__ float mblk[NWD][16];
+    constexpr int RB = D * 2;          // bytes per V row
+    constexpr int DG = D / 8;          // 16-byte chunks per row
+    constexpr int TB = BC * RB;        // bytes per V tile
+    constexpr int VI = TB / 1024;      // 1 KB copies per V tile (one wave copies a tile)
+    constexpr int RPI = 64 / DG;       // rows per copy
+    constexpr int NS = D / 32;         // 32-wide k-steps of the QK product
+    constexpr int NDT = D / 16;        // 16-row d tiles of O^T
+    constexpr int KLOADS = 4 * NS;     // K register loads per wave per block
+    __shared__ __attribute__((aligned(1024))) char vsm[NWD * TB];
+    __shared__ float mblk[2][NWD][16];
     __shared__ float mw_s[NWD][16], lw_s[NWD][16];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, grp = lane >> 4;
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int S = a.num_splits, G = a.G;
@@ -59,6 +67,7 @@ void decode_gqa_kernel(const DecodeArgs a)
 
     const uint16_t *kp = a.k + b * a.k_sb + g * a.k_sh;
     const uint16_t *vp = a.v + b * a.v_sb + g * a.v_sh;
+    char *const vt = vsm + w * TB; // this wave's V slice
 
     // q^T as the B operand: lane (n, grp) holds q[head n][32 st + 8 grp .. +7].
     bf16x8 qf[NS];
@@ -73,20 +82,34 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
     }
 
-    // K operand of S^T = K q^T for one 64-key block: tile kt = 16 keys,
-    // lane (m = key, grp) holds K[key][32 st + 8 grp .. +7].
+    // K operand of S^T = K q^T for one 64-key block, straight from HBM into
+    // registers: tile kt = 16 keys, lane (m = key, grp) holds
+    // K[key][32 st + 8 grp .. +7].  Every lane always issues all KLOADS loads:
+    // keys outside the split read row len-1 (finite; their scores are masked
+    // to -inf below), because the V wait counts on exactly KLOADS younger
+    // vector-memory operations.
     u32x4 kr[4][NS];
     auto load_k = [&](int j) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int key = j * BC + 16 * kt + n;
+            const int kc = (j < je && key < len) ? key : len - 1;
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                u32x4 u = {0, 0, 0, 0};
-                if (j < je && key < len)
-                    u = *(const u32x4 *)(kp + (int64_t)key * a.k_st + 32 * st + 8 * grp);
-                kr[kt][st] = u;
-            }
+            for (int st = 0; st < NS; ++st)
+                kr[kt][st] = __builtin_nontemporal_load((const u32x4 *)(kp + (int64_t)kc * a.k_st + 32 * st + 8 * grp));
+        }
+    };
+    // V tile of block j -> this wave's slice, row-major with the 16-byte
+    // chunks XOR-swizzled by row (rows past len re-read row len-1: finite
+    // values whose probabilities are exactly 0).
+    auto copy_v = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const int row = i * RPI + lane / DG;
+            const int c = (lane % DG) ^ (row & (DG - 1));
+            int key = j * BC + row;
+            key = key < len ? key : len - 1;
+            copy16_to_lds(vp + (int64_t)key * a.v_st + c * 8, vt + i * 1024);
         }
     };
 
@@ -94,23 +117,20 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
         o[dt] = f32x4{};
-    float m2 = neg_inf(); // this wave's running max for head n (base 2)
-    float lsum = 0.f;     // this lane's partial running sum for head n
+    float m2 = neg_inf();   // this wave's running max for head n (base 2)
+    float lsum = 0.f;       // this lane's partial running sum for head n
     float pmax = neg_inf(); // exclusive prefix max of block maxima (decisions)
     int n_skipped = 0;
 
-    // V load mapping: lane owns key quad (vq + 4 i) and 16-byte group vdg.
-    constexpr int DG = D / 8;
-    constexpr int VQ = 16 * DG / 64; // key quads per lane (4 for D=128)
-    const int vdg = lane % DG;
-    const int vq0 = lane / DG;
-    constexpr int QSTEP = 64 / DG;
+    // Transpose-read addressing of the V^T operand (16x16x32 A layout).
+    const int vj = (lane & 15) >> 2, vq = lane & 3, vgrp = lane >> 4;
 
-    int j0 = jb;
-    if (j0 < je)
-        load_k(j0 + w);
-    for (; j0 < je; j0 += NWD) {
+    if (jb < je)
+        load_k(jb + w);
+    int it = 0;
+    for (int j0 = jb; j0 < je; j0 += NWD, ++it) {
         const int j = j0 + w; // this wave's block
+        const int par = it & 1;
         f32x4 sc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -119,9 +139,6 @@ void decode_gqa_kernel(const DecodeArgs a)
             for (int st = 0; st < NS; ++st)
                 sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
         }
-        if (j0 + NWD < je)
-            load_k(j0 + NWD + w); // next batch in flight
-
         // Mask keys past the sequence (and the whole block if j >= je).
         const int k0 = j * BC;
         if (j >= je || k0 + BC > len) {
@@ -144,8 +161,8 @@ void decode_gqa_kernel(const DecodeArgs a)
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mt2 = mt * a.scale_log2;
         if (grp == 0)
-            mblk[w][n] = mt2;
-        __syncthreads();
+            mblk[par][w][n] = mt2;
+        lds_barrier();
 
         // Decisions of the batch, in block order, identical in every wave.
         bool my_skip = false;
@@ -154,7 +171,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         for (int i = 0; i < NWD; ++i) {
             if (j0 + i >= je)
                 break;
-            const float mb = mblk[i][n];
+            const float mb = mblk[par][i][n];
             const bool valid_head = n < G;
             const float dgap = (!valid_head || mb == neg_inf()) ? neg_inf() : mb - pmax;
             bool skip_i = false;
@@ -177,19 +194,14 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
         n_skipped += batch_skipped;
 
-        if (j < je && !my_skip) {
-            // V for an executed block only.
-            u32x4 vr[VQ][4];
-#pragma unroll
-            for (int qi = 0; qi < VQ; ++qi)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int key = k0 + 4 * (vq0 + QSTEP * qi) + k;
-                    u32x4 u = {0, 0, 0, 0};
-                    if (key < len)
-                        u = *(const u32x4 *)(vp + (int64_t)key * a.v_st + 8 * vdg);
-                    vr[qi][k] = u;
-                }
+        const bool exec = j < je && !my_skip;
+        if (exec)
+            copy_v(j); // V only for an executed block
+        const bool more = j0 + NWD < je;
+        if (more)
+            load_k(j0 + NWD + w); // next batch's K in flight
+
+        if (exec) {
             // Online-softmax update with this wave's running max.
             const float mnew = fmaxf(m2, mt2);
             const float msafe = mnew == neg_inf() ? 0.f : mnew;
@@ -214,36 +226,27 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 o[dt] *= alpha;
-            // Transposing store into this wave's V^T slice.
-            uint16_t *vt = Vt[w];
-#pragma unroll
-            for (int qi = 0; qi < VQ; ++qi) {
-                const int kq = vq0 + QSTEP * qi;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int sh = (e & 1) * 16, ix = e >> 1;
-                    const uint32_t x0 = (vr[qi][0][ix] >> sh) & 0xffffu, x1 = (vr[qi][1][ix] >> sh) & 0xffffu;
-                    const uint32_t x2 = (vr[qi][2][ix] >> sh) & 0xffffu, x3 = (vr[qi][3][ix] >> sh) & 0xffffu;
-                    const u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-                    *(u32x2 *)(vt + (8 * vdg + e) * VP + 4 * kq) = pk;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // O^T += V^T P^T: two k-steps of 32 keys.
+            // The V copy is older than the next K loads: wait for it only.
+            if (more)
+                wait_vmcnt<KLOADS>();
+            else
+                wait_vmcnt<0>();
+            compiler_fence();
+            // O^T += V^T P^T: two k-steps of 32 keys.  A operand lane (m = d,
+            // grp) slot i <-> key 32 u2 + 16 (i / 4) + 4 grp + i % 4.
 #pragma unroll
             for (int u2 = 0; u2 < 2; ++u2)
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    const uint16_t *row = vt + (16 * dt + n) * VP + 32 * u2 + 4 * grp;
-                    const u32x2 lo = *(const u32x2 *)row;
-                    const u32x2 hi = *(const u32x2 *)(row + 16);
-                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                    const int c = 2 * dt + (vq >> 1);
+                    const int ra = 32 * u2 + 4 * vgrp + vj, rb = ra + 16;
+                    const i16x4 x0 = lds_read_tr16(vt + ra * RB + ((c ^ (ra & (DG - 1))) * 16) + (vq & 1) * 8);
+                    const i16x4 x1 = lds_read_tr16(vt + rb * RB + ((c ^ (rb & (DG - 1))) * 16) + (vq & 1) * 8);
+                    const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+                    const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
                     o[dt] = mfma16(as_bf16x8(va), pf[u2], o[dt]);
                 }
         }
-        __syncthreads(); // mblk reuse; V^T slice reuse
     }
 
     // Merge the 4 wave states (log-sum-exp), then write O or the split partial.
@@ -254,24 +257,19 @@ void decode_gqa_kernel(const DecodeArgs a)
         mw_s[w][n] = m2;
         lw_s[w][n] = l;
     }
-    __syncthreads();
+    lds_barrier();
     float M = neg_inf();
 #pragma unroll
     for (int i = 0; i < NWD; ++i)
         M = fmaxf(M, mw_s[i][n]);
     const float Msafe = M == neg_inf() ? 0.f : M;
-    float ltot = 0.f;
-#pragma unroll
-    for (int i = 0; i < NWD; ++i)
-        ltot += lw_s[i][n] * exp2_hw(mw_s[i][n] - Msafe);
     const float cw = exp2_hw(m2 - Msafe);
-    // Stage the scaled wave accumulators as fp32 [wave][head][D] (reuses Vt).
-    float *stage = (float *)&Vt[0][0];
+    // Stage the scaled wave accumulators as fp32 [wave][head][D] (reuses the V slices).
+    float *stage = (float *)vsm;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
         *(f32x4 *)(stage + (w * 16 + n) * D + 16 * dt + 4 * grp) = o[dt] * cw;
-    __syncthreads();
-    // Every thread sums 4 waves for (head, d) pairs of the G valid heads.
+    lds_barrier();
     for (int idx = tid; idx < G * D; idx += 256) {
         const int hd = idx / D, d = idx % D;
         float acc = 0.f;
@@ -302,7 +300,6 @@ void decode_gqa_kernel(const DecodeArgs a)
             }
         }
     }
-    (void)ltot;
 
     if (tid == 0) {
         if (want_maps && s == S - 1)

@@ -48,3 +48,59 @@ __device__ __forceinline__ float wave_max(float x)
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 } // namespace blasst
+
+namespace blasst {
+
+// s_waitcnt that waits until at most N vector-memory operations (including
+// global->LDS copies) of this wave are outstanding; other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 16-byte global -> LDS copy (global_load_lds_dwordx4); the wave's 64 lanes
+// fill 1024 consecutive LDS bytes starting at lds_base (wave-uniform).  It is
+// issued from inline asm so that the compiler does not add its own
+// conservative vmcnt(0) waits before every later LDS read: the kernels wait
+// for these copies explicitly (wait_vmcnt) before the barrier that publishes
+// the data.  The instruction writes no register.
+// (m0 is set right before the copy; the compiler uses it nowhere else in
+// these kernels, so the clobber is honoured in practice.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Compiler-level memory barrier (no instruction): keeps LDS reads below an
+// explicit wait_vmcnt for copies the compiler does not track.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier that orders LDS accesses only: global memory is not
+// fenced, so outstanding global->LDS copies and global stores are not drained
+// (the kernels wait for their copies explicitly before the barrier).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// gfx950 LDS transpose read of 16-bit data.  Within each group of 16 lanes,
+// lane s supplies an 8-byte address; lane i receives element (i % 4) of the
+// data addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that order.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+}
+
+} // namespace blasst

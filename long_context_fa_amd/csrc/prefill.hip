@@ -16,13 +16,22 @@
 //    MFMA: lane (n, h) holds query n's scores for 32 of the 64 keys, so the
 //    row max, running max, running sum and rescale are per-lane scalars and
 //    the only cross-lane step is one exchange with lane n+32.
-//  * The P^T registers feed the P.V product O^T += V^T P^T directly as the
-//    B operand (no shuffles); V^T is staged in LDS by a transposing store.
+//  * The P^T registers feed O^T += V^T P^T directly as the B operand.  V stays
+//    row-major in LDS; its A operand (4 consecutive keys of one feature per
+//    lane) comes from the gfx950 transpose read ds_read_b64_tr_b16.
+//  * K and V tiles are copied global -> LDS with global_load_lds_dwordx4 (no
+//    registers), into a row-major layout whose 16-byte chunks are XOR-swizzled
+//    by row so that MFMA operand reads are bank-conflict free.  K runs in a
+//    ring of 3 buffers, two blocks ahead of the scores; V is requested only
+//    once the block's vote says it executes.
 //  * Skip vote: a lane meets the test when its row does; the tile skips when
 //    every valid row of every wave does (one LDS word per wave, exchanged at
-//    the barrier the K double-use needs anyway), so the branch is uniform.
+//    the barrier that also publishes the next K tile), so the branch is
+//    uniform across the workgroup.
 //  * Base-2 arithmetic: scores are scaled by scale*log2(e) in fp32, the test
-//    compares against log2(lambda), exponentials are v_exp_f32.
+//    compares against log2(lambda), exponentials are v_exp_f32.  The
+//    accumulator rescale is skipped when no row of the wave raised its max
+//    (after the first blocks the running max rarely moves).
 #include "device.h"
 #include "kernels.h"
 
@@ -30,34 +39,55 @@ namespace blasst {
 
 namespace {
 
-constexpr int BC = 64; // key block
+constexpr int BC = 64;       // key block
+constexpr int NKBUF = 3;     // K ring depth
 
 template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16>
-__global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, 2))) void prefill_kernel(const PrefillArgs a)
+__global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, 2)))
+void prefill_kernel(const PrefillArgs a)
 {
-    constexpr int NW = BR / 32;         // waves
-    constexpr int NT = 64 * NW;         // threads
-    constexpr int KP = D + 8;           // K row pitch in LDS (elements)
-    constexpr int VP = BC + 4;          // V^T row pitch in LDS (elements)
-    constexpr int DG = D / 8;           // 16-byte groups per row
-    constexpr int KCH = BC * DG / NT;   // K chunks of 16 B per thread
-    constexpr int VK = BC * DG / NT;    // keys per thread in the V^T store
-    static_assert(KCH >= 1 && VK >= 2 && VK % 2 == 0, "tile shape");
+    constexpr int NW = BR / 32;          // waves
+    constexpr int RB = D * 2;            // bytes per K/V row
+    constexpr int DG = D / 8;            // 16-byte chunks per row
+    constexpr int TB = BC * RB;          // bytes per tile
+    constexpr int KI = TB / 1024 / NW;   // 1 KB copy instructions per tile per wave
+    constexpr int RPI = 64 / DG;         // rows per copy instruction
+    static_assert(KI >= 1 && KI * NW * 1024 == TB, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-    __shared__ int vote[NW];
-    __shared__ float gapw[NW];
+    __shared__ __attribute__((aligned(1024))) char smem[(NKBUF + 1) * TB];
+    __shared__ int vote[2][NW];
+    __shared__ float gapw[2][NW];
+    char *const Vb = smem + NKBUF * TB;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hh = lane >> 5;
 
-    // Longest (latest) query tiles first; heads and batches inner.
-    const int per_t = a.Hq * a.B;
-    const int t = a.nqt - 1 - (int)blockIdx.x / per_t;
-    const int rem = (int)blockIdx.x % per_t;
-    const int h = rem % a.Hq, b = rem / a.Hq;
-    const int hk = h / (a.Hq / a.Hkv);
+    // Unit mapping.  Longest (latest) query tiles first.  Consecutive
+    // workgroups go to the 8 XCDs in turn; when the KV groups divide evenly,
+    // XCD x only sees KV groups x, x+8, ... so their K/V stay in its L2.
+    const int G = a.Hq / a.Hkv;
+    const int nkvg = a.B * a.Hkv;
+    int t, h, b;
+    {
+        const int k = blockIdx.x;
+        if (nkvg % 8 == 0) {
+            const int xcd = k & 7, s = k >> 3;
+            const int per_t = (nkvg / 8) * G;
+            t = a.nqt - 1 - s / per_t;
+            const int r = s % per_t;
+            const int kvg = (r / G) * 8 + xcd;
+            b = kvg / a.Hkv;
+            h = (kvg % a.Hkv) * G + r % G;
+        } else {
+            const int per_t = a.Hq * a.B;
+            t = a.nqt - 1 - k / per_t;
+            const int r = k % per_t;
+            h = r % a.Hq;
+            b = r / a.Hq;
+        }
+    }
+    const int hk = h / G;
     const int r0 = t * BR;
     const int L = a.L;
     const int qrow = r0 + 32 * w + n;
@@ -81,55 +111,59 @@ __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 
     const int last_row = (r0 + BR < L ? r0 + BR : L) - 1;
     const int nvis = CAUSAL ? (last_row / BC + 1 < a.nkb ? last_row / BC + 1 : a.nkb) : a.nkb;
 
-    // K tile: row-major [64][D] in LDS, 16-byte chunks, coalesced rows.
-    u32x4 kr[KCH];
-    auto load_k = [&](int j) {
+    // Tile copy: wave w fills rows [w*KI*RPI, (w+1)*KI*RPI); lane -> (row, chunk)
+    // with the chunk XOR-swizzled by the row.  Rows past L re-read row L-1
+    // (finite data; those keys are masked to -inf).
+    auto copy_tile = [&](const uint16_t *base, int64_t st, int j, char *dst) {
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT, row = c / DG, col = c % DG;
-            const int key = j * BC + row;
-            u32x4 u = {0, 0, 0, 0};
-            if (key < L)
-                u = *(const u32x4 *)(kp + (int64_t)key * a.k_st + col * 8);
-            kr[i] = u;
+        for (int i = 0; i < KI; ++i) {
+            const int ins = w * KI + i;
+            const int row = ins * RPI + lane / DG;
+            const int c = (lane % DG) ^ (row & (DG - 1));
+            int key = j * BC + row;
+            key = key < L ? key : L - 1;
+            copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024);
         }
     };
-    auto store_k = [&]() {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT, row = c / DG, col = c % DG;
-            *(u32x4 *)(Ks + row * KP + col * 8) = kr[i];
-        }
-    };
-    // V tile: thread owns VK consecutive keys x 8 features; stored transposed
-    // ([D][64] with pitch VP) so that a lane's MFMA operand is 4 consecutive keys.
-    const int vkg = (tid & 3) + 4 * (tid / (4 * DG));
-    const int vdg = (tid >> 2) % DG;
-    u32x4 vr[VK];
+    auto kbuf = [&](int j) { return smem + (j % NKBUF) * TB; };
 
-    load_k(0);
-    store_k();
-    __syncthreads();
+    // Prologue: K_0..K_2 into the ring.
+    copy_tile(kp, a.k_st, 0, kbuf(0));
+    if (1 < nvis)
+        copy_tile(kp, a.k_st, 1, kbuf(1));
+    if (2 < nvis)
+        copy_tile(kp, a.k_st, 2, kbuf(2));
+    if (2 < nvis)
+        wait_vmcnt<2 * KI>();
+    else if (1 < nvis)
+        wait_vmcnt<KI>();
+    else
+        wait_vmcnt<0>();
+    lds_barrier();
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
         o[dt] = f32x16{};
-    float m2 = neg_inf(); // running max of this lane's row (base-2 units)
-    float lsum = 0.f;     // running sum over this lane's half of each block
+    float m2 = neg_inf();   // running max of this lane's row (base 2)
+    float lsum = 0.f;       // running sum over this lane's half of each block
     int n_skipped = 0;
 
-    for (int j = 0; j < nvis; ++j) {
-        if (j + 1 < nvis)
-            load_k(j + 1);
+    // V operand addressing for the transpose read (fixed per lane).
+    const int vg = lane >> 4, vs = lane & 15;
+    const int vmb = vg & 1, vh = vg >> 1, vj = vs >> 2, vq = vs & 3;
 
+    for (int j = 0; j < nvis; ++j) {
+        const char *kb = kbuf(j);
         // S^T = K_j Q^T: two 32-key tiles.
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                bf16x8 ka = as_bf16x8(*(const u32x4 *)(Ks + (32 * kt + n) * KP + 16 * kk + 8 * hh));
+                const int row = 32 * kt + n;
+                const int c = (2 * kk + hh) ^ (row & (DG - 1));
+                const bf16x8 ka = as_bf16x8(*(const u32x4 *)(kb + row * RB + c * 16));
                 s[kt] = mfma32(ka, qf[kk], s[kt]);
             }
         }
@@ -154,37 +188,42 @@ __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mt2 = mt * a.scale_log2; // block-local row max, base 2
 
-        bool skip = false;
+        const int par = j & 1;
         if (SKIP || want_maps) {
             // d = m~ - m with the infinity rules: -inf if the row sees no key in
             // the block, +inf if the row has no running max yet.
             const float dgap = (!row_valid || mt2 == neg_inf()) ? neg_inf() : mt2 - m2;
             if (SKIP) {
-                const bool ok = !(dgap >= a.lnlam2); // also true for -inf rows
-                const int wall = __all(ok);
+                const int wall = __all(!(dgap >= a.lnlam2)); // -inf rows always meet it
                 if (lane == 0)
-                    vote[w] = wall;
+                    vote[par][w] = wall;
             }
             if (want_maps) {
                 const float wg = wave_max(dgap);
                 if (lane == 0)
-                    gapw[w] = wg;
+                    gapw[par][w] = wg;
             }
         }
-        __syncthreads(); // (A) votes visible; every wave is done reading Ks
+        // Own part of K_{j+1} landed (only K_{j+2} may still be in flight).
+        if (j + 2 < nvis)
+            wait_vmcnt<KI>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier(); // (A) votes, K_{j+1} visible; K_j fully consumed
 
+        bool skip = false;
         if (SKIP) {
             int all = 1;
 #pragma unroll
             for (int i = 0; i < NW; ++i)
-                all &= vote[i];
+                all &= vote[par][i];
             skip = all != 0;
         }
         if (want_maps && tid == 0) {
             float g = neg_inf();
 #pragma unroll
             for (int i = 0; i < NW; ++i)
-                g = fmaxf(g, gapw[i]);
+                g = fmaxf(g, gapw[par][i]);
             const int64_t idx = ((int64_t)(b * a.Hq + h) * a.nqt + t) * a.nkb + j;
             if (a.skip_map)
                 a.skip_map[idx] = skip ? 1 : 0;
@@ -192,20 +231,24 @@ __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 
                 a.gap_map[idx] = g * 0.69314718055994531f; // back to natural log
         }
 
+        if (!skip)
+            copy_tile(vp, a.v_st, j, Vb); // V_j only for an executed block
+        const bool k3 = j + 3 < nvis;
+        if (k3)
+            copy_tile(kp, a.k_st, j + 3, kbuf(j)); // K ring refill
+
         if (!skip) {
-            // V_j loads, issued only for executed blocks.
-#pragma unroll
-            for (int i = 0; i < VK; ++i) {
-                const int key = k0 + vkg * VK + i;
-                u32x4 u = {0, 0, 0, 0};
-                if (key < L)
-                    u = *(const u32x4 *)(vp + (int64_t)key * a.v_st + vdg * 8);
-                vr[i] = u;
-            }
             // Online-softmax update of this lane's row.
             const float mnew = fmaxf(m2, mt2);
-            const float msafe = mnew == neg_inf() ? 0.f : mnew;
-            const float alpha = exp2_hw(m2 - msafe);
+            if (__any(mnew > m2)) {
+                const float alpha = mnew > m2 ? exp2_hw(m2 - mnew) : 1.f; // 0 on the first block
+                lsum *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+                    o[dt] *= alpha;
+            }
+            m2 = mnew;
+            const float msafe = m2 == neg_inf() ? 0.f : m2;
             float rs = 0.f;
             bf16x8 pf[4];
 #pragma unroll
@@ -222,42 +265,30 @@ __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 
                 pf[2 * kt] = cvt_bf16x8(lo);
                 pf[2 * kt + 1] = cvt_bf16x8(hi);
             }
-            lsum = alpha * lsum + rs;
-            m2 = mnew;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-                o[dt] *= alpha;
-            // Transposing store of V_j into Vt[d][key].
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = vdg * 8 + e;
-#pragma unroll
-                for (int i = 0; i < VK; i += 2) {
-                    const uint32_t x = vr[i][e >> 1], y = vr[i + 1][e >> 1];
-                    const uint32_t packed = (e & 1) ? ((x >> 16) | (y & 0xffff0000u))
-                                                    : ((x & 0xffffu) | (y << 16));
-                    *(uint32_t *)(Vt + d * VP + vkg * VK + i) = packed;
-                }
-            }
-            __syncthreads(); // (B) V^T visible
+            lsum += rs;
+            // Own part of V_j landed (K_{j+3} may still be in flight).
+            if (k3)
+                wait_vmcnt<KI>();
+            else
+                wait_vmcnt<0>();
+            lds_barrier(); // (B) V_j visible
             // O^T += V^T P^T, k-steps of 16 keys.
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-                    const uint16_t *vrow = Vt + (32 * dt + n) * VP + 16 * u + 4 * hh;
-                    const u32x2 lo = *(const u32x2 *)vrow;
-                    const u32x2 hi = *(const u32x2 *)(vrow + 8);
-                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                    const int c = 4 * dt + 2 * vmb + (vq >> 1);
+                    const int ra = 16 * u + 4 * vh + vj, rb = ra + 8;
+                    const i16x4 x0 = lds_read_tr16(Vb + ra * RB + ((c ^ (ra & (DG - 1))) * 16) + (vq & 1) * 8);
+                    const i16x4 x1 = lds_read_tr16(Vb + rb * RB + ((c ^ (rb & (DG - 1))) * 16) + (vq & 1) * 8);
+                    const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+                    const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
                     o[dt] = mfma32(as_bf16x8(va), pf[u], o[dt]);
                 }
             }
         } else {
             ++n_skipped;
         }
-        if (j + 1 < nvis)
-            store_k();
-        __syncthreads(); // (C) next K visible; V^T reads done
     }
 
     // Finalize: O = acc / l, l summed over the two lane halves.
