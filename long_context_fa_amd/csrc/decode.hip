@@ -106,7 +106,7 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int row = i * RPI + lane / DG;
-            const int c = (lane % DG) ^ (row & (DG - 1));
+            const int c = (lane % DG) ^ swz<DG>(row);
             int key = j * BC + row;
             key = key < len ? key : len - 1;
             copy16_to_lds(vp + (int64_t)key * a.v_st + c * 8, vt + i * 1024);
@@ -240,8 +240,8 @@ void decode_gqa_kernel(const DecodeArgs a)
                 for (int dt = 0; dt < NDT; ++dt) {
                     const int c = 2 * dt + (vq >> 1);
                     const int ra = 32 * u2 + 4 * vgrp + vj, rb = ra + 16;
-                    const i16x4 x0 = lds_read_tr16(vt + ra * RB + ((c ^ (ra & (DG - 1))) * 16) + (vq & 1) * 8);
-                    const i16x4 x1 = lds_read_tr16(vt + rb * RB + ((c ^ (rb & (DG - 1))) * 16) + (vq & 1) * 8);
+                    const i16x4 x0 = lds_read_tr16(vt + ra * RB + ((c ^ swz<DG>(ra)) * 16) + (vq & 1) * 8);
+                    const i16x4 x1 = lds_read_tr16(vt + rb * RB + ((c ^ swz<DG>(rb)) * 16) + (vq & 1) * 8);
                     const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
                     const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
                     o[dt] = mfma16(as_bf16x8(va), pf[u2], o[dt]);

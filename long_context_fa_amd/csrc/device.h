@@ -79,11 +79,39 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
 }
+
+// Same copy with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
+// byte offset: the per-block address arithmetic becomes one scalar add.
+__device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff, void *lds_base)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    // readfirstlane returns int: zero-extend each half (a sign-extended low
+    // half would turn the base into an invalid address).
+    const uint64_t bs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(bs) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Compiler-level memory barrier (no instruction): keeps LDS reads below an
 // explicit wait_vmcnt for copies the compiler does not track.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// XOR swizzle of the 16-byte chunks of one row of an LDS K/V tile (DG chunks
+// per row): physical chunk = logical chunk ^ swz(row).  Chosen so that both
+// operand reads are bank-conflict free: 8 consecutive rows at one chunk
+// (ds_read_b128 of the K operand) and 4 consecutive rows (4-aligned) x 2
+// adjacent chunks (ds_read_b64_tr_b16 of the V operand) each land on
+// distinct chunks.
+template <int DG>
+__device__ __forceinline__ int swz(int row)
+{
+    int g = ((row & 3) << 1) | ((row >> 2) & 1);
+    if (DG > 8)
+        g |= row & 8;
+    return g;
+}
 
 // Workgroup barrier that orders LDS accesses only: global memory is not
 // fenced, so outstanding global->LDS copies and global stores are not drained

@@ -21,7 +21,7 @@
 //    lane) comes from the gfx950 transpose read ds_read_b64_tr_b16.
 //  * K and V tiles are copied global -> LDS with global_load_lds_dwordx4 (no
 //    registers), into a row-major layout whose 16-byte chunks are XOR-swizzled
-//    by row so that MFMA operand reads are bank-conflict free.  K runs in a
+//    by row (swz) so that MFMA operand reads are bank-conflict free.  K runs in a
 //    ring of 3 buffers, two blocks ahead of the scores; V is requested only
 //    once the block's vote says it executes.
 //  * Skip vote: a lane meets the test when its row does; the tile skips when
@@ -114,25 +114,42 @@ void prefill_kernel(const PrefillArgs a)
     // Tile copy: wave w fills rows [w*KI*RPI, (w+1)*KI*RPI); lane -> (row, chunk)
     // with the chunk XOR-swizzled by the row.  Rows past L re-read row L-1
     // (finite data; those keys are masked to -inf).
-    auto copy_tile = [&](const uint16_t *base, int64_t st, int j, char *dst) {
+    // Per-lane byte offsets of a whole tile, computed once; a block that lies
+    // entirely below L then costs one scalar add per tile copy.
+    uint32_t koff[KI], voff[KI];
 #pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            const int ins = w * KI + i;
-            const int row = ins * RPI + lane / DG;
-            const int c = (lane % DG) ^ (row & (DG - 1));
-            int key = j * BC + row;
-            key = key < L ? key : L - 1;
-            copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024);
+    for (int i = 0; i < KI; ++i) {
+        const int row = (w * KI + i) * RPI + lane / DG;
+        const int c = (lane % DG) ^ swz<DG>(row);
+        koff[i] = (uint32_t)((row * a.k_st + c * 8) * 2);
+        voff[i] = (uint32_t)((row * a.v_st + c * 8) * 2);
+    }
+    auto copy_tile = [&](const uint16_t *base, int64_t st, const uint32_t *off, int j, char *dst) {
+        if ((j + 1) * BC <= L) {
+            const uint16_t *sb = base + (int64_t)j * BC * st;
+#pragma unroll
+            for (int i = 0; i < KI; ++i)
+                copy16_to_lds_s(sb, off[i], dst + (w * KI + i) * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                const int ins = w * KI + i;
+                const int row = ins * RPI + lane / DG;
+                const int c = (lane % DG) ^ swz<DG>(row);
+                int key = j * BC + row;
+                key = key < L ? key : L - 1;
+                copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024);
+            }
         }
     };
     auto kbuf = [&](int j) { return smem + (j % NKBUF) * TB; };
 
     // Prologue: K_0..K_2 into the ring.
-    copy_tile(kp, a.k_st, 0, kbuf(0));
+    copy_tile(kp, a.k_st, koff, 0, kbuf(0));
     if (1 < nvis)
-        copy_tile(kp, a.k_st, 1, kbuf(1));
+        copy_tile(kp, a.k_st, koff, 1, kbuf(1));
     if (2 < nvis)
-        copy_tile(kp, a.k_st, 2, kbuf(2));
+        copy_tile(kp, a.k_st, koff, 2, kbuf(2));
     if (2 < nvis)
         wait_vmcnt<2 * KI>();
     else if (1 < nvis)
@@ -162,7 +179,7 @@ void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const int row = 32 * kt + n;
-                const int c = (2 * kk + hh) ^ (row & (DG - 1));
+                const int c = (2 * kk + hh) ^ swz<DG>(row);
                 const bf16x8 ka = as_bf16x8(*(const u32x4 *)(kb + row * RB + c * 16));
                 s[kt] = mfma32(ka, qf[kk], s[kt]);
             }
@@ -232,10 +249,10 @@ void prefill_kernel(const PrefillArgs a)
         }
 
         if (!skip)
-            copy_tile(vp, a.v_st, j, Vb); // V_j only for an executed block
+            copy_tile(vp, a.v_st, voff, j, Vb); // V_j only for an executed block
         const bool k3 = j + 3 < nvis;
         if (k3)
-            copy_tile(kp, a.k_st, j + 3, kbuf(j)); // K ring refill
+            copy_tile(kp, a.k_st, koff, j + 3, kbuf(j)); // K ring refill
 
         if (!skip) {
             // Online-softmax update of this lane's row.
@@ -279,8 +296,8 @@ void prefill_kernel(const PrefillArgs a)
                 for (int dt = 0; dt < D / 32; ++dt) {
                     const int c = 4 * dt + 2 * vmb + (vq >> 1);
                     const int ra = 16 * u + 4 * vh + vj, rb = ra + 8;
-                    const i16x4 x0 = lds_read_tr16(Vb + ra * RB + ((c ^ (ra & (DG - 1))) * 16) + (vq & 1) * 8);
-                    const i16x4 x1 = lds_read_tr16(Vb + rb * RB + ((c ^ (rb & (DG - 1))) * 16) + (vq & 1) * 8);
+                    const i16x4 x0 = lds_read_tr16(Vb + ra * RB + ((c ^ swz<DG>(ra)) * 16) + (vq & 1) * 8);
+                    const i16x4 x1 = lds_read_tr16(Vb + rb * RB + ((c ^ swz<DG>(rb)) * 16) + (vq & 1) * 8);
                     const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
                     const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
                     o[dt] = mfma32(as_bf16x8(va), pf[u], o[dt]);
