@@ -21,9 +21,13 @@
 //    lane) comes from the gfx950 transpose read ds_read_b64_tr_b16.
 //  * K and V tiles are copied global -> LDS with global_load_lds_dwordx4 (no
 //    registers), into a row-major layout whose 16-byte chunks are XOR-swizzled
-//    by row (swz) so that MFMA operand reads are bank-conflict free.  K runs in a
-//    ring of 3 buffers, two blocks ahead of the scores; V is requested only
-//    once the block's vote says it executes.
+//    by row (swz) so that MFMA operand reads are bank-conflict free.  K and V
+//    each run in a ring of 2 buffers; V is requested only once the block's
+//    vote says it executes, one iteration before its P.V product.
+//  * Software pipeline with one barrier per key block: iteration j finishes
+//    the P.V product of block j-1, forms the scores of block j+1 and the
+//    softmax of block j, so a skipped block costs its Q.K product, its row
+//    max and its vote, and a V copy has a whole iteration to land.
 //  * Skip vote: a lane meets the test when its row does; the tile skips when
 //    every valid row of every wave does (one LDS word per wave, exchanged at
 //    the barrier that also publishes the next K tile), so the branch is
@@ -40,7 +44,6 @@ namespace blasst {
 namespace {
 
 constexpr int BC = 64;       // key block
-constexpr int NKBUF = 3;     // K ring depth
 
 template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16>
 __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, 2)))
@@ -54,10 +57,10 @@ void prefill_kernel(const PrefillArgs a)
     constexpr int RPI = 64 / DG;         // rows per copy instruction
     static_assert(KI >= 1 && KI * NW * 1024 == TB, "tile shape");
 
-    __shared__ __attribute__((aligned(1024))) char smem[(NKBUF + 1) * TB];
+    // K ring (2 tiles) and V ring (2 tiles).
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
     __shared__ int vote[2][NW];
     __shared__ float gapw[2][NW];
-    char *const Vb = smem + NKBUF * TB;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,10 +115,10 @@ void prefill_kernel(const PrefillArgs a)
     const int nvis = CAUSAL ? (last_row / BC + 1 < a.nkb ? last_row / BC + 1 : a.nkb) : a.nkb;
 
     // Tile copy: wave w fills rows [w*KI*RPI, (w+1)*KI*RPI); lane -> (row, chunk)
-    // with the chunk XOR-swizzled by the row.  Rows past L re-read row L-1
+    // with the chunk XOR-swizzled by the row (swz).  Per-lane byte offsets of
+    // a whole tile are computed once: a block that lies entirely below L
+    // costs one scalar add per tile copy.  Rows past L re-read row L-1
     // (finite data; those keys are masked to -inf).
-    // Per-lane byte offsets of a whole tile, computed once; a block that lies
-    // entirely below L then costs one scalar add per tile copy.
     uint32_t koff[KI], voff[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -142,49 +145,41 @@ void prefill_kernel(const PrefillArgs a)
             }
         }
     };
-    auto kbuf = [&](int j) { return smem + (j % NKBUF) * TB; };
+    auto kbuf = [&](int j) { return smem + (j & 1) * TB; };
+    auto vbuf = [&](int j) { return smem + (2 + (j & 1)) * TB; };
 
-    // Prologue: K_0..K_2 into the ring.
-    copy_tile(kp, a.k_st, koff, 0, kbuf(0));
-    if (1 < nvis)
-        copy_tile(kp, a.k_st, koff, 1, kbuf(1));
-    if (2 < nvis)
-        copy_tile(kp, a.k_st, koff, 2, kbuf(2));
-    if (2 < nvis)
-        wait_vmcnt<2 * KI>();
-    else if (1 < nvis)
-        wait_vmcnt<KI>();
-    else
-        wait_vmcnt<0>();
-    lds_barrier();
-
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = f32x16{};
-    float m2 = neg_inf();   // running max of this lane's row (base 2)
-    float lsum = 0.f;       // running sum over this lane's half of each block
-    int n_skipped = 0;
-
-    // V operand addressing for the transpose read (fixed per lane).
-    const int vg = lane >> 4, vs = lane & 15;
-    const int vmb = vg & 1, vh = vg >> 1, vj = vs >> 2, vq = vs & 3;
-
-    for (int j = 0; j < nvis; ++j) {
+    // S^T = K_j Q^T (two 32-key tiles) with the causal / ragged mask, and the
+    // block-local row max (base 2).
+    auto scores = [&](int j, f32x16 (&s)[2], float &mt2) {
         const char *kb = kbuf(j);
-        // S^T = K_j Q^T: two 32-key tiles.
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        // K operands are read three k-steps ahead of their MFMAs so that the
+        // LDS latency hides behind the matrix work.
+        constexpr int NK = D / 16;
+        auto kread = [&](int kk, int kt) {
+            const int row = 32 * kt + n;
+            const int c = (2 * kk + hh) ^ swz<DG>(row);
+            return *(const u32x4 *)(kb + row * RB + c * 16);
+        };
+        u32x4 ka[3][2];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int row = 32 * kt + n;
-                const int c = (2 * kk + hh) ^ swz<DG>(row);
-                const bf16x8 ka = as_bf16x8(*(const u32x4 *)(kb + row * RB + c * 16));
-                s[kt] = mfma32(ka, qf[kk], s[kt]);
+            for (int kt = 0; kt < 2; ++kt)
+                ka[kk][kt] = kread(kk, kt);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            if (kk + 2 < NK) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    ka[(kk + 2) % 3][kt] = kread(kk + 2, kt);
             }
+            __builtin_amdgcn_sched_barrier(0); // keep the reads ahead of the MFMAs
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                s[kt] = mfma32(as_bf16x8(ka[kk % 3][kt]), qf[kk], s[kt]);
         }
-        // Mask the causal diagonal and the ragged tail (-inf entries).
         const int k0 = j * BC;
         if ((CAUSAL && k0 + BC - 1 > r0) || k0 + BC > L) {
 #pragma unroll
@@ -203,31 +198,128 @@ void prefill_kernel(const PrefillArgs a)
             for (int r = 0; r < 16; ++r)
                 mt = fmaxf(mt, s[kt][r]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mt2 = mt * a.scale_log2; // block-local row max, base 2
+        mt2 = mt * a.scale_log2;
+    };
 
-        const int par = j & 1;
+    float m2 = neg_inf(); // running max of this lane's row (base 2)
+    float lsum = 0.f;     // running sum over this lane's half of each block
+    int n_skipped = 0;
+
+    // Wave vote on block j against the running max; d = m~ - m with the
+    // infinity rules (-inf if the row sees no key in the block, +inf while the
+    // row has no running max).
+    auto vote_block = [&](int j, float mt2) {
         if (SKIP || want_maps) {
-            // d = m~ - m with the infinity rules: -inf if the row sees no key in
-            // the block, +inf if the row has no running max yet.
             const float dgap = (!row_valid || mt2 == neg_inf()) ? neg_inf() : mt2 - m2;
             if (SKIP) {
                 const int wall = __all(!(dgap >= a.lnlam2)); // -inf rows always meet it
                 if (lane == 0)
-                    vote[par][w] = wall;
+                    vote[j & 1][w] = wall;
             }
             if (want_maps) {
                 const float wg = wave_max(dgap);
                 if (lane == 0)
-                    gapw[par][w] = wg;
+                    gapw[j & 1][w] = wg;
             }
         }
-        // Own part of K_{j+1} landed (only K_{j+2} may still be in flight).
-        if (j + 2 < nvis)
-            wait_vmcnt<KI>();
-        else
-            wait_vmcnt<0>();
-        lds_barrier(); // (A) votes, K_{j+1} visible; K_j fully consumed
+    };
 
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = f32x16{};
+
+    // V operand addressing for the transpose read (fixed per lane).
+    const int vg = lane >> 4, vs = lane & 15;
+    const int vmb = vg & 1, vh = vg >> 1, vj = vs >> 2, vq = vs & 3;
+
+    // O^T += V_j^T P_j^T, k-steps of 16 keys.
+    // The V^T operands are read three MFMAs ahead (flattened over (u, dt)) so
+    // that the LDS latency hides behind the matrix work.
+    auto pv = [&](int j, const bf16x8 (&pf)[4]) {
+        const char *Vb = vbuf(j);
+        constexpr int NDT = D / 32, NM = 4 * NDT;
+        auto vread = [&](int m) {
+            const int u = m / NDT, dt = m % NDT;
+            const int c = 4 * dt + 2 * vmb + (vq >> 1);
+            const int ra = 16 * u + 4 * vh + vj, rb = ra + 8;
+            const i16x4 x0 = lds_read_tr16(Vb + ra * RB + ((c ^ swz<DG>(ra)) * 16) + (vq & 1) * 8);
+            const i16x4 x1 = lds_read_tr16(Vb + rb * RB + ((c ^ swz<DG>(rb)) * 16) + (vq & 1) * 8);
+            const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+            return u32x4{y0[0], y0[1], y1[0], y1[1]};
+        };
+        u32x4 va[4];
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+            va[m] = vread(m);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m + 3 < NM)
+                va[(m + 3) % 4] = vread(m + 3);
+            __builtin_amdgcn_sched_barrier(0); // keep the reads ahead of the MFMAs
+            o[m % NDT] = mfma32(as_bf16x8(va[m % 4]), pf[m / NDT], o[m % NDT]);
+        }
+    };
+
+    // Online-softmax update of an executed block: new running max, P (bf16,
+    // the B operand of the next P.V), row sum, and the rescale of the
+    // accumulator, skipped when no row of the wave raised its max.
+    auto softmax = [&](const f32x16 (&s)[2], float mt2, bf16x8 (&pf)[4]) {
+        const float mnew = fmaxf(m2, mt2);
+        const float msafe = mnew == neg_inf() ? 0.f : mnew;
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x8 lo, hi;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float p0 = exp2_hw(__builtin_fmaf(s[kt][r], a.scale_log2, -msafe));
+                const float p1 = exp2_hw(__builtin_fmaf(s[kt][r + 8], a.scale_log2, -msafe));
+                lo[r] = p0;
+                hi[r] = p1;
+                rs += p0 + p1;
+            }
+            pf[2 * kt] = cvt_bf16x8(lo);
+            pf[2 * kt + 1] = cvt_bf16x8(hi);
+        }
+        const float alpha = mnew > m2 ? exp2_hw(m2 - msafe) : 1.f; // 0 on the first block
+        lsum = alpha * lsum + rs;
+        if (__any(mnew > m2)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                o[dt] *= alpha;
+        }
+        m2 = mnew;
+    };
+
+    // Software pipeline, one barrier per block.  Entering iteration j:
+    //   S_j and its row max are in registers and its vote is in LDS;
+    //   K_{j+1} and (if block j-1 executed) V_{j-1} are in flight;
+    //   P_{j-1} is in registers if block j-1 executed.
+    // Iteration j: barrier; decide j; request V_j (if executed) and K_{j+2};
+    // then O += V_{j-1} P_{j-1} (MFMA), the softmax of block j (VALU) and the
+    // scores of block j+1 (MFMA); finally vote on block j+1.  The other
+    // workgroup on the compute unit fills the matrix / vector gaps.  By the barrier of iteration j+1 the V_j and K_{j+2} copies
+    // have had a whole iteration to land.
+    copy_tile(kp, a.k_st, koff, 0, kbuf(0));
+    if (1 < nvis) {
+        copy_tile(kp, a.k_st, koff, 1, kbuf(1));
+        wait_vmcnt<KI>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    lds_barrier();
+    f32x16 sc[2];
+    float mt2c;
+    scores(0, sc, mt2c);
+    vote_block(0, mt2c);
+
+    bf16x8 pprev[4];
+    bool eprev = false;
+    for (int j = 0; j < nvis; ++j) {
+        wait_vmcnt<0>();
+        lds_barrier(); // votes_j, K_{j+1}, V_{j-1} visible; iteration j-1 done everywhere
+        const int par = j & 1;
         bool skip = false;
         if (SKIP) {
             int all = 1;
@@ -247,65 +339,28 @@ void prefill_kernel(const PrefillArgs a)
             if (a.gap_map)
                 a.gap_map[idx] = g * 0.69314718055994531f; // back to natural log
         }
+        n_skipped += skip ? 1 : 0;
+        const bool ecur = !skip;
+        if (ecur)
+            copy_tile(vp, a.v_st, voff, j, vbuf(j)); // V_j only for an executed block
+        if (j + 2 < nvis)
+            copy_tile(kp, a.k_st, koff, j + 2, kbuf(j)); // K ring refill
+        const bool has_next = j + 1 < nvis;
 
-        if (!skip)
-            copy_tile(vp, a.v_st, voff, j, Vb); // V_j only for an executed block
-        const bool k3 = j + 3 < nvis;
-        if (k3)
-            copy_tile(kp, a.k_st, koff, j + 3, kbuf(j)); // K ring refill
-
-        if (!skip) {
-            // Online-softmax update of this lane's row.
-            const float mnew = fmaxf(m2, mt2);
-            if (__any(mnew > m2)) {
-                const float alpha = mnew > m2 ? exp2_hw(m2 - mnew) : 1.f; // 0 on the first block
-                lsum *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    o[dt] *= alpha;
-            }
-            m2 = mnew;
-            const float msafe = m2 == neg_inf() ? 0.f : m2;
-            float rs = 0.f;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                f32x8 lo, hi;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float p0 = exp2_hw(__builtin_fmaf(s[kt][r], a.scale_log2, -msafe));
-                    const float p1 = exp2_hw(__builtin_fmaf(s[kt][r + 8], a.scale_log2, -msafe));
-                    lo[r] = p0;
-                    hi[r] = p1;
-                    rs += p0 + p1;
-                }
-                pf[2 * kt] = cvt_bf16x8(lo);
-                pf[2 * kt + 1] = cvt_bf16x8(hi);
-            }
-            lsum += rs;
-            // Own part of V_j landed (K_{j+3} may still be in flight).
-            if (k3)
-                wait_vmcnt<KI>();
-            else
-                wait_vmcnt<0>();
-            lds_barrier(); // (B) V_j visible
-            // O^T += V^T P^T, k-steps of 16 keys.
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const int c = 4 * dt + 2 * vmb + (vq >> 1);
-                    const int ra = 16 * u + 4 * vh + vj, rb = ra + 8;
-                    const i16x4 x0 = lds_read_tr16(Vb + ra * RB + ((c ^ swz<DG>(ra)) * 16) + (vq & 1) * 8);
-                    const i16x4 x1 = lds_read_tr16(Vb + rb * RB + ((c ^ swz<DG>(rb)) * 16) + (vq & 1) * 8);
-                    const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
-                    const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
-                    o[dt] = mfma32(as_bf16x8(va), pf[u], o[dt]);
-                }
-            }
-        } else {
-            ++n_skipped;
+        if (eprev)
+            pv(j - 1, pprev); // P_{j-1} is dead afterwards
+        if (ecur)
+            softmax(sc, mt2c, pprev); // P_j reuses its registers
+        if (has_next) {
+            scores(j + 1, sc, mt2c); // S_j is dead: S_{j+1} takes its registers
+            vote_block(j + 1, mt2c);
         }
+        eprev = ecur;
+    }
+    if (eprev) {
+        wait_vmcnt<0>();
+        lds_barrier(); // V of the last executed block visible
+        pv(nvis - 1, pprev);
     }
 
     // Finalize: O = acc / l, l summed over the two lane halves.
