@@ -200,9 +200,13 @@ int choose_splits(const blasst_decode_params *p)
     if (p->num_splits > 0)
         return p->num_splits;
     const int64_t units = p->B * p->Hkv;
-    // Aim for >= 1024 workgroups (4 per compute unit), keep >= 16 blocks a split.
+    // GQA: aim for >= 1024 workgroups (4 per compute unit).  Latent decode
+    // holds one workgroup per compute unit (its K ring fills the LDS), so one
+    // wave of 256 workgroups; more splits only add partial-result traffic.
+    // Either way keep >= 16 blocks a split.
+    const int64_t want = decode_kind(p) == KIND_MLA ? 256 : 1024;
     int s = 1;
-    while (units * s < 1024 && nkb / (2 * s) >= 16)
+    while (units * s < want && nkb / (2 * s) >= 16)
         s *= 2;
     return s;
 }

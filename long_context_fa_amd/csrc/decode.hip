@@ -352,6 +352,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a,
     }
 }
 
+} // namespace
+
+hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_t stream)
+{
+    const dim3 grid(a.Hq, a.B), block(dv < 256 ? dv : 256);
+    if (out_bf16)
+        hipLaunchKernelGGL((decode_combine_kernel<true>), grid, block, 0, stream, a, dv);
+    else
+        hipLaunchKernelGGL((decode_combine_kernel<false>), grid, block, 0, stream, a, dv);
+    return hipGetLastError();
+}
+
+namespace {
+
 template <int D, bool SKIP, bool OUT_BF16>
 hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream)
 {
@@ -360,9 +374,7 @@ hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1)
         return e;
-    hipLaunchKernelGGL((decode_combine_kernel<OUT_BF16>), dim3(a.Hq, a.B), dim3(D < 256 ? D : 256), 0, stream, a,
-                       D);
-    return hipGetLastError();
+    return launch_combine(a, D, OUT_BF16, stream);
 }
 
 } // namespace

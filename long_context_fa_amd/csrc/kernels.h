@@ -44,4 +44,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16,
                          hipStream_t stream);
 
+// Log-sum-exp merge of the split partials into O (num_splits > 1).
+hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_t stream);
+
 } // namespace blasst

@@ -1,14 +1,453 @@
-// mla.hip -- latent (MLA, absorbed form) decode: 128 query heads sharing one
-// latent KV head of width 576, values = first 512 latent columns.
+// mla.hip -- latent (MLA, absorbed form) decode with BLASST block skipping,
+// gfx950: 128 query heads share one latent KV head of width 576 (512 latent
+// + 64 rotary); the value of a token is the first 512 columns of its latent
+// row, so V costs no bytes of its own.
+//
+// Method: "BLASST: Dynamic BLocked Attention Sparsity via Softmax
+// Thresholding" (gist.science/pt/paper/2512.12087, section 2; section 3 lists
+// MHA/GQA/MQA/MLA support).  A query tile is the group of heads sharing the KV
+// head -- here all 128 -- and a key block is skipped when every head meets
+// m~ - m < ln(lambda).  With V aliasing the latent K, a skipped block saves the
+// exponentials and the P.V product (about half the matrix work), not bytes.
+//
+// One workgroup (4 waves x 32 heads, one wave per SIMD so that each wave can
+// hold the 576-wide Q^T operand in VGPRs and its 512x32 O^T accumulator in
+// AGPRs) walks the key blocks of one (sequence, split):
+//  * the 64 x 576 bf16 K tile (72 KB) is copied global -> LDS with
+//    global_load_lds_dwordx4 into a double buffer; 16-byte chunks are
+//    XOR-swizzled by row inside aligned groups of 8 chunks;
+//  * S^T = K Q^T with the 32x32x16 bf16 MFMA (per-lane head statistics, as in
+//    prefill); the 4 wave votes are exchanged through LDS;
+//  * executed blocks: online softmax (rescale skipped when no head raised
+//    its max) and O^T += V^T P^T with the V^T operand transpose-read
+//    (ds_read_b64_tr_b16) from the same K tile;
+//  * split partials (O, max, sum) go to the workspace for the log-sum-exp
+//    combine kernel, or O is written directly for a single split.
 #include "device.h"
 #include "kernels.h"
 
 namespace blasst {
 
+namespace {
+
+constexpr int BC = 64;
+constexpr int DQK = 576, DV = 512;
+constexpr int RB = DQK * 2;          // 1152 bytes per K row
+constexpr int TB = BC * RB;          // 73728 bytes per tile
+constexpr int NWM = 4;               // waves (32 heads each)
+constexpr int CPW = TB / 1024 / NWM; // 1 KB copies per tile per wave (18)
+constexpr int NKK = DQK / 16;        // QK k-steps (36)
+constexpr int NDT = DV / 32;         // O^T d tiles (16)
+
+// Register placement.  Each wave owns 32 heads.  The O^T accumulator
+// (512 x 32 fp32) is pinned in the 256 AGPRs, d-tile dt in a[16dt, 16dt+16);
+// Q^T, the scores and the MFMA operands live in the 256 VGPRs.  Every access
+// to the accumulator (zeroing, the P.V MFMAs, rescaling, read-out) is inline
+// asm on the physical registers, and the compiler, which sees no AGPR values,
+// keeps its own values in VGPRs (a CPU test checks the generated code for
+// AGPR use outside these blocks).  The score MFMAs are asm too, with VGPR
+// accumulators.  Hazard padding is explicit because the compiler does not
+// see through asm: three wait states before each MFMA cover a VALU or
+// accvgpr write of its sources, and 24 wait states follow the last MFMA of a
+// chain before any other instruction reads its result.
+#define MLA_ALL_AGPRS \
+    "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", \
+    "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", \
+    "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", \
+    "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63", \
+    "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79", \
+    "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95", \
+    "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111", \
+    "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", \
+    "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143", \
+    "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159", \
+    "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", \
+    "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191", \
+    "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207", \
+    "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223", \
+    "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239", \
+    "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255"
+
+__device__ __forceinline__ void o_zero()
+{
+    asm volatile(".set .Lmo, 0\n\t.rept 256\n\tv_accvgpr_write_b32 a[.Lmo], 0\n\t"
+                 ".set .Lmo, .Lmo+1\n\t.endr" ::: MLA_ALL_AGPRS);
+}
+// O^T[dt] += V^T P^T for one d-tile (dt a compile-time constant after unrolling).
+__device__ __forceinline__ void o_mfma(int dt, const u32x4 &a, const bf16x8 &b)
+{
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 a[%2:%3], %0, %1, a[%2:%3]"
+                 ::"v"(a), "v"(b), "i"(16 * dt), "i"(16 * dt + 15));
+}
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+// O^T *= alpha (per lane: alpha of the lane's head), four registers at a time.
+__device__ __forceinline__ void o_rescale(float alpha)
+{
+    float t0, t1, t2, t3;
+    asm volatile(".set .Lmo, 0\n\t.rept 64\n\t"
+                 "v_accvgpr_read_b32 %0, a[.Lmo]\n\tv_accvgpr_read_b32 %1, a[.Lmo+1]\n\t"
+                 "v_accvgpr_read_b32 %2, a[.Lmo+2]\n\tv_accvgpr_read_b32 %3, a[.Lmo+3]\n\t"
+                 "v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\t"
+                 "v_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\t"
+                 "v_accvgpr_write_b32 a[.Lmo], %0\n\tv_accvgpr_write_b32 a[.Lmo+1], %1\n\t"
+                 "v_accvgpr_write_b32 a[.Lmo+2], %2\n\tv_accvgpr_write_b32 a[.Lmo+3], %3\n\t"
+                 ".set .Lmo, .Lmo+4\n\t.endr"
+                 : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+                 : "v"(alpha)
+                 : MLA_ALL_AGPRS);
+}
+// Reads the 16 accumulator registers of d-tile dt.
+__device__ __forceinline__ f32x16 o_read(int dt)
+{
+    float e[16];
+    asm volatile("v_accvgpr_read_b32 %0, a[%16]\n\tv_accvgpr_read_b32 %1, a[%16+1]\n\t"
+                 "v_accvgpr_read_b32 %2, a[%16+2]\n\tv_accvgpr_read_b32 %3, a[%16+3]\n\t"
+                 "v_accvgpr_read_b32 %4, a[%16+4]\n\tv_accvgpr_read_b32 %5, a[%16+5]\n\t"
+                 "v_accvgpr_read_b32 %6, a[%16+6]\n\tv_accvgpr_read_b32 %7, a[%16+7]\n\t"
+                 "v_accvgpr_read_b32 %8, a[%16+8]\n\tv_accvgpr_read_b32 %9, a[%16+9]\n\t"
+                 "v_accvgpr_read_b32 %10, a[%16+10]\n\tv_accvgpr_read_b32 %11, a[%16+11]\n\t"
+                 "v_accvgpr_read_b32 %12, a[%16+12]\n\tv_accvgpr_read_b32 %13, a[%16+13]\n\t"
+                 "v_accvgpr_read_b32 %14, a[%16+14]\n\tv_accvgpr_read_b32 %15, a[%16+15]"
+                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]),
+                   "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]),
+                   "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15])
+                 : "i"(16 * dt));
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        r[i] = e[i];
+    return r;
+}
+// S^T accumulation (VGPR accumulators).
+__device__ __forceinline__ void mfma_v_first(f32x16 &c, const u32x4 &a, const bf16x8 &b)
+{
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16 &c, const u32x4 &a, const bf16x8 &b)
+{
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_drain(f32x16 &c0, f32x16 &c1)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+}
+
+// 3-bit swizzle: keeps chunks inside aligned groups of 8 (a row has 72).
+__device__ __forceinline__ int swz8(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+template <bool SKIP, bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_mla_kernel(const DecodeArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[2 * TB];
+    __shared__ int vote[2][NWM];
+    __shared__ float gapw[2][NWM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hh = lane >> 5;
+    const int s = blockIdx.x, b = blockIdx.z;
+    const int S = a.num_splits;
+    const int head = 32 * w + n;
+    const bool want_maps = a.skip_map != nullptr || a.gap_map != nullptr;
+
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
+    const int nkb_b = (len + BC - 1) / BC;
+    const int per = (nkb_b + S - 1) / S;
+    const int jb = s * per;
+    const int je = (jb + per < nkb_b) ? jb + per : nkb_b;
+
+    const uint16_t *kp = a.k + b * a.k_sb;
+
+    // Q^T as the B operand: lane (n, hh) holds q[head][16kk + 8hh .. +7].
+    bf16x8 qf[NKK];
+    {
+        const uint16_t *qp = a.q + b * a.q_sb + (int64_t)head * a.q_sh;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            qf[kk] = as_bf16x8(*(const u32x4 *)(qp + 16 * kk + 8 * hh));
+    }
+
+    // Tile copy: wave w fills rows [16w, 16w+16) of the tile, 18 DMA copies
+    // of 1 KB; copy i, lane l covers physical chunk 64i + l of those rows.
+    // The physical chunk (row, pc) holds logical chunk pc ^ swz8(row).  The
+    // per-lane offsets are recomputed each tile (cheap VALU) rather than held
+    // in 18 registers.  Rows past len re-read row len-1 (masked later).
+    auto tile = [&](int j) { return smem + (j & 1) * TB; };
+    auto copy_tile = [&](int j) {
+        char *dst = tile(j) + w * (16 * RB);
+        int lv = lane;
+        asm volatile("" : "+v"(lv)); // keep the offset arithmetic in the loop
+        int row = 16 * w + lv / 72, pc = lv % 72;
+        if ((j + 1) * BC <= len) {
+            const uint16_t *sb = kp + (int64_t)j * BC * a.k_st;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int c = pc ^ swz8(row);
+                copy16_to_lds_s(sb, (uint32_t)((row * (int)a.k_st + c * 8) * 2), dst + i * 1024);
+                pc += 64;
+                const bool wrap = pc >= 72;
+                pc = wrap ? pc - 72 : pc;
+                row += wrap ? 1 : 0;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int c = pc ^ swz8(row);
+                int key = j * BC + row;
+                key = key < len ? key : len - 1;
+                copy16_to_lds(kp + (int64_t)key * a.k_st + c * 8, dst + i * 1024);
+                pc += 64;
+                const bool wrap = pc >= 72;
+                pc = wrap ? pc - 72 : pc;
+                row += wrap ? 1 : 0;
+            }
+        }
+    };
+
+    // LDS read offsets.  K operand (row n, logical chunk 2kk + hh): chunk
+    // 8(kk/4) + ((2(kk%4) + hh) ^ swz8(n)), so 4 per-lane offsets plus
+    // immediates; row n + 32 has the same swizzle.  V^T operand (rows
+    // 16u + 4vh + vj (+8), chunk 4dt + 2vmb + vq/2): 2 per-lane offsets.
+    const int vg = lane >> 4, vs = lane & 15;
+    const int vmb = vg & 1, vh = vg >> 1, vj = vs >> 2, vq = vs & 3;
+    int koff[4], voffv[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+        koff[q4] = n * RB + ((2 * q4 + hh) ^ swz8(n)) * 16;
+    {
+        const int ra = 4 * vh + vj;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            voffv[x] = ra * RB + ((4 * x + 2 * vmb + (vq >> 1)) ^ swz8(ra)) * 16 + (vq & 1) * 8;
+    }
+
+    o_zero();
+    float m2 = neg_inf(), lsum = 0.f;
+    int n_skipped = 0;
+
+    if (jb < je) {
+        copy_tile(jb);
+        if (jb + 1 < je) {
+            copy_tile(jb + 1);
+            wait_vmcnt<CPW>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+    }
+    for (int j = jb; j < je; ++j) {
+        const char *kb = tile(j);
+        // S^T = K_j Q^T, K operands read two k-steps ahead.
+        f32x16 sc[2];
+        auto kread = [&](int kk, int kt) {
+            return *(const u32x4 *)(kb + koff[kk & 3] + 128 * (kk >> 2) + kt * 32 * RB);
+        };
+        u32x4 ka[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+            ka[0][kt] = kread(0, kt);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            if (kk + 1 < NKK) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    ka[(kk + 1) & 1][kt] = kread(kk + 1, kt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                if (kk == 0)
+                    mfma_v_first(sc[kt], ka[0][kt], qf[0]);
+                else
+                    mfma_v(sc[kt], ka[kk & 1][kt], qf[kk]);
+            }
+        }
+        mfma_v_drain(sc[0], sc[1]);
+        const int k0 = j * BC;
+        if (k0 + BC > len) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (k0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3) >= len)
+                        sc[kt][r] = neg_inf();
+        }
+        float mt = neg_inf();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mt = fmaxf(mt, sc[kt][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mt2 = mt * a.scale_log2;
+        const int par = j & 1;
+        if (SKIP || want_maps) {
+            const float dgap = mt2 == neg_inf() ? neg_inf() : mt2 - m2;
+            if (SKIP) {
+                const int wall = __all(!(dgap >= a.lnlam2));
+                if (lane == 0)
+                    vote[par][w] = wall;
+            }
+            if (want_maps) {
+                const float wgap = wave_max(dgap);
+                if (lane == 0)
+                    gapw[par][w] = wgap;
+            }
+        }
+        // Own part of K_{j+1} landed; votes and K_{j+1} visible after this.
+        wait_vmcnt<0>();
+        lds_barrier();
+        bool skip = false;
+        if (SKIP) {
+            int all = 1;
+#pragma unroll
+            for (int i = 0; i < NWM; ++i)
+                all &= vote[par][i];
+            skip = __builtin_amdgcn_readfirstlane(all) != 0;
+        }
+        if (want_maps && tid == 0) {
+            float g = neg_inf();
+#pragma unroll
+            for (int i = 0; i < NWM; ++i)
+                g = fmaxf(g, gapw[par][i]);
+            const int64_t idx = (int64_t)b * a.nkb + j;
+            if (a.skip_map)
+                a.skip_map[idx] = skip ? 1 : 0;
+            if (a.gap_map)
+                a.gap_map[idx] = g * 0.69314718055994531f;
+        }
+        if (!skip) {
+            const float mnew = fmaxf(m2, mt2);
+            const float msafe = mnew == neg_inf() ? 0.f : mnew;
+            float rs = 0.f;
+            bf16x8 pf[4];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x8 lo, hi;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float p0 = exp2_hw(__builtin_fmaf(sc[kt][r], a.scale_log2, -msafe));
+                    const float p1 = exp2_hw(__builtin_fmaf(sc[kt][r + 8], a.scale_log2, -msafe));
+                    lo[r] = p0;
+                    hi[r] = p1;
+                    rs += p0 + p1;
+                }
+                pf[2 * kt] = cvt_bf16x8(lo);
+                pf[2 * kt + 1] = cvt_bf16x8(hi);
+            }
+            const float alpha = mnew > m2 ? exp2_hw(m2 - msafe) : 1.f;
+            lsum = alpha * lsum + rs;
+            if (__any(mnew > m2))
+                o_rescale(alpha);
+            m2 = mnew;
+            // O^T += V^T P^T, V = first 512 columns of the K tile.
+            auto vread = [&](int m) {
+                const int u = m / NDT, dt = m % NDT;
+                const char *va0 = kb + voffv[dt & 1] + 16 * u * RB + 128 * (dt >> 1);
+                const i16x4 x0 = lds_read_tr16(va0);
+                const i16x4 x1 = lds_read_tr16(va0 + 8 * RB);
+                const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
+                return u32x4{y0[0], y0[1], y1[0], y1[1]};
+            };
+            constexpr int NM = 4 * NDT;
+            u32x4 va[3];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                va[m] = vread(m);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m + 2 < NM)
+                    va[(m + 2) % 3] = vread(m + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                o_mfma(m % NDT, va[m % 3], pf[m / NDT]);
+            }
+            mfma_drain();
+        } else {
+            ++n_skipped;
+        }
+        lds_barrier(); // every wave is done with tile j
+        if (j + 2 < je)
+            copy_tile(j + 2);
+    }
+
+    // Output: O^T lane (n, hh) holds head `head`, d = 32dt + 8g + 4hh + i.
+    const float l = lsum + __shfl_xor(lsum, 32);
+    if (S == 1) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        char *ob = (char *)a.o;
+        const int64_t base = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const f32x16 od = o_read(dt);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                const f32x4 v4 = {od[4 * g] * inv, od[4 * g + 1] * inv, od[4 * g + 2] * inv,
+                                  od[4 * g + 3] * inv};
+                if (OUT_BF16)
+                    *(bf16x4 *)(ob + 2 * (base + d)) = __builtin_convertvector(v4, bf16x4);
+                else
+                    *(f32x4 *)(ob + 4 * (base + d)) = v4;
+            }
+        }
+    } else {
+        const int64_t pu = ((int64_t)b * S + s) * 128 + head; // Hkv = 1, G = 128
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const f32x16 od = o_read(dt);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * dt + 8 * g + 4 * hh;
+                *(f32x4 *)(a.part_o + pu * DV + d) = f32x4{od[4 * g], od[4 * g + 1], od[4 * g + 2], od[4 * g + 3]};
+            }
+        }
+        if (hh == 0) {
+            a.part_ml[2 * pu] = m2;
+            a.part_ml[2 * pu + 1] = l;
+        }
+    }
+    if (tid == 0) {
+        if (want_maps && s == S - 1)
+            for (int j = nkb_b; j < a.nkb; ++j) {
+                const int64_t idx = (int64_t)b * a.nkb + j;
+                if (a.skip_map)
+                    a.skip_map[idx] = 255;
+                if (a.gap_map)
+                    a.gap_map[idx] = neg_inf();
+            }
+        if (a.counters && je > jb) {
+            atomicAdd(a.counters, (unsigned long long)(je - jb));
+            atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
+        }
+    }
+}
+
+} // namespace
+
+hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_t stream);
+
 hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream)
 {
-    (void)a; (void)skip; (void)out_bf16; (void)stream;
-    return hipErrorInvalidValue;
+    if (a.G != 128 || a.Hkv != 1)
+        return hipErrorInvalidValue;
+    const dim3 grid(a.num_splits, 1, a.B);
+    if (skip) {
+        if (out_bf16)
+            hipLaunchKernelGGL((decode_mla_kernel<true, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_mla_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (out_bf16)
+            hipLaunchKernelGGL((decode_mla_kernel<false, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_mla_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.num_splits == 1)
+        return e;
+    return launch_combine(a, DV, out_bf16, stream);
 }
 
 } // namespace blasst

@@ -104,3 +104,51 @@ def test_bf16_output_and_determinism():
     assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(g1, g2)
     o3, _, _, _ = gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=2, out_dtype=torch.bfloat16)
     assert torch.equal(o3.float(), o1.to(torch.bfloat16).float())
+
+
+# ---------------------------------------------------------------- latent (MLA)
+# 128 query heads share one latent KV head of width 576; V = first 512 columns.
+
+def _mla(B, Lmax, *, seed, n_random=16, lens=None):
+    q, kc, _, sl = inputs.decode_inputs(B, 128, 1, Lmax, 576, 512, n_random=n_random, mla=True,
+                                        device=DEV, seed=seed, seq_lens=lens)
+    return q, kc, sl
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_parity_mla_ragged(splits):
+    q, kc, lens = _mla(3, 2000, seed=41 + splits, lens=[2000, 1, 777])
+    _, _, gap0, _ = gpu_decode(q, kc, kc, lens, lam=0.0, num_splits=splits, dv=512)
+    lam, _ = lambda_for(gap0, 0.6)
+    _run(q, kc, kc, lens, lam=lam, splits=splits, dv=512, mla=True, what="mla ragged")
+
+
+def test_dense_mla_matches_oracle():
+    q, kc, lens = _mla(2, 4096, seed=43)
+    cnt, _ = _run(q, kc, kc, lens, lam=0.0, splits=3, dv=512, mla=True, what="mla dense")
+    assert cnt[1] == 0
+
+
+def test_mla_bf16_output_and_determinism():
+    q, kc, lens = _mla(2, 3000, seed=44, lens=[3000, 1234])
+    o1, s1, g1, _ = gpu_decode(q, kc, kc, lens, lam=2e-3, num_splits=2, dv=512)
+    o2, s2, g2, _ = gpu_decode(q, kc, kc, lens, lam=2e-3, num_splits=2, dv=512)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(g1, g2)
+    o3, _, _, _ = gpu_decode(q, kc, kc, lens, lam=2e-3, num_splits=2, dv=512, out_dtype=torch.bfloat16)
+    assert torch.equal(o3.float(), o1.to(torch.bfloat16).float())
+    # one split writes O directly (no combine pass); same decisions as the oracle
+    o4, _, _, _ = gpu_decode(q, kc, kc, lens, lam=2e-3, num_splits=1, dv=512, out_dtype=torch.bfloat16)
+    assert o4.dtype == torch.bfloat16 and torch.isfinite(o4.float()).all()
+
+
+def test_parity_mla_decode_full_size_sampled():
+    """The 16-sequence, 64K-token latent decode step at ~70% sparsity, in the
+    split configuration the planner picks; the oracle checks two whole
+    sequences (all 128 heads)."""
+    q, kc, lens = _mla(16, 65536, seed=2005)
+    S, _ = bl.blasst_decode_plan(q, kc, kc, lens, lam=0.01, dv=512)
+    _, _, gap0, _ = gpu_decode(q, kc, kc, lens, lam=0.0, num_splits=S, dv=512)
+    lam, reached = lambda_for(gap0, 0.7)
+    cnt, _ = _run(q, kc, kc, lens, lam=lam, splits=S, dv=512, mla=True, what="mla 16x128x65536x576",
+                  unit_mask=[(3, 0), (15, 0)])
+    assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
