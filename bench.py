@@ -12,9 +12,15 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
   * the GQA decode workload (148 sequences, Hq=32, Hkv=8, 32768 cached tokens,
     d=128, bf16 cache, block 64) at the 70% and 50% lambdas and lambda = 0:
     microseconds per decode step and HBM GB/s on the bytes actually loaded;
+  * the latent (MLA) decode workload (16 sequences, 128 query heads sharing one
+    576-wide latent KV head, V = its first 512 columns, 65536 cached tokens)
+    at the 70% lambda and lambda = 0: microseconds per step, GB/s on the
+    loaded bytes and MFMA utilisation (the workload sits near the ridge);
+  * the long causal prefill (B=2, Hq=32, Hkv=8, L=32768, d=128) over the
+    target sparsities 30/50/70/80% and dense;
   * the fp64 CPU oracle on a bounded sample of the prefill workload.
 Inputs are seeded synthetic segment-center tensors generated on the device.
-Prints ONE JSON line.
+Prints ONE JSON line.  ``--only NAME`` runs one measurement (for profilers).
 """
 import argparse
 import json
@@ -68,6 +74,18 @@ def decode_workload(seed=1002):
     return (B, Hq, Hkv, L, d), (q, kc, vc, lens)
 
 
+def mla_workload(seed=2005):
+    B, Hq, L, dqk, dv = 16, 128, 65536, 576, 512
+    q, kc, _, lens = inputs.decode_inputs(B, Hq, 1, L, dqk, dv, n_random=16, mla=True, device="cuda", seed=seed)
+    return (B, Hq, L, dqk, dv), (q, kc, lens)
+
+
+def long_prefill_workload(seed=1004):
+    B, Hq, Hkv, L, d = 2, 32, 8, 32768, 128
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=12, local_window=4, device="cuda", seed=seed)
+    return (B, Hq, Hkv, L, d), (q, k, v)
+
+
 def calibrate_prefill(q, k, v, targets):
     B, Hq, L, _ = q.shape
     gap = torch.empty(B, Hq, -(-L // 128), -(-L // 64), dtype=torch.float32, device="cuda")
@@ -76,10 +94,10 @@ def calibrate_prefill(q, k, v, targets):
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
 
-def calibrate_decode(q, kc, vc, lens, S, targets):
+def calibrate_decode(q, kc, vc, lens, S, targets, dv=None):
     B, Hkv, L = q.shape[0], kc.shape[1], kc.shape[2]
     gap = torch.empty(B, Hkv, -(-L // 64), dtype=torch.float32, device="cuda")
-    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap)
+    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap, dv=dv)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
@@ -133,13 +151,123 @@ def cpu_baseline_prefill(q, k, v, lam, budget_s=20.0):
                       f"70% lambda, {done_s:.1f} s of fp64 work on {threads} threads"}
 
 
+def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
+    (B, Hq, Hkv, L, d), (q, k, v) = prefill_workload()
+    cal = calibrate_prefill(q, k, v, [0.5, 0.7])
+    lam70, reach70 = cal[0.7]
+    lam50, reach50 = cal[0.5]
+    log(f"prefill lambda70={lam70:.4g} (gap-map sparsity {reach70:.4f}) lambda50={lam50:.4g} ({reach50:.4f})")
+    out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
+
+    def pf(lam, cnt=None):
+        return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
+
+    dense_flops = 4.0 * B * Hq * L * L * d / 2
+    lams = {"s70": lam70, "s50": lam50, "dense": 0.0}
+    res = {}
+    for name in names:
+        lam = lams[name]
+        mean_ms, med_ms, _ = time_calls(pf(lam), steps, warmup)
+        vis, skp = counts(lambda c: pf(lam, c)())
+        res[name] = {"lambda": lam, "ms": mean_ms, "ms_median": med_ms, "visited": vis, "skipped": skp,
+                     "sparsity": skp / vis if vis else 0.0,
+                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12}
+        log(f"prefill {name}: {mean_ms:.4f} ms, sparsity {res[name]['sparsity']:.4f}, "
+            f"{res[name]['dense_equiv_tflops']:.1f} dense-equiv TFLOP/s")
+    return (q, k, v, lam70), res, dense_flops
+
+
+def bench_decode(steps, warmup, names=("s70", "s50", "dense")):
+    (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
+    S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    dout = torch.empty(DB, DHq, Dd, dtype=torch.bfloat16, device="cuda")
+    dcal = calibrate_decode(dq, kc, vc, lens, S, [0.5, 0.7])
+
+    def dc(lam, cnt=None):
+        return lambda: bl.blasst_decode(dq, kc, vc, lens, lam=lam, num_splits=S, out=dout,
+                                        workspace=work, counters=cnt)
+
+    lams = {"s70": dcal[0.7][0], "s50": dcal[0.5][0], "dense": 0.0}
+    dres = {}
+    for name in names:
+        lam = lams[name]
+        mean_ms, med_ms, _ = time_calls(dc(lam), steps, warmup)
+        vis, skp = counts(lambda c: dc(lam, c)())
+        blk = 64 * Dd * 2
+        loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
+        if S > 1:
+            loaded += 2 * DB * DHq * S * (Dd + 2) * 4
+        dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "bytes": loaded,
+                      "gbps": loaded / (mean_ms * 1e-3) / 1e9}
+        log(f"decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
+            f"{dres[name]['gbps']:.0f} GB/s on loaded bytes")
+    return S, dres
+
+
+def bench_mla(steps, warmup, names=("s70", "s50", "dense")):
+    (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
+    S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=1e-3, dv=dv)
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, dv, dtype=torch.bfloat16, device="cuda")
+    cal = calibrate_decode(q, kc, kc, lens, S, [0.5, 0.7], dv=dv)
+
+    def dc(lam, cnt=None):
+        return lambda: bl.blasst_decode(q, kc, kc, lens, lam=lam, num_splits=S, out=out, dv=dv,
+                                        workspace=work, counters=cnt)
+
+    lams = {"s70": cal[0.7][0], "s50": cal[0.5][0], "dense": 0.0}
+    res = {}
+    for name in names:
+        lam = lams[name]
+        mean_ms, _, _ = time_calls(dc(lam), steps, warmup)
+        vis, skp = counts(lambda c: dc(lam, c)())
+        # V aliases the K tile: a visited block loads its 64 x 576 latent rows once
+        loaded = vis * 64 * dqk * 2 + q.numel() * 2 + out.numel() * 2
+        if S > 1:
+            loaded += 2 * B * Hq * S * (dv + 2) * 4
+        flops = vis * 2.0 * Hq * 64 * dqk + (vis - skp) * 2.0 * Hq * 64 * dv
+        sec = mean_ms * 1e-3
+        res[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "bytes": loaded,
+                     "gbps": loaded / sec / 1e9, "tflops": flops / sec / 1e12}
+        log(f"mla decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
+            f"{res[name]['gbps']:.0f} GB/s, {res[name]['tflops']:.0f} TFLOP/s")
+    return S, res
+
+
+def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8)):
+    (B, Hq, Hkv, L, d), (q, k, v) = long_prefill_workload()
+    cal = calibrate_prefill(q, k, v, list(targets))
+    out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
+    dense_flops = 4.0 * B * Hq * L * L * d / 2
+
+    def pf(lam, cnt=None):
+        return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
+
+    rows = []
+    for t in list(targets) + [None]:
+        lam = 0.0 if t is None else cal[t][0]
+        mean_ms, _, _ = time_calls(pf(lam), steps, warmup)
+        vis, skp = counts(lambda c: pf(lam, c)())
+        rows.append({"target": t, "lambda": lam, "ms": mean_ms, "sparsity": skp / vis,
+                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12})
+        log(f"long prefill target {t}: {mean_ms:.3f} ms, sparsity {skp / vis:.4f}")
+    dense_ms = rows[-1]["ms"]
+    for r in rows:
+        r["speedup_vs_dense"] = dense_ms / r["ms"]
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode and long-prefill sections")
+    ap.add_argument("--only", choices=["prefill70", "prefill_dense", "decode70", "decode_dense", "mla70",
+                                       "mla_dense"],
+                    help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -158,34 +286,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only:
+        which, name = args.only.split("70")[0].split("_dense")[0], ("dense" if "dense" in args.only else "s70")
+        fn = {"prefill": bench_prefill, "decode": bench_decode, "mla": bench_mla}[which]
+        r = fn(steps, warmup, names=(name,))
+        print(json.dumps({"only": args.only, "result": r[1] if which == "prefill" else r}, default=str), flush=True)
+        return
+
     # ------------------------------------------------------------ prefill
-    (B, Hq, Hkv, L, d), (q, k, v) = prefill_workload()
-    cal = calibrate_prefill(q, k, v, [0.5, 0.7])
-    lam70, reach70 = cal[0.7]
-    lam50, reach50 = cal[0.5]
-    log(f"prefill lambda70={lam70:.4g} (gap-map sparsity {reach70:.4f}) lambda50={lam50:.4g} ({reach50:.4f})")
-    out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
-
-    def pf(lam, cnt=None):
-        return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
-
-    dense_flops = 4.0 * B * Hq * L * L * d / 2
-    res = {}
-    for name, lam in [("s70", lam70), ("s50", lam50), ("dense", 0.0)]:
-        mean_ms, med_ms, _ = time_calls(pf(lam), steps, warmup)
-        vis, skp = counts(lambda c: pf(lam, c)())
-        res[name] = {"lambda": lam, "ms": mean_ms, "ms_median": med_ms, "visited": vis, "skipped": skp,
-                     "sparsity": skp / vis if vis else 0.0,
-                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12}
-        log(f"prefill {name}: {mean_ms:.4f} ms, sparsity {res[name]['sparsity']:.4f}, "
-            f"{res[name]['dense_equiv_tflops']:.1f} dense-equiv TFLOP/s")
+    (q, k, v, lam70), res, dense_flops = bench_prefill(steps, warmup)
+    B, Hq, L, d = q.shape
     bc, br = 64, 128
     exec70 = res["s70"]["visited"] - res["s70"]["skipped"]
     mfma_flops70 = res["s70"]["visited"] * 2.0 * br * bc * d + exec70 * 2.0 * br * bc * d
     achieved = mfma_flops70 / (res["s70"]["ms"] * 1e-3) / 1e12
     prefill = {
         "lambda70": lam70, "sparsity70": res["s70"]["sparsity"], "ms70": res["s70"]["ms"],
-        "lambda50": lam50, "sparsity50": res["s50"]["sparsity"], "ms50": res["s50"]["ms"],
+        "lambda50": res["s50"]["lambda"], "sparsity50": res["s50"]["sparsity"], "ms50": res["s50"]["ms"],
         "ms_dense": res["dense"]["ms"],
         "dense_equiv_tflops_dense_path": res["dense"]["dense_equiv_tflops"],
         "speedup70_vs_dense": res["dense"]["ms"] / res["s70"]["ms"],
@@ -195,30 +312,9 @@ def main():
     }
 
     # ------------------------------------------------------------- decode
-    decode = None
+    decode = mla = long_prefill = None
     if not args.no_decode:
-        (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
-        S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
-        work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
-        dout = torch.empty(DB, DHq, Dd, dtype=torch.bfloat16, device="cuda")
-        dcal = calibrate_decode(dq, kc, vc, lens, S, [0.5, 0.7])
-
-        def dc(lam, cnt=None):
-            return lambda: bl.blasst_decode(dq, kc, vc, lens, lam=lam, num_splits=S, out=dout,
-                                            workspace=work, counters=cnt)
-
-        dres = {}
-        for name, lam in [("s70", dcal[0.7][0]), ("s50", dcal[0.5][0]), ("dense", 0.0)]:
-            mean_ms, med_ms, _ = time_calls(dc(lam), steps, warmup)
-            vis, skp = counts(lambda c: dc(lam, c)())
-            blk = 64 * Dd * 2
-            loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
-            if S > 1:
-                loaded += 2 * DB * DHq * S * (Dd + 2) * 4
-            dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "bytes": loaded,
-                          "gbps": loaded / (mean_ms * 1e-3) / 1e9}
-            log(f"decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
-                f"{dres[name]['gbps']:.0f} GB/s on loaded bytes")
+        S, dres = bench_decode(steps, warmup)
         decode = {
             "workload": "GQA decode B=148 Hq=32 Hkv=8 L=32768 d=128 bf16, block 64, one query token per sequence",
             "num_splits": S,
@@ -230,7 +326,28 @@ def main():
             "roofline": {"bound": "hbm", "achieved": dres["s70"]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dres["s70"]["gbps"] / PEAK_HBM_GBS, "traffic": None},
         }
-        del dq, kc, vc, work, dout
+        torch.cuda.empty_cache()
+        S, mres = bench_mla(steps, warmup)
+        m70 = mres["s70"]
+        mla = {
+            "workload": "latent (MLA) decode B=16 Hq=128 sharing one KV head, dqk=576 dv=512 (V = K[..., :512]), "
+                        "L=65536, bf16 cache, block 64",
+            "num_splits": S,
+            "us_per_step70": m70["us"], "sparsity70": m70["sparsity"],
+            "us_per_step50": mres["s50"]["us"], "sparsity50": mres["s50"]["sparsity"],
+            "us_per_step_dense": mres["dense"]["us"],
+            "speedup70_vs_dense": mres["dense"]["us"] / m70["us"],
+            "hbm_gbps70": m70["gbps"], "mfma_tflops70": m70["tflops"],
+            "mfma_tflops_dense": mres["dense"]["tflops"], "hbm_gbps_dense": mres["dense"]["gbps"],
+            "roofline": {"bound": "hbm", "achieved": m70["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": m70["gbps"] / PEAK_HBM_GBS, "traffic": None,
+                         "mfma_frac": m70["tflops"] / PEAK_BF16_TFLOPS},
+        }
+        torch.cuda.empty_cache()
+        long_prefill = {
+            "workload": "GQA causal prefill B=2 Hq=32 Hkv=8 L=32768 d=128 bf16, query tile 128, key block 64",
+            "sweep": bench_long_prefill(max(2, steps // 4), max(1, warmup // 2)),
+        }
         torch.cuda.empty_cache()
 
     cpu = None
@@ -251,6 +368,8 @@ def main():
                    "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
         "prefill": prefill,
         "decode": decode,
+        "mla_decode": mla,
+        "long_prefill": long_prefill,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
         "cpu_baseline": cpu,

@@ -186,6 +186,9 @@ blasst_status validate_decode(const blasst_decode_params *p)
                     "decode supports dqk = dv in {64,128} with Hq/Hkv <= 16, or dqk=576, dv=512, Hkv=1, Hq=128");
     if (kind == KIND_MLA && p->v_cache.ptr != p->k_cache.ptr)
         return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs v_cache to alias k_cache");
+    // the latent kernel addresses a sequence's cache rows with 32-bit byte offsets
+    if (kind == KIND_MLA && p->Lmax * p->k_cache.st * 2 >= ((int64_t)1 << 31))
+        return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs Lmax * token stride * 2 < 2^31 bytes");
     const int64_t nkb = (p->Lmax + 63) / 64;
     if (p->num_splits < 0 || p->num_splits > nkb)
         return fail(BLASST_ERR_INVALID_ARG, "num_splits must be in 0..ceil(Lmax/64)");

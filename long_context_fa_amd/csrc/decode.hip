@@ -317,46 +317,54 @@ void decode_gqa_kernel(const DecodeArgs a)
     }
 }
 
-// Log-sum-exp merge of split partials: one workgroup per (query head, seq).
+// Log-sum-exp merge of split partials.  A thread owns 4 consecutive output
+// columns of one (sequence, query head); a workgroup covers 256 / (dv/4)
+// heads.  Weights are exp2(m_s - M) with M the largest split max among
+// splits that saw keys; splits with l = 0 contribute nothing.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a, int dv)
 {
-    const int hq = blockIdx.x, b = blockIdx.y;
+    const int tph = dv / 4, hpw = 256 / tph;
+    const int hq = blockIdx.x * hpw + (int)threadIdx.x / tph;
+    const int b = blockIdx.y;
+    if (hq >= a.Hq)
+        return;
+    const int d = 4 * ((int)threadIdx.x % tph);
     const int G = a.G, g = hq / G, hd = hq % G, S = a.num_splits;
     const int64_t pu0 = ((int64_t)(b * a.Hkv + g) * S) * G + hd;
     float M = neg_inf();
     for (int s = 0; s < S; ++s) {
-        const float ls = a.part_ml[2 * (pu0 + (int64_t)s * G) + 1];
-        const float ms = a.part_ml[2 * (pu0 + (int64_t)s * G)];
-        if (ls > 0.f)
-            M = fmaxf(M, ms);
+        const float2 ml = *(const float2 *)(a.part_ml + 2 * (pu0 + (int64_t)s * G));
+        if (ml.y > 0.f)
+            M = fmaxf(M, ml.x);
     }
     const float Ms = M == neg_inf() ? 0.f : M;
-    for (int d = threadIdx.x; d < dv; d += blockDim.x) {
-        float num = 0.f, den = 0.f;
-        for (int s = 0; s < S; ++s) {
-            const int64_t pu = pu0 + (int64_t)s * G;
-            const float ls = a.part_ml[2 * pu + 1];
-            if (!(ls > 0.f))
-                continue;
-            const float wgt = exp2_hw(a.part_ml[2 * pu] - Ms);
-            num += wgt * a.part_o[pu * dv + d];
-            den += wgt * ls;
-        }
-        const float val = den > 0.f ? num / den : 0.f;
-        const int64_t off = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + d;
-        if (OUT_BF16)
-            ((__bf16 *)a.o)[off] = (__bf16)val;
-        else
-            ((float *)a.o)[off] = val;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+        const int64_t pu = pu0 + (int64_t)s * G;
+        const float2 ml = *(const float2 *)(a.part_ml + 2 * pu);
+        const f32x4 po = *(const f32x4 *)(a.part_o + pu * dv + d);
+        const float wgt = ml.y > 0.f ? exp2_hw(ml.x - Ms) : 0.f;
+        num += wgt * po;
+        den += wgt * ml.y;
     }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const f32x4 val = num * inv;
+    const int64_t off = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + d;
+    if (OUT_BF16)
+        *(bf16x4 *)((__bf16 *)a.o + off) = __builtin_convertvector(val, bf16x4);
+    else
+        *(f32x4 *)((float *)a.o + off) = val;
 }
 
 } // namespace
 
 hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_t stream)
 {
-    const dim3 grid(a.Hq, a.B), block(dv < 256 ? dv : 256);
+    const int hpw = 256 / (dv / 4);
+    const dim3 grid((a.Hq + hpw - 1) / hpw, a.B), block(256);
     if (out_bf16)
         hipLaunchKernelGGL((decode_combine_kernel<true>), grid, block, 0, stream, a, dv);
     else

@@ -14,8 +14,11 @@
 // hold the 576-wide Q^T operand in VGPRs and its 512x32 O^T accumulator in
 // AGPRs) walks the key blocks of one (sequence, split):
 //  * the 64 x 576 bf16 K tile (72 KB) is copied global -> LDS with
-//    global_load_lds_dwordx4 into a double buffer; 16-byte chunks are
-//    XOR-swizzled by row inside aligned groups of 8 chunks;
+//    global_load_lds_dwordx4 into a double buffer, issued between the score
+//    MFMAs of the previous block.  In LDS a tile is a latent region (64 rows
+//    of 512 columns, one 1 KB copy per row) and a rope region (64 rows of 64
+//    columns); 16-byte chunks are XOR-swizzled by row so that the operand
+//    reads hit distinct banks;
 //  * S^T = K Q^T with the 32x32x16 bf16 MFMA (per-lane head statistics, as in
 //    prefill); the 4 wave votes are exchanged through LDS;
 //  * executed blocks: online softmax (rescale skipped when no head raised
@@ -32,10 +35,12 @@ namespace {
 
 constexpr int BC = 64;
 constexpr int DQK = 576, DV = 512;
-constexpr int RB = DQK * 2;          // 1152 bytes per K row
-constexpr int TB = BC * RB;          // 73728 bytes per tile
-constexpr int NWM = 4;               // waves (32 heads each)
-constexpr int CPW = TB / 1024 / NWM; // 1 KB copies per tile per wave (18)
+constexpr int LRB = DV * 2;              // 1024 bytes per latent row in LDS
+constexpr int RRB = (DQK - DV) * 2;      // 128 bytes per rope row in LDS
+constexpr int ROPE = BC * LRB;           // rope region offset in a tile (64 KB)
+constexpr int TB = BC * (LRB + RRB);     // 73728 bytes per tile
+constexpr int NWM = 4;                   // waves (32 heads each)
+constexpr int CPW = TB / 1024 / NWM;     // 1 KB copies per tile per wave (18)
 constexpr int NKK = DQK / 16;        // QK k-steps (36)
 constexpr int NDT = DV / 32;         // O^T d tiles (16)
 
@@ -119,9 +124,15 @@ __device__ __forceinline__ f32x16 o_read(int dt)
     return r;
 }
 // S^T accumulation (VGPR accumulators).
-__device__ __forceinline__ void mfma_v_first(f32x16 &c, const u32x4 &a, const bf16x8 &b)
+// First k-step of both key tiles in one statement: the early-clobber outputs
+// cannot overlap either A operand while the first MFMA may still read it.
+__device__ __forceinline__ void mfma_v_first2(f32x16 &c0, f32x16 &c1, const u32x4 &a0, const u32x4 &a1,
+                                              const bf16x8 &b)
 {
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
+                 "v_mfma_f32_32x32x16_bf16 %1, %3, %4, 0"
+                 : "=&v"(c0), "=&v"(c1)
+                 : "v"(a0), "v"(a1), "v"(b));
 }
 __device__ __forceinline__ void mfma_v(f32x16 &c, const u32x4 &a, const bf16x8 &b)
 {
@@ -132,8 +143,15 @@ __device__ __forceinline__ void mfma_v_drain(f32x16 &c0, f32x16 &c1)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
 }
 
-// 3-bit swizzle: keeps chunks inside aligned groups of 8 (a row has 72).
-__device__ __forceinline__ int swz8(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Chunk swizzles.  Latent rows (64 chunks, bank-aligned): physical chunk p of
+// row r holds logical chunk p ^ swzl(r), a 4-bit XOR that is a permutation
+// over r mod 16, so the 16 rows of a ds_read_b128 phase hit 16 distinct bank
+// groups, and whose bits 2-3 differ across each aligned quad of rows, so the
+// 4 rows x 4 chunks of a 32-lane ds_read_b64_tr_b16 phase do too.  Rope rows
+// (8 chunks, 128 bytes): p ^ swzr(r), distinct over the 8 even and the 8 odd
+// rows of a phase.
+__host__ __device__ constexpr int swzl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__host__ __device__ constexpr int swzr(int r) { return (r >> 1) & 7; }
 
 template <bool SKIP, bool OUT_BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -169,58 +187,50 @@ void decode_mla_kernel(const DecodeArgs a)
             qf[kk] = as_bf16x8(*(const u32x4 *)(qp + 16 * kk + 8 * hh));
     }
 
-    // Tile copy: wave w fills rows [16w, 16w+16) of the tile, 18 DMA copies
-    // of 1 KB; copy i, lane l covers physical chunk 64i + l of those rows.
-    // The physical chunk (row, pc) holds logical chunk pc ^ swz8(row).  The
-    // per-lane offsets are recomputed each tile (cheap VALU) rather than held
-    // in 18 registers.  Rows past len re-read row len-1 (masked later).
+    // Tile copy: wave w fills rows [16w, 16w+16) with 18 DMA copies of 1 KB:
+    // copy i < 16 is the latent part of row 16w+i (lane l loads logical
+    // chunk l ^ swzl(i) into physical chunk l), copies 16 and 17 are the rope
+    // parts of 8 rows each (lane l: row +l/8, physical chunk l%8, logical
+    // chunk (l%8) ^ swzr(row)).  Rows past len re-read row len-1 (finite
+    // data, masked later).  Offsets are 32-bit from the sequence base (the
+    // host checks Lmax * row stride).
     auto tile = [&](int j) { return smem + (j & 1) * TB; };
-    auto copy_tile = [&](int j) {
-        char *dst = tile(j) + w * (16 * RB);
-        int lv = lane;
-        asm volatile("" : "+v"(lv)); // keep the offset arithmetic in the loop
-        int row = 16 * w + lv / 72, pc = lv % 72;
-        if ((j + 1) * BC <= len) {
-            const uint16_t *sb = kp + (int64_t)j * BC * a.k_st;
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-                const int c = pc ^ swz8(row);
-                copy16_to_lds_s(sb, (uint32_t)((row * (int)a.k_st + c * 8) * 2), dst + i * 1024);
-                pc += 64;
-                const bool wrap = pc >= 72;
-                pc = wrap ? pc - 72 : pc;
-                row += wrap ? 1 : 0;
-            }
+    const uint32_t rowb = (uint32_t)a.k_st * 2;
+    auto copy_one = [&](int j, int i) {
+        char *t = tile(j);
+        if (i < 16) {
+            int key = j * BC + 16 * w + i;
+            key = key < len ? key : len - 1;
+            copy16_to_lds_s(kp + (int64_t)key * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))), t + (16 * w + i) * LRB);
         } else {
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-                const int c = pc ^ swz8(row);
-                int key = j * BC + row;
-                key = key < len ? key : len - 1;
-                copy16_to_lds(kp + (int64_t)key * a.k_st + c * 8, dst + i * 1024);
-                pc += 64;
-                const bool wrap = pc >= 72;
-                pc = wrap ? pc - 72 : pc;
-                row += wrap ? 1 : 0;
-            }
+            const int e = i - 16;
+            int lr = lane >> 3;
+            asm volatile("" : "+v"(lr)); // no loop-carried per-lane key registers
+            int key = j * BC + 16 * w + 8 * e + lr;
+            key = key < len ? key : len - 1;
+            const uint32_t off = LRB + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7)); // swzr of the row
+            copy16_to_lds_s(kp, (uint32_t)key * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
         }
     };
 
-    // LDS read offsets.  K operand (row n, logical chunk 2kk + hh): chunk
-    // 8(kk/4) + ((2(kk%4) + hh) ^ swz8(n)), so 4 per-lane offsets plus
-    // immediates; row n + 32 has the same swizzle.  V^T operand (rows
-    // 16u + 4vh + vj (+8), chunk 4dt + 2vmb + vq/2): 2 per-lane offsets.
+    // LDS read offsets.  K operand, lane (n, hh), logical chunk c = 2kk + hh:
+    // latent (kk < 32) at row n, chunk (c & 48) | ((c & 15) ^ swzl(n)): 8
+    // per-lane offsets (kk % 8) plus immediates, the same for row n + 32; rope
+    // (kk >= 32) at row n, chunk (c - 64) ^ swzr(n), computed per block.  V^T
+    // operand: rows 16u + 4vh + vj and that + 8, logical chunk
+    // 4dt + 2vmb + vq/2: 4 per-lane offsets (dt % 4) for each row quad.
     const int vg = lane >> 4, vs = lane & 15;
     const int vmb = vg & 1, vh = vg >> 1, vj = vs >> 2, vq = vs & 3;
-    int koff[4], voffv[2];
+    int koffl[8], voffv[2][4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-        koff[q4] = n * RB + ((2 * q4 + hh) ^ swz8(n)) * 16;
-    {
-        const int ra = 4 * vh + vj;
+    for (int q = 0; q < 8; ++q)
+        koffl[q] = n * LRB + ((2 * q + hh) ^ swzl(n)) * 16;
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-            voffv[x] = ra * RB + ((4 * x + 2 * vmb + (vq >> 1)) ^ swz8(ra)) * 16 + (vq & 1) * 8;
+    for (int t = 0; t < 2; ++t) {
+        const int ra = 4 * vh + vj + 8 * t;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            voffv[t][x] = ra * LRB + ((4 * x + 2 * vmb + (vq >> 1)) ^ swzl(ra)) * 16 + (vq & 1) * 8;
     }
 
     o_zero();
@@ -228,21 +238,29 @@ void decode_mla_kernel(const DecodeArgs a)
     int n_skipped = 0;
 
     if (jb < je) {
-        copy_tile(jb);
-        if (jb + 1 < je) {
-            copy_tile(jb + 1);
-            wait_vmcnt<CPW>();
-        } else {
-            wait_vmcnt<0>();
-        }
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            copy_one(jb, i);
+        wait_vmcnt<0>();
         lds_barrier();
     }
     for (int j = jb; j < je; ++j) {
         const char *kb = tile(j);
-        // S^T = K_j Q^T, K operands read two k-steps ahead.
+        // S^T = K_j Q^T, K operands read one k-step ahead.  The copy of
+        // K_{j+1} into the other buffer (free since the last barrier) is
+        // issued between the score MFMAs, one 1 KB copy every two k-steps
+        // (a DMA instruction holds the wave until the address unit accepts
+        // it, so a burst would stall the MFMA stream).
+        const bool dma = j + 1 < je;
         f32x16 sc[2];
+        // rope offsets are recomputed here (4 per block) to spare registers
+        int nl = n;
+        asm volatile("" : "+v"(nl));
         auto kread = [&](int kk, int kt) {
-            return *(const u32x4 *)(kb + koff[kk & 3] + 128 * (kk >> 2) + kt * 32 * RB);
+            if (kk < 32)
+                return *(const u32x4 *)(kb + koffl[kk & 7] + 256 * (kk >> 3) + kt * 32 * LRB);
+            const int koffr = ROPE + nl * RRB + ((2 * (kk - 32) + hh) ^ swzr(nl)) * 16;
+            return *(const u32x4 *)(kb + koffr + kt * 32 * RRB);
         };
         u32x4 ka[2][2];
 #pragma unroll
@@ -256,11 +274,13 @@ void decode_mla_kernel(const DecodeArgs a)
                     ka[(kk + 1) & 1][kt] = kread(kk + 1, kt);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if ((kk & 1) == 0 && dma)
+                copy_one(j + 1, kk >> 1);
+            if (kk == 0) {
+                mfma_v_first2(sc[0], sc[1], ka[0][0], ka[0][1], qf[0]);
+            } else {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                if (kk == 0)
-                    mfma_v_first(sc[kt], ka[0][kt], qf[0]);
-                else
+                for (int kt = 0; kt < 2; ++kt)
                     mfma_v(sc[kt], ka[kk & 1][kt], qf[kk]);
             }
         }
@@ -296,8 +316,7 @@ void decode_mla_kernel(const DecodeArgs a)
                     gapw[par][w] = wgap;
             }
         }
-        // Own part of K_{j+1} landed; votes and K_{j+1} visible after this.
-        wait_vmcnt<0>();
+        // Votes visible after this (the copy of K_{j+1} stays in flight).
         lds_barrier();
         bool skip = false;
         if (SKIP) {
@@ -321,33 +340,30 @@ void decode_mla_kernel(const DecodeArgs a)
         if (!skip) {
             const float mnew = fmaxf(m2, mt2);
             const float msafe = mnew == neg_inf() ? 0.f : mnew;
-            float rs = 0.f;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                f32x8 lo, hi;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float p0 = exp2_hw(__builtin_fmaf(sc[kt][r], a.scale_log2, -msafe));
-                    const float p1 = exp2_hw(__builtin_fmaf(sc[kt][r + 8], a.scale_log2, -msafe));
-                    lo[r] = p0;
-                    hi[r] = p1;
-                    rs += p0 + p1;
-                }
-                pf[2 * kt] = cvt_bf16x8(lo);
-                pf[2 * kt + 1] = cvt_bf16x8(hi);
-            }
             const float alpha = mnew > m2 ? exp2_hw(m2 - msafe) : 1.f;
-            lsum = alpha * lsum + rs;
             if (__any(mnew > m2))
                 o_rescale(alpha);
             m2 = mnew;
+            // P^T for k-step u (keys 16u..16u+15 in the sigma order) is
+            // sc[u/2][8(u%2) + r]; the exponentials of step u+1 are spread
+            // between the P.V MFMAs of step u.
+            float rs = 0.f;
+            f32x8 pv8;
+            auto pexp = [&](int u, int r) {
+                const float p = exp2_hw(__builtin_fmaf(sc[u >> 1][8 * (u & 1) + r], a.scale_log2, -msafe));
+                pv8[r] = p;
+                rs += p;
+            };
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                pexp(0, r);
+            bf16x8 pf = cvt_bf16x8(pv8);
             // O^T += V^T P^T, V = first 512 columns of the K tile.
             auto vread = [&](int m) {
                 const int u = m / NDT, dt = m % NDT;
-                const char *va0 = kb + voffv[dt & 1] + 16 * u * RB + 128 * (dt >> 1);
-                const i16x4 x0 = lds_read_tr16(va0);
-                const i16x4 x1 = lds_read_tr16(va0 + 8 * RB);
+                const char *vb = kb + 16 * u * LRB + 256 * (dt >> 2);
+                const i16x4 x0 = lds_read_tr16(vb + voffv[0][dt & 3]);
+                const i16x4 x1 = lds_read_tr16(vb + voffv[1][dt & 3]);
                 const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
                 return u32x4{y0[0], y0[1], y1[0], y1[1]};
             };
@@ -356,20 +372,32 @@ void decode_mla_kernel(const DecodeArgs a)
 #pragma unroll
             for (int m = 0; m < 2; ++m)
                 va[m] = vread(m);
+            bf16x8 pnext = pf;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
+                const int u = m / NDT, dt = m % NDT;
                 if (m + 2 < NM)
                     va[(m + 2) % 3] = vread(m + 2);
                 __builtin_amdgcn_sched_barrier(0);
-                o_mfma(m % NDT, va[m % 3], pf[m / NDT]);
+                if (dt == 0)
+                    pf = pnext;
+                o_mfma(dt, va[m % 3], pf);
+                if (u + 1 < 4) {
+                    if (dt < 8)
+                        pexp(u + 1, dt);
+                    else if (dt == 8)
+                        pnext = cvt_bf16x8(pv8);
+                }
             }
             mfma_drain();
+            lsum = alpha * lsum + rs;
         } else {
             ++n_skipped;
         }
-        lds_barrier(); // every wave is done with tile j
-        if (j + 2 < je)
-            copy_tile(j + 2);
+        // Own part of K_{j+1} landed; after the barrier every wave is done
+        // with tile j and all of K_{j+1} is visible.
+        wait_vmcnt<0>();
+        lds_barrier();
     }
 
     // Output: O^T lane (n, hh) holds head `head`, d = 32dt + 8g + 4hh + i.
