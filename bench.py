@@ -47,19 +47,45 @@ def log(*a):
 
 
 def time_calls(fn, steps, warmup):
-    """Average ms per call over ``steps`` calls, timed with events on the launch stream."""
+    """ms per call: ``warmup`` untimed calls, then ``steps`` calls enqueued back to back
+    between two events on the launch stream, bracketed by device synchronisation."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for s, e in ev:
-        s.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
         fn()
-        e.record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
-    per = [s.elapsed_time(e) for s, e in ev]
-    return float(np.mean(per)), float(np.median(per)), per
+    ms = start.elapsed_time(end) / steps
+    return ms, ms, None
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "long_context_fa_amd", "csrc")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE passes, or None when
+    the record is missing or the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if not line.startswith("traffic " + workload + " "):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split()[2:])
+        h = hashlib.sha256()
+        for src in f["sources"].split(","):
+            h.update(open(os.path.join(CSRC, src), "rb").read())
+        if h.hexdigest()[:16] != f["sha"]:
+            return None
+        return float(f["bytes_per_launch"])
+    return None
 
 
 def prefill_workload(seed=1001):
@@ -145,10 +171,12 @@ def cpu_baseline_prefill(q, k, v, lam, budget_s=20.0):
         if done_s + 2 * dt > budget_s:
             break
         batch *= 2
+    what = (f"all {n_units} query tiles (the whole workload)" if n_units == len(all_units)
+            else f"{n_units} random query tiles of {len(all_units)}")
     return {"value": done_flops / done_s / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_units} random query tiles (128 rows) of the 1x32/8x8192x128 prefill at the "
-                      f"70% lambda, {done_s:.1f} s of fp64 work on {threads} threads"}
+            "sample": f"{what}, 128 rows each, of the 1x32/8x8192x128 causal prefill at the 70% lambda: "
+                      f"{done_s:.1f} s of fp64 work on {threads} threads"}
 
 
 def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
@@ -167,9 +195,9 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
     res = {}
     for name in names:
         lam = lams[name]
-        mean_ms, med_ms, _ = time_calls(pf(lam), steps, warmup)
+        mean_ms, _, _ = time_calls(pf(lam), steps, warmup)
         vis, skp = counts(lambda c: pf(lam, c)())
-        res[name] = {"lambda": lam, "ms": mean_ms, "ms_median": med_ms, "visited": vis, "skipped": skp,
+        res[name] = {"lambda": lam, "ms": mean_ms, "visited": vis, "skipped": skp,
                      "sparsity": skp / vis if vis else 0.0,
                      "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12}
         log(f"prefill {name}: {mean_ms:.4f} ms, sparsity {res[name]['sparsity']:.4f}, "
@@ -192,7 +220,7 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense")):
     dres = {}
     for name in names:
         lam = lams[name]
-        mean_ms, med_ms, _ = time_calls(dc(lam), steps, warmup)
+        mean_ms, _, _ = time_calls(dc(lam), steps, warmup)
         vis, skp = counts(lambda c: dc(lam, c)())
         blk = 64 * Dd * 2
         loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
@@ -324,7 +352,8 @@ def main():
             "speedup70_vs_dense": dres["dense"]["us"] / dres["s70"]["us"],
             "speedup50_vs_dense": dres["dense"]["us"] / dres["s50"]["us"],
             "roofline": {"bound": "hbm", "achieved": dres["s70"]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": dres["s70"]["gbps"] / PEAK_HBM_GBS, "traffic": None},
+                         "frac": dres["s70"]["gbps"] / PEAK_HBM_GBS, "traffic": measured_traffic("decode70"),
+                         "algorithmic_bytes": dres["s70"]["bytes"]},
         }
         torch.cuda.empty_cache()
         S, mres = bench_mla(steps, warmup)
@@ -340,8 +369,8 @@ def main():
             "hbm_gbps70": m70["gbps"], "mfma_tflops70": m70["tflops"],
             "mfma_tflops_dense": mres["dense"]["tflops"], "hbm_gbps_dense": mres["dense"]["gbps"],
             "roofline": {"bound": "hbm", "achieved": m70["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": m70["gbps"] / PEAK_HBM_GBS, "traffic": None,
-                         "mfma_frac": m70["tflops"] / PEAK_BF16_TFLOPS},
+                         "frac": m70["gbps"] / PEAK_HBM_GBS, "traffic": measured_traffic("mla70"),
+                         "algorithmic_bytes": m70["bytes"], "mfma_frac": m70["tflops"] / PEAK_BF16_TFLOPS},
         }
         torch.cuda.empty_cache()
         long_prefill = {
@@ -371,7 +400,8 @@ def main():
         "mla_decode": mla,
         "long_prefill": long_prefill,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill70"),
+                     "algorithmic_flops": mfma_flops70},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
