@@ -26,7 +26,7 @@
 //    (ds_read_b64_tr_b16) from the same K tile;
 //  * split partials (O, max, sum) go to the workspace for the log-sum-exp
 //    combine kernel, or O is written directly for a single split.
-#include "device.h"
+#include "acc.h"
 #include "kernels.h"
 
 namespace blasst {
@@ -45,103 +45,8 @@ constexpr int NKK = DQK / 16;        // QK k-steps (36)
 constexpr int NDT = DV / 32;         // O^T d tiles (16)
 
 // Register placement.  Each wave owns 32 heads.  The O^T accumulator
-// (512 x 32 fp32) is pinned in the 256 AGPRs, d-tile dt in a[16dt, 16dt+16);
-// Q^T, the scores and the MFMA operands live in the 256 VGPRs.  Every access
-// to the accumulator (zeroing, the P.V MFMAs, rescaling, read-out) is inline
-// asm on the physical registers, and the compiler, which sees no AGPR values,
-// keeps its own values in VGPRs (a CPU test checks the generated code for
-// AGPR use outside these blocks).  The score MFMAs are asm too, with VGPR
-// accumulators.  Hazard padding is explicit because the compiler does not
-// see through asm: three wait states before each MFMA cover a VALU or
-// accvgpr write of its sources, and 24 wait states follow the last MFMA of a
-// chain before any other instruction reads its result.
-#define MLA_ALL_AGPRS \
-    "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", \
-    "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", \
-    "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", \
-    "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63", \
-    "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79", \
-    "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95", \
-    "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111", \
-    "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", \
-    "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143", \
-    "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159", \
-    "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", \
-    "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191", \
-    "a192", "a193", "a194", "a195", "a196", "a197", "a198", "a199", "a200", "a201", "a202", "a203", "a204", "a205", "a206", "a207", \
-    "a208", "a209", "a210", "a211", "a212", "a213", "a214", "a215", "a216", "a217", "a218", "a219", "a220", "a221", "a222", "a223", \
-    "a224", "a225", "a226", "a227", "a228", "a229", "a230", "a231", "a232", "a233", "a234", "a235", "a236", "a237", "a238", "a239", \
-    "a240", "a241", "a242", "a243", "a244", "a245", "a246", "a247", "a248", "a249", "a250", "a251", "a252", "a253", "a254", "a255"
-
-__device__ __forceinline__ void o_zero()
-{
-    asm volatile(".set .Lmo, 0\n\t.rept 256\n\tv_accvgpr_write_b32 a[.Lmo], 0\n\t"
-                 ".set .Lmo, .Lmo+1\n\t.endr" ::: MLA_ALL_AGPRS);
-}
-// O^T[dt] += V^T P^T for one d-tile (dt a compile-time constant after unrolling).
-__device__ __forceinline__ void o_mfma(int dt, const u32x4 &a, const bf16x8 &b)
-{
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 a[%2:%3], %0, %1, a[%2:%3]"
-                 ::"v"(a), "v"(b), "i"(16 * dt), "i"(16 * dt + 15));
-}
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
-// O^T *= alpha (per lane: alpha of the lane's head), four registers at a time.
-__device__ __forceinline__ void o_rescale(float alpha)
-{
-    float t0, t1, t2, t3;
-    asm volatile(".set .Lmo, 0\n\t.rept 64\n\t"
-                 "v_accvgpr_read_b32 %0, a[.Lmo]\n\tv_accvgpr_read_b32 %1, a[.Lmo+1]\n\t"
-                 "v_accvgpr_read_b32 %2, a[.Lmo+2]\n\tv_accvgpr_read_b32 %3, a[.Lmo+3]\n\t"
-                 "v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\t"
-                 "v_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\t"
-                 "v_accvgpr_write_b32 a[.Lmo], %0\n\tv_accvgpr_write_b32 a[.Lmo+1], %1\n\t"
-                 "v_accvgpr_write_b32 a[.Lmo+2], %2\n\tv_accvgpr_write_b32 a[.Lmo+3], %3\n\t"
-                 ".set .Lmo, .Lmo+4\n\t.endr"
-                 : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
-                 : "v"(alpha)
-                 : MLA_ALL_AGPRS);
-}
-// Reads the 16 accumulator registers of d-tile dt.
-__device__ __forceinline__ f32x16 o_read(int dt)
-{
-    float e[16];
-    asm volatile("v_accvgpr_read_b32 %0, a[%16]\n\tv_accvgpr_read_b32 %1, a[%16+1]\n\t"
-                 "v_accvgpr_read_b32 %2, a[%16+2]\n\tv_accvgpr_read_b32 %3, a[%16+3]\n\t"
-                 "v_accvgpr_read_b32 %4, a[%16+4]\n\tv_accvgpr_read_b32 %5, a[%16+5]\n\t"
-                 "v_accvgpr_read_b32 %6, a[%16+6]\n\tv_accvgpr_read_b32 %7, a[%16+7]\n\t"
-                 "v_accvgpr_read_b32 %8, a[%16+8]\n\tv_accvgpr_read_b32 %9, a[%16+9]\n\t"
-                 "v_accvgpr_read_b32 %10, a[%16+10]\n\tv_accvgpr_read_b32 %11, a[%16+11]\n\t"
-                 "v_accvgpr_read_b32 %12, a[%16+12]\n\tv_accvgpr_read_b32 %13, a[%16+13]\n\t"
-                 "v_accvgpr_read_b32 %14, a[%16+14]\n\tv_accvgpr_read_b32 %15, a[%16+15]"
-                 : "=v"(e[0]), "=v"(e[1]), "=v"(e[2]), "=v"(e[3]), "=v"(e[4]), "=v"(e[5]),
-                   "=v"(e[6]), "=v"(e[7]), "=v"(e[8]), "=v"(e[9]), "=v"(e[10]), "=v"(e[11]),
-                   "=v"(e[12]), "=v"(e[13]), "=v"(e[14]), "=v"(e[15])
-                 : "i"(16 * dt));
-    f32x16 r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        r[i] = e[i];
-    return r;
-}
-// S^T accumulation (VGPR accumulators).
-// First k-step of both key tiles in one statement: the early-clobber outputs
-// cannot overlap either A operand while the first MFMA may still read it.
-__device__ __forceinline__ void mfma_v_first2(f32x16 &c0, f32x16 &c1, const u32x4 &a0, const u32x4 &a1,
-                                              const bf16x8 &b)
-{
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
-                 "v_mfma_f32_32x32x16_bf16 %1, %3, %4, 0"
-                 : "=&v"(c0), "=&v"(c1)
-                 : "v"(a0), "v"(a1), "v"(b));
-}
-__device__ __forceinline__ void mfma_v(f32x16 &c, const u32x4 &a, const bf16x8 &b)
-{
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_drain(f32x16 &c0, f32x16 &c1)
-{
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
-}
+// (512 x 32 fp32) is pinned in the 256 AGPRs, d-tile dt in a[16dt, 16dt+16)
+// (acc.h); Q^T, the scores and the MFMA operands live in the 256 VGPRs.
 
 // Chunk swizzles.  Latent rows (64 chunks, bank-aligned): physical chunk p of
 // row r holds logical chunk p ^ swzl(r), a 4-bit XOR that is a permutation
@@ -233,7 +138,7 @@ void decode_mla_kernel(const DecodeArgs a)
             voffv[t][x] = ra * LRB + ((4 * x + 2 * vmb + (vq >> 1)) ^ swzl(ra)) * 16 + (vq & 1) * 8;
     }
 
-    o_zero();
+    acc_zero();
     float m2 = neg_inf(), lsum = 0.f;
     int n_skipped = 0;
 
@@ -284,7 +189,7 @@ void decode_mla_kernel(const DecodeArgs a)
                     mfma_v(sc[kt], ka[kk & 1][kt], qf[kk]);
             }
         }
-        mfma_v_drain(sc[0], sc[1]);
+        mfma_v_drain2(sc[0], sc[1]);
         const int k0 = j * BC;
         if (k0 + BC > len) {
 #pragma unroll
@@ -342,7 +247,7 @@ void decode_mla_kernel(const DecodeArgs a)
             const float msafe = mnew == neg_inf() ? 0.f : mnew;
             const float alpha = mnew > m2 ? exp2_hw(m2 - msafe) : 1.f;
             if (__any(mnew > m2))
-                o_rescale(alpha);
+                acc_scale(alpha);
             m2 = mnew;
             // P^T for k-step u (keys 16u..16u+15 in the sigma order) is
             // sc[u/2][8(u%2) + r]; the exponentials of step u+1 are spread
@@ -381,7 +286,7 @@ void decode_mla_kernel(const DecodeArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 if (dt == 0)
                     pf = pnext;
-                o_mfma(dt, va[m % 3], pf);
+                acc_mfma(16 * dt, va[m % 3], pf);
                 if (u + 1 < 4) {
                     if (dt < 8)
                         pexp(u + 1, dt);
@@ -408,7 +313,7 @@ void decode_mla_kernel(const DecodeArgs a)
         const int64_t base = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const f32x16 od = o_read(dt);
+            const f32x16 od = acc_read(16 * dt);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * dt + 8 * g + 4 * hh;
@@ -424,7 +329,7 @@ void decode_mla_kernel(const DecodeArgs a)
         const int64_t pu = ((int64_t)b * S + s) * 128 + head; // Hkv = 1, G = 128
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const f32x16 od = o_read(dt);
+            const f32x16 od = acc_read(16 * dt);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * dt + 8 * g + 4 * hh;

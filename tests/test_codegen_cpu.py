@@ -1,7 +1,8 @@
-"""Code-generation guards for the latent decode kernel (CPU: hipcc cross-compiles).
+"""Code-generation guards for the kernels with AGPR-pinned accumulators (the
+latent decode kernel; CPU: hipcc cross-compiles).
 
-The latent kernel keeps its O^T accumulator in the physical AGPRs a0..a255
-and touches them only from inline asm.  That is sound only while the
+These kernels keep their O^T accumulator in physical AGPRs and touch them
+only from inline asm.  That is sound only while the
 compiler itself allocates no AGPR (for a value, a spill or an MFMA it
 emits) and the kernel descriptor reserves all 256 AGPRs.  These tests compile
 the source to assembly with the library's own flags and check both, so that
@@ -21,13 +22,16 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hi
                                 reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def mla_asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "mla.s"
-    cmd = [B.HIPCC] + B.FLAGS + ["-S", "--cuda-device-only", os.path.join(B.CSRC, "mla.hip"), "-o", str(out)]
+KERNELS = {"mla.hip": "decode_mla_kernel"}
+
+
+@pytest.fixture(scope="module", params=sorted(KERNELS))
+def kasm(request, tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / (request.param + ".s")
+    cmd = [B.HIPCC] + B.FLAGS + ["-S", "--cuda-device-only", os.path.join(B.CSRC, request.param), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    return out.read_text()
+    return KERNELS[request.param], out.read_text()
 
 
 def _outside_asm(text):
@@ -42,17 +46,19 @@ def _outside_asm(text):
     return keep
 
 
-def test_compiler_emits_no_agpr_access(mla_asm):
+def test_compiler_emits_no_agpr_access(kasm):
+    _, text = kasm
     agpr = re.compile(r"\ba\[\d|\ba\d+\b|accvgpr")
-    bad = [l for l in _outside_asm(mla_asm) if agpr.search(l) and not l.strip().startswith(".")]
+    bad = [l for l in _outside_asm(text) if agpr.search(l) and not l.strip().startswith(".")]
     assert not bad, "compiler-generated AGPR access:\n" + "\n".join(bad[:10])
 
 
-def test_no_scratch_and_all_agprs_reserved(mla_asm):
-    kernels = re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", mla_asm, re.S)
-    mla = [(n, body) for n, body in kernels if "decode_mla_kernel" in n]
-    assert len(mla) == 4
-    for name, body in mla:
+def test_no_scratch_and_all_agprs_reserved(kasm):
+    kname, text = kasm
+    kernels = re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S)
+    mine = [(n, body) for n, body in kernels if kname in n]
+    assert len(mine) >= 4
+    for name, body in mine:
         f = dict(re.findall(r"\.amdhsa_(\w+) (\d+)", body))
         assert int(f["private_segment_fixed_size"]) == 0, f"{name} spills"
         assert int(f["next_free_vgpr"]) - int(f["accum_offset"]) >= 256, f"{name} reserves too few AGPRs"
