@@ -18,6 +18,8 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
     loaded bytes and MFMA utilisation (the workload sits near the ridge);
   * the long causal prefill (B=2, Hq=32, Hkv=8, L=32768, d=128) over the
     target sparsities 30/50/70/80% and dense;
+  * the calibration law lambda = a/L: a fitted on calibration inputs at
+    L = 4K..32K, then the sparsity lambda = a/L achieves on fresh inputs;
   * the fp64 CPU oracle on a bounded sample of the prefill workload.
 Inputs are seeded synthetic segment-center tensors generated on the device.
 Prints ONE JSON line.  ``--only NAME`` runs one measurement (for profilers).
@@ -46,11 +48,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps, warmup):
-    """ms per call: ``warmup`` untimed calls, then ``steps`` calls enqueued back to back
-    between two events on the launch stream, bracketed by device synchronisation."""
-    for _ in range(warmup):
+def time_calls(fn, steps, warmup, min_warm_ms=100.0):
+    """ms per call: at least ``warmup`` untimed calls and at least ``min_warm_ms`` of
+    untimed work (the clocks settle), then ``steps`` calls enqueued back to back between
+    two events on the launch stream, bracketed by device synchronisation."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < min_warm_ms:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -286,13 +294,55 @@ def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8)):
     return rows
 
 
+def bench_calibration(lengths=(4096, 8192, 16384, 32768), targets=(0.5, 0.7)):
+    """The calibration law lambda = a(target) / L on the GQA prefill generator.
+
+    For each L, lambda_L is the exact quantile of the gap map of a calibration
+    input (seed 2000 + L/1024); a is fitted as ln a = mean(ln(lambda_L * L)).
+    Fresh evaluation inputs (seed 1000 + L/1024) are then run with
+    lambda = a / L from the fitted table, and the achieved block sparsity is
+    compared with the target."""
+    B, Hq, Hkv, d = 1, 32, 8, 128
+    lam_at = {t: [] for t in targets}
+    for L in lengths:
+        q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda",
+                                        seed=2000 + L // 1024)
+        cal = calibrate_prefill(q, k, v, list(targets))
+        for t in targets:
+            lam_at[t].append(cal[t][0])
+        del q, k, v
+    a_fit = [bl.blasst_calibrate_fit(lam_at[t], lengths) for t in targets]
+    rows = []
+    for L in lengths:
+        q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda",
+                                        seed=1000 + L // 1024)
+        for t in targets:
+            lam = bl.blasst_calibrate(list(targets), a_fit, t, L)
+            cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
+            bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, counters=cnt)
+            torch.cuda.synchronize()
+            vis, skp = (int(x) for x in cnt.cpu())
+            rows.append({"L": L, "target": t, "lambda_L_calibrated": lam_at[t][list(lengths).index(L)],
+                         "lambda_from_fit": lam, "achieved": skp / vis, "deviation": skp / vis - t})
+            log(f"calibration L={L} target {t}: lambda(a/L)={lam:.4g} achieved {skp / vis:.4f}")
+        del q, k, v
+    torch.cuda.empty_cache()
+    return {"workload": "GQA causal prefill B=1 Hq=32 Hkv=8 d=128, tile 128, block 64; calibration seeds "
+                        "2000+L/1024, evaluation seeds 1000+L/1024",
+            "a_fit": dict(zip([str(t) for t in targets], a_fit)),
+            "mean_abs_deviation": {str(t): float(np.mean([abs(r["deviation"]) for r in rows if r["target"] == t]))
+                                   for t in targets},
+            "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and long-prefill sections")
+    ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "decode70", "decode_dense", "mla70",
                                        "mla_dense"],
                     help="run one measurement only and print its numbers (profiling runs)")
@@ -379,6 +429,10 @@ def main():
         }
         torch.cuda.empty_cache()
 
+    calibration = None
+    if not args.no_calibration:
+        calibration = bench_calibration()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_prefill(q, k, v, lam70)
@@ -399,6 +453,7 @@ def main():
         "decode": decode,
         "mla_decode": mla,
         "long_prefill": long_prefill,
+        "calibration": calibration,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill70"),
                      "algorithmic_flops": mfma_flops70},

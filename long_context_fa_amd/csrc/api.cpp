@@ -203,11 +203,13 @@ int choose_splits(const blasst_decode_params *p)
     if (p->num_splits > 0)
         return p->num_splits;
     const int64_t units = p->B * p->Hkv;
-    // GQA: aim for >= 1024 workgroups (4 per compute unit).  Latent decode
-    // holds one workgroup per compute unit (its K ring fills the LDS), so one
-    // wave of 256 workgroups; more splits only add partial-result traffic.
-    // Either way keep >= 16 blocks a split.
-    const int64_t want = decode_kind(p) == KIND_MLA ? 256 : 1024;
+    // GQA: two workgroups are resident per compute unit (512 on the chip);
+    // aim for >= 4096 workgroups, about eight rounds, so that the last,
+    // partly filled round is a small share of the step.  Latent decode holds
+    // one workgroup per compute unit (its K ring fills the LDS): one round of
+    // 256; more splits only add partial-result traffic.  Either way keep
+    // >= 16 blocks a split.
+    const int64_t want = decode_kind(p) == KIND_MLA ? 256 : 4096;
     int s = 1;
     while (units * s < want && nkb / (2 * s) >= 16)
         s *= 2;
