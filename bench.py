@@ -12,6 +12,8 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
   * the GQA decode workload (148 sequences, Hq=32, Hkv=8, 32768 cached tokens,
     d=128, bf16 cache, block 64) at the 70% and 50% lambdas and lambda = 0:
     microseconds per decode step and HBM GB/s on the bytes actually loaded;
+    then the same step over a paged cache (64-row pages of a shuffled pool;
+    likewise for the latent decode below);
   * the latent (MLA) decode workload (16 sequences, 128 query heads sharing one
     576-wide latent KV head, V = its first 512 columns, 65536 cached tokens)
     at the 70% lambda and lambda = 0: microseconds per step, GB/s on the
@@ -213,7 +215,7 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
     return (q, k, v, lam70), res, dense_flops
 
 
-def bench_decode(steps, warmup, names=("s70", "s50", "dense")):
+def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=()):
     (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
     S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -238,10 +240,25 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense")):
                       "gbps": loaded / (mean_ms * 1e-3) / 1e9}
         log(f"decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
             f"{dres[name]['gbps']:.0f} GB/s on loaded bytes")
+    if paged_names:
+        # The same step over a paged cache: 64-row pages in a shuffled pool
+        # (the layout of serving engines), same lambda and split count.
+        (kp, vp), table = inputs.paged_pool([kc, vc], lens, 64, seed=9)
+        for name in paged_names:
+            lam = lams[name.replace("paged_", "")]
+
+            def pg(cnt=None, lam=lam):
+                return bl.blasst_decode_paged(dq, kp, vp, table, lens, DL, lam=lam, num_splits=S, out=dout,
+                                              workspace=work, counters=cnt)
+
+            mean_ms, _, _ = time_calls(pg, steps, warmup)
+            vis, skp = counts(lambda c: pg(c))
+            dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis}
+            log(f"decode {name} (64-row pages): {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}")
     return S, dres
 
 
-def bench_mla(steps, warmup, names=("s70", "s50", "dense")):
+def bench_mla(steps, warmup, names=("s70", "s50", "dense"), paged_names=()):
     (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
     S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=1e-3, dv=dv)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -268,6 +285,20 @@ def bench_mla(steps, warmup, names=("s70", "s50", "dense")):
                      "gbps": loaded / sec / 1e9, "tflops": flops / sec / 1e12}
         log(f"mla decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
             f"{res[name]['gbps']:.0f} GB/s, {res[name]['tflops']:.0f} TFLOP/s")
+    if paged_names:
+        # The same step over a paged latent cache: 64-row pages in a shuffled pool.
+        (kp,), table = inputs.paged_pool([kc], lens, 64, seed=9)
+        for name in paged_names:
+            lam = lams[name.replace("paged_", "")]
+
+            def pg(cnt=None, lam=lam):
+                return bl.blasst_decode_paged(q, kp, kp, table, lens, L, lam=lam, num_splits=S, out=out, dv=dv,
+                                              workspace=work, counters=cnt)
+
+            mean_ms, _, _ = time_calls(pg, steps, warmup)
+            vis, skp = counts(lambda c: pg(c))
+            res[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis}
+            log(f"mla decode {name} (64-row pages): {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}")
     return S, res
 
 
@@ -344,7 +375,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and long-prefill sections")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "decode70", "decode_dense", "mla70",
-                                       "mla_dense"],
+                                       "mla_dense", "decode_paged70", "mla_paged70"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -364,6 +395,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only in ("decode_paged70", "mla_paged70"):
+        fn = bench_decode if args.only == "decode_paged70" else bench_mla
+        r = fn(steps, warmup, names=(), paged_names=("paged_s70",))
+        print(json.dumps({"only": args.only, "result": r}, default=str), flush=True)
+        return
     if args.only:
         which, name = args.only.split("70")[0].split("_dense")[0], ("dense" if "dense" in args.only else "s70")
         fn = {"prefill": bench_prefill, "decode": bench_decode, "mla": bench_mla}[which]
@@ -392,7 +428,7 @@ def main():
     # ------------------------------------------------------------- decode
     decode = mla = long_prefill = None
     if not args.no_decode:
-        S, dres = bench_decode(steps, warmup)
+        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"))
         decode = {
             "workload": "GQA decode B=148 Hq=32 Hkv=8 L=32768 d=128 bf16, block 64, one query token per sequence",
             "num_splits": S,
@@ -404,9 +440,14 @@ def main():
             "roofline": {"bound": "hbm", "achieved": dres["s70"]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dres["s70"]["gbps"] / PEAK_HBM_GBS, "traffic": measured_traffic("decode70"),
                          "algorithmic_bytes": dres["s70"]["bytes"]},
+            "paged": {"page_size": 64, "layout": "pool [pages, Hkv, 64, d] in shuffled order, int32 page table",
+                      "us_per_step70": dres["paged_s70"]["us"], "sparsity70": dres["paged_s70"]["sparsity"],
+                      "us_per_step_dense": dres["paged_dense"]["us"],
+                      "overhead70_vs_contiguous": dres["paged_s70"]["us"] / dres["s70"]["us"] - 1.0,
+                      "overhead_dense_vs_contiguous": dres["paged_dense"]["us"] / dres["dense"]["us"] - 1.0},
         }
         torch.cuda.empty_cache()
-        S, mres = bench_mla(steps, warmup)
+        S, mres = bench_mla(steps, warmup, paged_names=("paged_s70", "paged_dense"))
         m70 = mres["s70"]
         mla = {
             "workload": "latent (MLA) decode B=16 Hq=128 sharing one KV head, dqk=576 dv=512 (V = K[..., :512]), "
@@ -421,6 +462,11 @@ def main():
             "roofline": {"bound": "hbm", "achieved": m70["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": m70["gbps"] / PEAK_HBM_GBS, "traffic": measured_traffic("mla70"),
                          "algorithmic_bytes": m70["bytes"], "mfma_frac": m70["tflops"] / PEAK_BF16_TFLOPS},
+            "paged": {"page_size": 64, "layout": "pool [pages, 1, 64, 576] in shuffled order, int32 page table",
+                      "us_per_step70": mres["paged_s70"]["us"], "sparsity70": mres["paged_s70"]["sparsity"],
+                      "us_per_step_dense": mres["paged_dense"]["us"],
+                      "overhead70_vs_contiguous": mres["paged_s70"]["us"] / m70["us"] - 1.0,
+                      "overhead_dense_vs_contiguous": mres["paged_dense"]["us"] / mres["dense"]["us"] - 1.0},
         }
         torch.cuda.empty_cache()
         long_prefill = {

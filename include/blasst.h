@@ -152,6 +152,56 @@ blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_
 blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes,
                             void *hip_stream);
 
+/* ------------------------------------------------------------ paged decode
+ * blasst_decode over a paged KV cache, the layout of serving engines: the
+ * cache rows of every sequence live in fixed-size pages of one shared pool,
+ * found through a per-sequence page table.  The pages name integration into
+ * serving stacks (TensorRT-LLM, FlashInfer: gist.science/pt/paper/2512.12087,
+ * section 3, contribution 4) and end-to-end runs with PagedAttention serving
+ * (BLASST reading notes, papers.lqhl.me/papers/BLASST-MLSys26, "局限与后续工作"
+ * future work 2).  The result equals blasst_decode on the contiguous cache
+ * obtained by gathering every sequence's pages in table order: the method,
+ * the split rule, the decisions and the outputs are the same; only the
+ * address of a cache row changes.
+ *
+ *   d            : the decode parameters, with d.k_cache / d.v_cache
+ *                  describing the page POOLS instead of per-sequence caches:
+ *                  k pool [num_pages, Hkv, page_size, dqk], strides
+ *                  (sb = page stride, sh = head stride, st = row stride);
+ *                  likewise the v pool (dv columns).  Any stride order works
+ *                  ([page, row, head, d] pools pass sh = d, st = Hkv * d).
+ *                  d.Lmax is the largest sequence length of the call (it
+ *                  sizes the skip and gap maps as in blasst_decode).
+ *   page_table   : device int32 [B, page_table_stride]; entry i of row b is
+ *                  the pool page holding rows [i * page_size, (i+1) *
+ *                  page_size) of sequence b.  Only entries
+ *                  i < ceil(seq_lens[b] / page_size) are read.  An id outside
+ *                  [0, num_pages) is clamped into that range (it reads a wrong
+ *                  page but never outside the pool).  K and V share the table.
+ *   page_table_stride : elements between table rows, >= ceil(Lmax/page_size).
+ *   num_pages    : pages in each pool (>= 1).
+ *   page_size    : rows per page, a power of two >= 16.
+ * Errors: as blasst_decode, plus INVALID_ARG for a null table, num_pages < 1,
+ * a page size that is not a power of two >= 16, or a table stride below
+ * ceil(Lmax/page_size); UNSUPPORTED for the latent form when one page spans
+ * 2^31 bytes or more.
+ */
+typedef struct {
+    blasst_decode_params d;
+    const int32_t *page_table;
+    int64_t page_table_stride;
+    int64_t num_pages;
+    int64_t page_size;
+} blasst_decode_paged_params;
+
+/* Host-only planner of blasst_decode_paged (same contract as
+ * blasst_decode_plan). */
+blasst_status blasst_decode_paged_plan(const blasst_decode_paged_params *p, int *num_splits_used,
+                                       size_t *workspace_bytes);
+
+blasst_status blasst_decode_paged(const blasst_decode_paged_params *p, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
 /* ---------------------------------------------------------------- calibrate
  * blasst_calibrate(target_sparsity, L) -> lambda = a(target) / L.  The table
  * holds a fitted per target sparsity (strictly increasing targets, a > 0); ln a

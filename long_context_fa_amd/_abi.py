@@ -53,6 +53,12 @@ class _DecodeParams(ctypes.Structure):
                 ("counters", ctypes.c_void_p)]
 
 
+class _DecodePagedParams(ctypes.Structure):
+    _fields_ = [("d", _DecodeParams), ("page_table", ctypes.c_void_p),
+                ("page_table_stride", ctypes.c_int64), ("num_pages", ctypes.c_int64),
+                ("page_size", ctypes.c_int64)]
+
+
 class _CalibTable(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int), ("target", ctypes.POINTER(ctypes.c_double)),
                 ("a", ctypes.POINTER(ctypes.c_double))]
@@ -84,6 +90,12 @@ def load_library():
     lib.blasst_decode.restype = st
     lib.blasst_decode.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]
+    lib.blasst_decode_paged_plan.restype = st
+    lib.blasst_decode_paged_plan.argtypes = [ctypes.POINTER(_DecodePagedParams), ctypes.POINTER(ctypes.c_int),
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.blasst_decode_paged.restype = st
+    lib.blasst_decode_paged.argtypes = [ctypes.POINTER(_DecodePagedParams), ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
     lib.blasst_calibrate.restype = st
     lib.blasst_calibrate.argtypes = [ctypes.POINTER(_CalibTable), ctypes.c_double, ctypes.c_int64,
                                      ctypes.POINTER(ctypes.c_double)]
@@ -208,6 +220,65 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
         workspace = torch.empty(max(ws.value, 1), dtype=torch.uint8, device=q.device)
     _check(lib.blasst_decode(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                              _stream(stream, q.device)), "blasst_decode")
+    return out
+
+
+def _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits, o,
+                  skip_map, gap_map, counters):
+    B, Hq, dqk = q.shape
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
+        raise ValueError("page_table must be an int32 [B, pages_per_seq] tensor with unit column stride")
+    d = _DecodeParams(_tensor(q, True), _tensor(k_pages), _tensor(v_pages), o,
+                      _ptr(seq_lens), B, Hq, k_pages.shape[1], int(Lmax), dqk, 0,
+                      float(scale) if scale is not None else 0.0, float(lam), int(block_k),
+                      int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters))
+    return _DecodePagedParams(d, page_table.data_ptr(), page_table.stride(0), k_pages.shape[0],
+                              k_pages.shape[2])
+
+
+def blasst_decode_paged_plan(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=0.0, scale=None,
+                             block_k=64, num_splits=0, dv=None, out_dtype=torch.float32):
+    """(num_splits the paged call will use, workspace bytes it needs)."""
+    B, Hq, _ = q.shape
+    dv = dv if dv is not None else v_pages.shape[3]
+    # the planner reads no device memory: describe O [B,Hq,dv] at q's (aligned) address
+    o = _Tensor(q.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _FP32, Hq * dv, dv, 0)
+    p = _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits, o,
+                      None, None, None)
+    p.d.dv = dv
+    ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+    _check(load_library().blasst_decode_paged_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)),
+           "blasst_decode_paged_plan")
+    return ns.value, ws.value
+
+
+def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=0.0, scale=None, block_k=64,
+                        num_splits=0, dv=None, out=None, out_dtype=torch.float32, workspace=None, skip_map=None,
+                        gap_map=None, counters=None, stream=None):
+    """Block-skipping decode over a paged cache.
+
+    q [B,Hq,dqk]; k_pages [num_pages,Hkv,page_size,dqk] and v_pages
+    [num_pages,Hkv,page_size,dv] (any strides with a contiguous last dim, e.g.
+    a [num_pages,page_size,Hkv,d] pool permuted to that order); page_table
+    int32 [B, pages_per_seq]; seq_lens int32 [B]; Lmax the largest length (it
+    sizes the skip/gap maps [B,Hkv,ceil(Lmax/64)]).  Latent form: pass
+    ``v_pages = k_pages`` and ``dv=512``.  Returns O [B,Hq,dv].
+    """
+    B, Hq, _ = q.shape
+    dv = dv if dv is not None else v_pages.shape[3]
+    if out is None:
+        out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
+    p = _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits,
+                      _tensor(out, True), skip_map, gap_map, counters)
+    p.d.dv = dv
+    lib = load_library()
+    if workspace is None:
+        ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+        _check(lib.blasst_decode_paged_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)),
+               "blasst_decode_paged_plan")
+        workspace = torch.empty(max(ws.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.blasst_decode_paged(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                   _stream(stream, q.device)), "blasst_decode_paged")
     return out
 
 

@@ -156,7 +156,8 @@ DecodeKind decode_kind(const blasst_decode_params *p)
     return KIND_NONE;
 }
 
-blasst_status validate_decode(const blasst_decode_params *p)
+// pg: the paging fields of blasst_decode_paged, nullptr for a contiguous cache.
+blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode_paged_params *pg = nullptr)
 {
     if (p == nullptr)
         return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
@@ -186,9 +187,23 @@ blasst_status validate_decode(const blasst_decode_params *p)
                     "decode supports dqk = dv in {64,128} with Hq/Hkv <= 16, or dqk=576, dv=512, Hkv=1, Hq=128");
     if (kind == KIND_MLA && p->v_cache.ptr != p->k_cache.ptr)
         return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs v_cache to alias k_cache");
-    // the latent kernel addresses a sequence's cache rows with 32-bit byte offsets
-    if (kind == KIND_MLA && p->Lmax * p->k_cache.st * 2 >= ((int64_t)1 << 31))
-        return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs Lmax * token stride * 2 < 2^31 bytes");
+    if (pg) {
+        if (pg->page_table == nullptr)
+            return fail(BLASST_ERR_INVALID_ARG, "page_table: null pointer");
+        if (pg->num_pages < 1 || pg->num_pages > INT32_MAX)
+            return fail(BLASST_ERR_INVALID_ARG, "num_pages must be in 1..2^31-1");
+        if (pg->page_size < 16 || pg->page_size > ((int64_t)1 << 30) || (pg->page_size & (pg->page_size - 1)))
+            return fail(BLASST_ERR_INVALID_ARG, "page_size must be a power of two >= 16 (got %lld)",
+                        (long long)pg->page_size);
+        if (pg->page_table_stride < (p->Lmax + pg->page_size - 1) / pg->page_size)
+            return fail(BLASST_ERR_INVALID_ARG, "page_table_stride must be >= ceil(Lmax / page_size)");
+    }
+    // the latent kernel addresses a sequence's (or a page's) cache rows with
+    // 32-bit byte offsets
+    const int64_t span = pg ? std::min(pg->page_size, p->Lmax) : p->Lmax;
+    if (kind == KIND_MLA && span * p->k_cache.st * 2 >= ((int64_t)1 << 31))
+        return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs rows * token stride * 2 < 2^31 bytes "
+                                            "(rows = Lmax, or the page size of a paged cache)");
     const int64_t nkb = (p->Lmax + 63) / 64;
     if (p->num_splits < 0 || p->num_splits > nkb)
         return fail(BLASST_ERR_INVALID_ARG, "num_splits must be in 0..ceil(Lmax/64)");
@@ -239,9 +254,14 @@ blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_
     return BLASST_OK;
 }
 
-blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes, void *hip_stream)
+} // extern "C"
+
+namespace {
+
+blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_paged_params *pg, void *workspace,
+                         size_t workspace_bytes, void *hip_stream)
 {
-    if (blasst_status s = validate_decode(p))
+    if (blasst_status s = validate_decode(p, pg))
         return s;
     const int S = choose_splits(p);
     const size_t need = workspace_for(p, S);
@@ -276,6 +296,15 @@ blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size
     a.skip_map = p->skip_map;
     a.gap_map = p->gap_map;
     a.counters = p->counters;
+    if (pg) {
+        a.page_table = pg->page_table;
+        a.pt_stride = pg->page_table_stride;
+        a.num_pages = (int)pg->num_pages;
+        int shift = 0;
+        while (((int64_t)1 << shift) < pg->page_size)
+            ++shift;
+        a.page_shift = shift;
+    }
     hipError_t e = blasst::launch_decode(a, (int)p->dqk, (int)p->dv, p->lambda > 0.0, p->o.dtype == BLASST_BF16,
                                          (hipStream_t)hip_stream);
     if (e == hipErrorInvalidValue)
@@ -283,6 +312,38 @@ blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size
     if (e != hipSuccess)
         return fail(BLASST_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
     return BLASST_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    return run_decode(p, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+blasst_status blasst_decode_paged_plan(const blasst_decode_paged_params *p, int *num_splits_used,
+                                       size_t *workspace_bytes)
+{
+    if (p == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
+    if (blasst_status s = validate_decode(&p->d, p))
+        return s;
+    const int S = choose_splits(&p->d);
+    if (num_splits_used)
+        *num_splits_used = S;
+    if (workspace_bytes)
+        *workspace_bytes = workspace_for(&p->d, S);
+    return BLASST_OK;
+}
+
+blasst_status blasst_decode_paged(const blasst_decode_paged_params *p, void *workspace, size_t workspace_bytes,
+                                  void *hip_stream)
+{
+    if (p == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
+    return run_decode(&p->d, p, workspace, workspace_bytes, hip_stream);
 }
 
 // ------------------------------------------------------------- calibration

@@ -35,7 +35,7 @@ namespace {
 constexpr int BC = 64;
 constexpr int NWD = 4; // waves per decode workgroup = blocks per batch
 
-template <int D, bool SKIP, bool OUT_BF16>
+template <int D, bool SKIP, bool OUT_BF16, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_kernel(const DecodeArgs a)
 {
@@ -44,6 +44,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     constexpr int TB = BC * RB;        // bytes per V tile
     constexpr int VI = TB / 1024;      // 1 KB copies per V tile (one wave copies a tile)
     constexpr int RPI = 64 / DG;       // rows per copy
+    static_assert(16 % RPI == 0, "a V copy must stay inside one 16-row group");
     constexpr int NS = D / 32;         // 32-wide k-steps of the QK product
     constexpr int NDT = D / 16;        // 16-row d tiles of O^T
     constexpr int KLOADS = 4 * NS;     // K register loads per wave per block
@@ -65,8 +66,37 @@ void decode_gqa_kernel(const DecodeArgs a)
     const int jb = s * per;
     const int je = (jb + per < nkb_b) ? jb + per : nkb_b;
 
-    const uint16_t *kp = a.k + b * a.k_sb + g * a.k_sh;
-    const uint16_t *vp = a.v + b * a.v_sb + g * a.v_sh;
+    // Cache rows.  Contiguous cache: row r of the sequence at kp + r * k_st.
+    // Paged cache: pool page page_table[b][r >> page_shift], row r & pmask of
+    // that page.  A page holds a power of two >= 16 rows, so the 16 rows of an
+    // aligned group share one page; a row past the sequence is read as row
+    // len-1, which lies in the page of the group's first row clamped to len-1.
+    // The 4 group ids of a block come from one vector load (lane kt < 4 reads
+    // group kt's entry) issued a batch ahead, right behind the K loads of the
+    // batch before; they are moved to SGPRs before the next V copy is issued,
+    // so a table read never stalls a cache load.
+    const uint16_t *kp = a.k + (PAGED ? 0 : b * a.k_sb) + g * a.k_sh;
+    const uint16_t *vp = a.v + (PAGED ? 0 : b * a.v_sb) + g * a.v_sh;
+    const int pmask = PAGED ? (1 << a.page_shift) - 1 : -1;
+    auto ids_load = [&](int j) -> int {
+        if (!PAGED)
+            return 0;
+        int g0 = j * BC + 16 * (lane & 3);
+        g0 = (j < je && g0 < len) ? g0 : len - 1;
+        return a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
+    };
+    auto ids_take = [&](int v, int (&ids)[4]) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            int id = __builtin_amdgcn_readlane(v, kt);
+            id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
+            asm volatile("" : "+s"(id)); // in SGPRs here, before any later copy
+            ids[kt] = id;
+        }
+    };
+    auto page_off = [&](const int (&ids)[4], int grp16, int64_t sb) -> int64_t {
+        return PAGED ? (int64_t)ids[grp16] * sb : 0;
+    };
     char *const vt = vsm + w * TB; // this wave's V slice
 
     // q^T as the B operand: lane (n, grp) holds q[head n][32 st + 8 grp .. +7].
@@ -87,29 +117,31 @@ void decode_gqa_kernel(const DecodeArgs a)
     // K[key][32 st + 8 grp .. +7].  Every lane always issues all KLOADS loads:
     // keys outside the split read row len-1 (finite; their scores are masked
     // to -inf below), because the V wait counts on exactly KLOADS younger
-    // vector-memory operations.
+    // vector-memory operations (plus the id load of a paged cache).
     u32x4 kr[4][NS];
-    auto load_k = [&](int j) {
+    auto load_k = [&](int j, const int (&ids)[4]) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int key = j * BC + 16 * kt + n;
             const int kc = (j < je && key < len) ? key : len - 1;
+            const uint16_t *rp = kp + page_off(ids, kt, a.k_sb) + (int64_t)(kc & pmask) * a.k_st;
 #pragma unroll
             for (int st = 0; st < NS; ++st)
-                kr[kt][st] = __builtin_nontemporal_load((const u32x4 *)(kp + (int64_t)kc * a.k_st + 32 * st + 8 * grp));
+                kr[kt][st] = __builtin_nontemporal_load((const u32x4 *)(rp + 32 * st + 8 * grp));
         }
     };
     // V tile of block j -> this wave's slice, row-major with the 16-byte
     // chunks XOR-swizzled by row (rows past len re-read row len-1: finite
     // values whose probabilities are exactly 0).
-    auto copy_v = [&](int j) {
+    auto copy_v = [&](int j, const int (&ids)[4]) {
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int row = i * RPI + lane / DG;
             const int c = (lane % DG) ^ swz<DG>(row);
             int key = j * BC + row;
             key = key < len ? key : len - 1;
-            copy16_to_lds(vp + (int64_t)key * a.v_st + c * 8, vt + i * 1024);
+            copy16_to_lds(vp + page_off(ids, (i * RPI) >> 4, a.v_sb) + (int64_t)(key & pmask) * a.v_st + c * 8,
+                          vt + i * 1024);
         }
     };
 
@@ -125,8 +157,14 @@ void decode_gqa_kernel(const DecodeArgs a)
     // Transpose-read addressing of the V^T operand (16x16x32 A layout).
     const int vj = (lane & 15) >> 2, vq = lane & 3, vgrp = lane >> 4;
 
-    if (jb < je)
-        load_k(jb + w);
+    // Page ids (paged cache): pc for this batch's block (its V copy), pn for
+    // the next batch's (its K loads); idv is the vector load in flight.
+    int pc[4] = {0, 0, 0, 0}, pn[4] = {0, 0, 0, 0}, idv = 0;
+    if (jb < je) {
+        ids_take(ids_load(jb + w), pc);
+        load_k(jb + w, pc);
+        idv = ids_load(jb + NWD + w);
+    }
     int it = 0;
     for (int j0 = jb; j0 < je; j0 += NWD, ++it) {
         const int j = j0 + w; // this wave's block
@@ -139,6 +177,8 @@ void decode_gqa_kernel(const DecodeArgs a)
             for (int st = 0; st < NS; ++st)
                 sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
         }
+        if (PAGED)
+            ids_take(idv, pn); // issued behind the K loads just consumed
         // Mask keys past the sequence (and the whole block if j >= je).
         const int k0 = j * BC;
         if (j >= je || k0 + BC > len) {
@@ -196,10 +236,17 @@ void decode_gqa_kernel(const DecodeArgs a)
 
         const bool exec = j < je && !my_skip;
         if (exec)
-            copy_v(j); // V only for an executed block
+            copy_v(j, pc); // V only for an executed block
         const bool more = j0 + NWD < je;
-        if (more)
-            load_k(j0 + NWD + w); // next batch's K in flight
+        if (more) {
+            load_k(j0 + NWD + w, pn); // next batch's K in flight
+            if (PAGED) {
+                idv = ids_load(j0 + 2 * NWD + w);
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    pc[kt] = pn[kt];
+            }
+        }
 
         if (exec) {
             // Online-softmax update with this wave's running max.
@@ -226,9 +273,10 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 o[dt] *= alpha;
-            // The V copy is older than the next K loads: wait for it only.
+            // The V copy is older than the next K loads (and, paged, the id
+            // load behind them): wait for it only.
             if (more)
-                wait_vmcnt<KLOADS>();
+                wait_vmcnt<KLOADS + (PAGED ? 1 : 0)>();
             else
                 wait_vmcnt<0>();
             compiler_fence();
@@ -377,8 +425,11 @@ namespace {
 template <int D, bool SKIP, bool OUT_BF16>
 hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16>), dim3(a.num_splits, a.Hkv, a.B), dim3(256), 0,
-                       stream, a);
+    const dim3 grid(a.num_splits, a.Hkv, a.B);
+    if (a.page_table)
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, false>), grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1)
         return e;

@@ -37,6 +37,13 @@ struct DecodeArgs {
     uint8_t *skip_map;
     float *gap_map;
     unsigned long long *counters;
+    // Paged cache (page_table != nullptr): k/v point at page pools whose
+    // batch stride is the page stride; row r of sequence b lives in pool page
+    // page_table[b * pt_stride + (r >> page_shift)] (ids clamped into
+    // [0, num_pages)), at row r & (2^page_shift - 1) of that page.
+    const int32_t *page_table;
+    int64_t pt_stride;
+    int num_pages, page_shift;
 };
 
 // GQA/MQA/MHA decode (dqk = dv in {64, 128}, G <= 16) and latent (MLA) decode

@@ -58,7 +58,7 @@ constexpr int NDT = DV / 32;         // O^T d tiles (16)
 __host__ __device__ constexpr int swzl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __host__ __device__ constexpr int swzr(int r) { return (r >> 1) & 7; }
 
-template <bool SKIP, bool OUT_BF16>
+template <bool SKIP, bool OUT_BF16, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mla_kernel(const DecodeArgs a)
 {
@@ -81,7 +81,23 @@ void decode_mla_kernel(const DecodeArgs a)
     const int jb = s * per;
     const int je = (jb + per < nkb_b) ? jb + per : nkb_b;
 
-    const uint16_t *kp = a.k + b * a.k_sb;
+    // Rows of wave w's copies: the aligned 16-row group 16w.. of a block.  A
+    // contiguous cache holds row r at kp + r * k_st; a paged cache holds it in
+    // pool page page_table[b][r >> page_shift] at row r & pmask, and a page
+    // of >= 16 rows holds the whole group (rows past len read row len-1, in
+    // the page of the group's first row clamped to len-1): one wave-uniform
+    // page lookup per block.
+    const uint16_t *kp = a.k + (PAGED ? 0 : b * a.k_sb);
+    const int pmask = PAGED ? (1 << a.page_shift) - 1 : -1;
+    auto group_base = [&](int j) -> const uint16_t * {
+        if (!PAGED)
+            return kp;
+        int g0 = j * BC + 16 * w;
+        g0 = g0 < len ? g0 : len - 1;
+        int id = a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
+        id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
+        return kp + (int64_t)id * a.k_sb;
+    };
 
     // Q^T as the B operand: lane (n, hh) holds q[head][16kk + 8hh .. +7].
     bf16x8 qf[NKK];
@@ -97,16 +113,17 @@ void decode_mla_kernel(const DecodeArgs a)
     // chunk l ^ swzl(i) into physical chunk l), copies 16 and 17 are the rope
     // parts of 8 rows each (lane l: row +l/8, physical chunk l%8, logical
     // chunk (l%8) ^ swzr(row)).  Rows past len re-read row len-1 (finite
-    // data, masked later).  Offsets are 32-bit from the sequence base (the
-    // host checks Lmax * row stride).
+    // data, masked later).  Offsets are 32-bit from the sequence (or page)
+    // base gb = group_base(j) (the host checks rows * row stride).
     auto tile = [&](int j) { return smem + (j & 1) * TB; };
     const uint32_t rowb = (uint32_t)a.k_st * 2;
-    auto copy_one = [&](int j, int i) {
+    auto copy_one = [&](const uint16_t *gb, int j, int i) {
         char *t = tile(j);
         if (i < 16) {
             int key = j * BC + 16 * w + i;
             key = key < len ? key : len - 1;
-            copy16_to_lds_s(kp + (int64_t)key * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))), t + (16 * w + i) * LRB);
+            copy16_to_lds_s(gb + (int64_t)(key & pmask) * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))),
+                            t + (16 * w + i) * LRB);
         } else {
             const int e = i - 16;
             int lr = lane >> 3;
@@ -114,7 +131,7 @@ void decode_mla_kernel(const DecodeArgs a)
             int key = j * BC + 16 * w + 8 * e + lr;
             key = key < len ? key : len - 1;
             const uint32_t off = LRB + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7)); // swzr of the row
-            copy16_to_lds_s(kp, (uint32_t)key * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
+            copy16_to_lds_s(gb, (uint32_t)(key & pmask) * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
         }
     };
 
@@ -143,9 +160,10 @@ void decode_mla_kernel(const DecodeArgs a)
     int n_skipped = 0;
 
     if (jb < je) {
+        const uint16_t *gb = group_base(jb);
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            copy_one(jb, i);
+            copy_one(gb, jb, i);
         wait_vmcnt<0>();
         lds_barrier();
     }
@@ -157,6 +175,7 @@ void decode_mla_kernel(const DecodeArgs a)
         // (a DMA instruction holds the wave until the address unit accepts
         // it, so a burst would stall the MFMA stream).
         const bool dma = j + 1 < je;
+        const uint16_t *gbn = group_base(j + 1);
         f32x16 sc[2];
         // rope offsets are recomputed here (4 per block) to spare registers
         int nl = n;
@@ -180,7 +199,7 @@ void decode_mla_kernel(const DecodeArgs a)
             }
             __builtin_amdgcn_sched_barrier(0);
             if ((kk & 1) == 0 && dma)
-                copy_one(j + 1, kk >> 1);
+                copy_one(gbn, j + 1, kk >> 1);
             if (kk == 0) {
                 mfma_v_first2(sc[0], sc[1], ka[0][0], ka[0][1], qf[0]);
             } else {
@@ -361,6 +380,19 @@ void decode_mla_kernel(const DecodeArgs a)
 
 hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_t stream);
 
+namespace {
+
+template <bool SKIP, bool OUT_BF16>
+void launch_mla_variant(const DecodeArgs &a, dim3 grid, hipStream_t stream)
+{
+    if (a.page_table)
+        hipLaunchKernelGGL((decode_mla_kernel<SKIP, OUT_BF16, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_mla_kernel<SKIP, OUT_BF16, false>), grid, dim3(256), 0, stream, a);
+}
+
+} // namespace
+
 hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream)
 {
     if (a.G != 128 || a.Hkv != 1)
@@ -368,14 +400,14 @@ hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t
     const dim3 grid(a.num_splits, 1, a.B);
     if (skip) {
         if (out_bf16)
-            hipLaunchKernelGGL((decode_mla_kernel<true, true>), grid, dim3(256), 0, stream, a);
+            launch_mla_variant<true, true>(a, grid, stream);
         else
-            hipLaunchKernelGGL((decode_mla_kernel<true, false>), grid, dim3(256), 0, stream, a);
+            launch_mla_variant<true, false>(a, grid, stream);
     } else {
         if (out_bf16)
-            hipLaunchKernelGGL((decode_mla_kernel<false, true>), grid, dim3(256), 0, stream, a);
+            launch_mla_variant<false, true>(a, grid, stream);
         else
-            hipLaunchKernelGGL((decode_mla_kernel<false, false>), grid, dim3(256), 0, stream, a);
+            launch_mla_variant<false, false>(a, grid, stream);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1)

@@ -132,3 +132,51 @@ def random_inputs(shape_q, shape_k, shape_v, *, dtype=torch.float64, device="cpu
     k = (torch.randn(*shape_k, generator=g, device=device) * std).to(dtype)
     v = torch.randn(*shape_v, generator=g, device=device).to(dtype)
     return q, k, v
+
+
+def paged_pool(caches, seq_lens, page_size, *, seed=0, spare_pages=0, fill=float("nan"),
+               row_major_heads=False):
+    """Scatter contiguous caches [B, H, Lmax, d] into a shuffled page pool.
+
+    The pages of all sequences take a seeded random order among
+    ``num_pages = used + spare_pages`` pool pages; every pool row that holds
+    no token of a sequence (rows past seq_len in a sequence's last page, spare
+    pages) is ``fill`` (NaN by default, so a read of such a row shows up in
+    the result).  All caches share one page table (a KV cache's K and V).
+
+    Returns (pools, page_table): each pool is an [num_pages, H, page_size, d]
+    tensor (with ``row_major_heads`` a permuted view of [num_pages,
+    page_size, H, d] storage), and page_table is int32 [B, ceil(Lmax /
+    page_size)] on the caches' device, -1 past each sequence's pages.
+    """
+    B, H, Lmax, _ = caches[0].shape
+    dev = caches[0].device
+    lens = [int(x) for x in (seq_lens.tolist() if torch.is_tensor(seq_lens) else seq_lens)]
+    npg = [-(-ln // page_size) for ln in lens]
+    used = sum(npg)
+    total = used + spare_pages
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    perm = torch.randperm(total, generator=g)[:used]
+    table = torch.full((B, -(-Lmax // page_size)), -1, dtype=torch.int32)
+    pools = []
+    for c in caches:
+        d = c.shape[3]
+        if row_major_heads:
+            pool = torch.full((total, page_size, H, d), fill, dtype=c.dtype, device=dev).permute(0, 2, 1, 3)
+        else:
+            pool = torch.full((total, H, page_size, d), fill, dtype=c.dtype, device=dev)
+        pools.append(pool)
+    off = 0
+    for b in range(B):
+        ids = perm[off:off + npg[b]]
+        off += npg[b]
+        table[b, :npg[b]] = ids.to(torch.int32)
+        if npg[b] == 0:
+            continue
+        idx = ids.to(dev)
+        for c, pool in zip(caches, pools):
+            rows = torch.full((H, npg[b] * page_size, c.shape[3]), fill, dtype=c.dtype, device=dev)
+            rows[:, :lens[b]] = c[b, :, :lens[b]]
+            pool[idx] = rows.view(H, npg[b], page_size, c.shape[3]).permute(1, 0, 2, 3)
+    return pools, table.to(dev)

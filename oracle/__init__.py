@@ -141,6 +141,31 @@ def decode(q, k, v, seq_lens, scale=None, lam=0.0, block_k=64, num_splits=1,
     return {"o": o, "skip": skip, "gap": gap, "visited": int(cnt[0]), "skipped": int(cnt[1])}
 
 
+def gather_pages(pool, page_table, seq_lens, Lmax):
+    """Contiguous per-sequence cache [B, H, Lmax, d] (float64) from a paged pool.
+
+    The paged layout of serving engines (PagedAttention, which the BLASST
+    reading notes name for end-to-end serving runs, "局限与后续工作"): row r of
+    sequence b is row r mod P of pool page page_table[b, r div P], for
+    pool [num_pages, H, P, d].  Rows at or past seq_lens[b] are left 0 (the
+    decode never reads them).  Decode over a paged cache is defined as decode
+    over this gathered cache.
+    """
+    pool = np.asarray(pool, dtype=np.float64)
+    table = np.asarray(page_table)
+    num_pages, H, P, d = pool.shape
+    B = table.shape[0]
+    out = np.zeros((B, H, int(Lmax), d), np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        r = np.arange(n)
+        pages = table[b, r // P]
+        if n and (pages.min() < 0 or pages.max() >= num_pages):
+            raise ValueError(f"page table row {b} names a page outside the pool")
+        out[b, :, :n, :] = pool[pages, :, r % P, :].transpose(1, 0, 2)
+    return out
+
+
 def lambda_for_target(gaps, target):
     """lambda whose skip set is the ceil(target*N) smallest gaps; returns (lambda, reached)."""
     lib = _load()

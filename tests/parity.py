@@ -89,6 +89,20 @@ def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dt
     return o, skip, gap, cnt.cpu().numpy()
 
 
+def gpu_decode_paged(q, k_pages, v_pages, table, lens, Lmax, *, lam, num_splits=0, dv=None,
+                     out_dtype=torch.float32):
+    """blasst_decode_paged with fresh skip/gap maps and counters (as gpu_decode)."""
+    B, Hkv = q.shape[0], k_pages.shape[1]
+    nkb = -(-Lmax // 64)
+    skip = torch.full((B, Hkv, nkb), 7, dtype=torch.uint8, device=q.device)
+    gap = torch.full((B, Hkv, nkb), float("nan"), dtype=torch.float32, device=q.device)
+    cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
+    o = bl.blasst_decode_paged(q, k_pages, v_pages, table, lens, Lmax, lam=lam, num_splits=num_splits, dv=dv,
+                               skip_map=skip, gap_map=gap, counters=cnt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, skip, gap, cnt.cpu().numpy()
+
+
 def lambda_for(gap_map_gpu, target):
     """Calibrate lambda on a GPU gap map with the library's host search."""
     g = gap_map_gpu.cpu().numpy().ravel()

@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every declared
 symbol, rejects invalid arguments with the documented codes before any launch,
 and its host-only calibration calls agree with the oracle."""
+import ctypes
 import math
 import os
 import re
@@ -19,7 +20,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_library_exports_every_declared_symbol():
     header = open(os.path.join(ROOT, "include", "blasst.h")).read()
     declared = set(re.findall(r"\b(blasst_[a-z_]+)\s*\(", header))
-    assert {"blasst_prefill", "blasst_decode", "blasst_decode_plan", "blasst_calibrate",
+    assert {"blasst_prefill", "blasst_decode", "blasst_decode_plan", "blasst_decode_paged",
+            "blasst_decode_paged_plan", "blasst_calibrate",
             "blasst_calibrate_search", "blasst_calibrate_fit", "blasst_status_str",
             "blasst_last_error", "blasst_abi_version"} <= declared
     lib = bl.load_library()
@@ -107,6 +109,67 @@ def test_decode_plan_host_only():
     S2, _ = bl.blasst_decode_plan(q1, kc1, kc1, torch.full((1,), 32768, dtype=torch.int32), lam=0.01,
                                   num_splits=7)
     assert S2 == 7
+
+
+# ------------------------------------------------------------- paged decode
+def _paged_err(page_size=64, pages=8, table_cols=4, Lmax=256, **kw):
+    q = _bf16(2, 8, 128)
+    pool = _bf16(max(pages, 0), 2, page_size, 128)
+    table = torch.zeros(2, table_cols, dtype=torch.int32)
+    lens = torch.full((2,), Lmax, dtype=torch.int32)
+    args = dict(lam=0.01, stream=0, workspace=torch.zeros(16, dtype=torch.uint8))
+    args.update(kw)
+    with pytest.raises(bl.BlasstError) as ei:
+        bl.blasst_decode_paged(q, pool, pool, table, lens, Lmax, **args)
+    return ei.value.status
+
+
+def test_decode_paged_rejects():
+    assert _paged_err(page_size=24) == 1            # not a power of two
+    assert _paged_err(page_size=8, table_cols=32) == 1  # below 16 rows
+    assert _paged_err(table_cols=3) == 1            # table narrower than ceil(Lmax / page_size)
+    assert _paged_err(pages=0) == 1                 # empty pool
+    assert _paged_err(lam=1.0) == 1                 # the decode checks still apply
+    assert _paged_err(num_splits=4, workspace=torch.zeros(16, dtype=torch.uint8)) == 3
+    # a null table through the C ABI itself
+    q, pool = _bf16(2, 8, 128), _bf16(8, 2, 64, 128)
+    o = _abi._Tensor(q.data_ptr(), 1, 8 * 128, 128, 0)
+    d = _abi._DecodeParams(_abi._tensor(q, True), _abi._tensor(pool), _abi._tensor(pool), o,
+                           torch.zeros(2, dtype=torch.int32).data_ptr(), 2, 8, 2, 256, 128, 128,
+                           0.0, 0.01, 64, 0, None, None, None)
+    p = _abi._DecodePagedParams(d, None, 4, 8, 64)
+    assert bl.load_library().blasst_decode_paged_plan(ctypes.byref(p), None, None) == 1
+    assert "page_table" in bl.blasst_last_error()
+
+
+def test_decode_paged_plan_equals_contiguous_plan():
+    """Paging changes addresses only: the split plan and the workspace are
+    those of the contiguous call of the same lengths."""
+    q = _bf16(16, 32, 128)
+    lens = torch.full((16,), 32768, dtype=torch.int32)
+    kc = _bf16(1, 8, 32768, 128).expand(16, 8, 32768, 128)
+    pool = _bf16(1, 8, 64, 128).expand(8192, 8, 64, 128)
+    table = torch.zeros(16, 512, dtype=torch.int32)
+    for lam, ns in [(0.01, 0), (0.0, 5)]:
+        assert bl.blasst_decode_paged_plan(q, pool, pool, table, lens, 32768, lam=lam, num_splits=ns) == \
+            bl.blasst_decode_plan(q, kc, kc, lens, lam=lam, num_splits=ns)
+
+
+def test_paged_pool_builder_round_trips_through_the_oracle_gather():
+    from long_context_fa_amd import inputs
+    g = torch.Generator().manual_seed(3)
+    kc = torch.randn(3, 2, 200, 16, generator=g).to(torch.bfloat16)
+    vc = torch.randn(3, 2, 200, 8, generator=g).to(torch.bfloat16)
+    lens = [200, 1, 77]
+    for P, rm in [(16, False), (64, True), (256, False)]:
+        (kp, vp), table = inputs.paged_pool([kc, vc], lens, P, seed=5, spare_pages=2, row_major_heads=rm)
+        assert kp.shape[1:] == (2, P, 16) and table.shape == (3, -(-200 // P))
+        for c, pool in [(kc, kp), (vc, vp)]:
+            got = oracle.gather_pages(pool.float().numpy(), table.numpy(), lens, 200)
+            for b, n in enumerate(lens):
+                np.testing.assert_array_equal(got[b, :, :n], c[b, :, :n].float().numpy())
+        used = table[table >= 0]
+        assert used.unique().numel() == used.numel()  # no page is shared
 
 
 # ------------------------------------------------------ calibration (host C)

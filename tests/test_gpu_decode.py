@@ -6,11 +6,27 @@ import torch
 import long_context_fa_amd as bl
 import oracle
 from long_context_fa_amd import inputs
-from parity import (check_decisions, check_output, f64, gpu_decode, lambda_for, say,
+from parity import (check_decisions, check_output, f64, gpu_decode, gpu_decode_paged, lambda_for, say,
                     SPARSITY_ABS)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+
+
+def _compare(q, kk, vv, lens, got, *, lam, S, what):
+    """Whole-call parity: GPU results ``got`` = (o, skip, gap, counters)
+    against the oracle over the float64 caches kk, vv [B, Hkv, Lmax, *]."""
+    o, skip, gap, cnt = got
+    ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S)
+    nb = check_decisions(skip.cpu().numpy(), gap.cpu().numpy(), ref["skip"], ref["gap"], lam)
+    check_output(o.cpu().numpy(), ref["o"], what)
+    gs = skip.cpu().numpy()
+    g_frac = (gs == 1).sum() / max(1, (gs != 255).sum())
+    r_frac = ref["skipped"] / max(1, ref["visited"])
+    say(f"  splits {S}; sparsity gpu {g_frac:.4f} oracle {r_frac:.4f}; band {nb}")
+    assert abs(g_frac - r_frac) <= SPARSITY_ABS
+    assert cnt[0] == ref["visited"] and abs(cnt[1] - ref["skipped"]) <= nb
+    return cnt, S
 
 
 def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=False):
@@ -22,29 +38,27 @@ def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=Fal
     if unit_mask is None:
         kk = f64(kc)
         vv = kk[..., :dv] if mla else f64(vc)
-        ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S_used)
-        sel_u = np.ones((B, Hkv), bool)
-    else:
-        # copy only the sampled sequences to the host
-        bs = sorted({b for b, _ in unit_mask})
-        sub = {b: i for i, b in enumerate(bs)}
-        kk = f64(kc[bs])
-        vv = kk[..., :dv] if mla else f64(vc[bs])
-        m = np.zeros((len(bs), Hkv), np.uint8)
-        for b, g in unit_mask:
-            m[sub[b], g] = 1
-        ref_sub = oracle.decode(f64(q[bs]), kk, vv, lens[bs].cpu().numpy(), lam=lam, block_k=64,
-                                num_splits=S_used, unit_mask=m)
-        sel_u = np.zeros((B, Hkv), bool)
-        ref = {"skip": np.full(skip.shape, 255, np.uint8), "gap": np.full(gap.shape, -np.inf),
-               "o": np.zeros(o.shape), "visited": ref_sub["visited"], "skipped": ref_sub["skipped"]}
-        for b, g in unit_mask:
-            sel_u[b, g] = True
-            ref["skip"][b, g] = ref_sub["skip"][sub[b], g]
-            ref["gap"][b, g] = ref_sub["gap"][sub[b], g]
-        G = Hq // Hkv
-        for b in bs:
-            ref["o"][b] = ref_sub["o"][sub[b]]
+        return _compare(q, kk, vv, lens, (o, skip, gap, cnt), lam=lam, S=S_used, what=what)
+    # copy only the sampled sequences to the host
+    bs = sorted({b for b, _ in unit_mask})
+    sub = {b: i for i, b in enumerate(bs)}
+    kk = f64(kc[bs])
+    vv = kk[..., :dv] if mla else f64(vc[bs])
+    m = np.zeros((len(bs), Hkv), np.uint8)
+    for b, g in unit_mask:
+        m[sub[b], g] = 1
+    ref_sub = oracle.decode(f64(q[bs]), kk, vv, lens[bs].cpu().numpy(), lam=lam, block_k=64,
+                            num_splits=S_used, unit_mask=m)
+    sel_u = np.zeros((B, Hkv), bool)
+    ref = {"skip": np.full(skip.shape, 255, np.uint8), "gap": np.full(gap.shape, -np.inf),
+           "o": np.zeros(o.shape), "visited": ref_sub["visited"], "skipped": ref_sub["skipped"]}
+    for b, g in unit_mask:
+        sel_u[b, g] = True
+        ref["skip"][b, g] = ref_sub["skip"][sub[b], g]
+        ref["gap"][b, g] = ref_sub["gap"][sub[b], g]
+    G = Hq // Hkv
+    for b in bs:
+        ref["o"][b] = ref_sub["o"][sub[b]]
     nb = check_decisions(skip.cpu().numpy()[sel_u], gap.cpu().numpy()[sel_u], ref["skip"][sel_u],
                          ref["gap"][sel_u], lam)
     G = Hq // Hkv
@@ -55,8 +69,6 @@ def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=Fal
     r_frac = ref["skipped"] / max(1, ref["visited"])
     say(f"  splits {S_used}; sparsity gpu {g_frac:.4f} oracle {r_frac:.4f}; band {nb}")
     assert abs(g_frac - r_frac) <= SPARSITY_ABS
-    if unit_mask is None:
-        assert cnt[0] == ref["visited"] and abs(cnt[1] - ref["skipped"]) <= nb
     return cnt, S_used
 
 
@@ -152,3 +164,71 @@ def test_parity_mla_decode_full_size_sampled():
     cnt, _ = _run(q, kc, kc, lens, lam=lam, splits=S, dv=512, mla=True, what="mla 16x128x65536x576",
                   unit_mask=[(3, 0), (15, 0)])
     assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
+
+
+# ---------------------------------------------------------------- paged cache
+# Pools are NaN wherever no token lives (rows past a sequence's end, spare
+# pages), so a stray read shows up in O.  Paging changes only the address of
+# a row: results must equal the contiguous call bit for bit, and the oracle
+# over the gathered pages.
+
+def _equal_calls(a, b):
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    assert (a[3] == b[3]).all()
+
+
+def _gathered(pool, table, lens, Lmax):
+    return oracle.gather_pages(f64(pool), table.cpu().numpy(), lens.cpu().numpy(), Lmax)
+
+
+@pytest.mark.parametrize("P,row_major", [(16, False), (64, True), (256, False)])
+@pytest.mark.parametrize("d,G,splits", [(128, 4, 3), (64, 8, 1), (128, 16, 16)])
+def test_paged_gqa_matches_contiguous_and_oracle(P, row_major, d, G, splits):
+    B, Hkv, Lmax = 3, 2, 1000
+    q, kc, vc, _ = inputs.decode_inputs(B, G * Hkv, Hkv, Lmax, d, device=DEV, seed=61 + d + G + P)
+    lens = torch.tensor([1000, 1, 333], dtype=torch.int32, device=DEV)
+    (kp, vp), table = inputs.paged_pool([kc, vc], lens, P, seed=P + d, spare_pages=3, row_major_heads=row_major)
+    say(f"[paged] d={d} G={G} page={P} row_major={row_major} pool{tuple(kp.shape)} splits={splits}")
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=splits)
+    lam, _ = lambda_for(gap0, 0.6)
+    got = gpu_decode_paged(q, kp, vp, table, lens, Lmax, lam=lam, num_splits=splits)
+    _equal_calls(got, gpu_decode(q, kc, vc, lens, lam=lam, num_splits=splits))
+    _compare(q, _gathered(kp, table, lens, Lmax), _gathered(vp, table, lens, Lmax), lens, got,
+             lam=lam, S=splits, what=f"paged d={d} G={G} P={P}")
+
+
+def test_paged_gqa_dense_and_bf16_output():
+    q, kc, vc, lens = inputs.decode_inputs(2, 8, 2, 4096, 128, device=DEV, seed=66)
+    (kp, vp), table = inputs.paged_pool([kc, vc], lens, 32, seed=1, spare_pages=5)
+    for lam, dt in [(0.0, torch.float32), (1e-3, torch.bfloat16)]:
+        got = gpu_decode_paged(q, kp, vp, table, lens, 4096, lam=lam, num_splits=4, out_dtype=dt)
+        _equal_calls(got, gpu_decode(q, kc, vc, lens, lam=lam, num_splits=4, out_dtype=dt))
+        assert torch.isfinite(got[0].float()).all()
+
+
+@pytest.mark.parametrize("P,splits", [(64, 2), (16, 5), (1024, 1)])
+def test_paged_mla_matches_contiguous_and_oracle(P, splits):
+    q, kc, lens = _mla(3, 2000, seed=71 + P, lens=[2000, 1, 777])
+    (kp,), table = inputs.paged_pool([kc], lens, P, seed=P, spare_pages=2)
+    say(f"[paged] mla page={P} pool{tuple(kp.shape)} splits={splits}")
+    _, _, gap0, _ = gpu_decode(q, kc, kc, lens, lam=0.0, num_splits=splits, dv=512)
+    lam, _ = lambda_for(gap0, 0.6)
+    got = gpu_decode_paged(q, kp, kp, table, lens, 2000, lam=lam, num_splits=splits, dv=512)
+    _equal_calls(got, gpu_decode(q, kc, kc, lens, lam=lam, num_splits=splits, dv=512))
+    kk = _gathered(kp, table, lens, 2000)
+    _compare(q, kk, kk[..., :512], lens, got, lam=lam, S=splits, what=f"paged mla P={P}")
+
+
+def test_paged_gqa_decode_148_sequences_equals_contiguous():
+    """The full 148-sequence, 32K, 32/8-head step over 64-row pages in a
+    shuffled pool equals the contiguous call (itself checked against the
+    oracle on sampled units) bit for bit, at the planner's split count."""
+    q, kc, vc, lens = inputs.decode_inputs(148, 32, 8, 32768, 128, n_random=8, device=DEV, seed=1002)
+    (kp, vp), table = inputs.paged_pool([kc, vc], lens, 64, seed=9)
+    S, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=0.01)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=S)
+    lam, _ = lambda_for(gap0, 0.7)
+    say(f"[paged] 148x32/8x32768x128 page=64 splits={S} lam={lam:.4g}")
+    got = gpu_decode_paged(q, kp, vp, table, lens, 32768, lam=lam)
+    _equal_calls(got, gpu_decode(q, kc, vc, lens, lam=lam, num_splits=S))

@@ -361,3 +361,44 @@ def test_lambda_from_table():
     assert abs(oracle.lambda_from_table(t, a, 0.5, 1000) - 8.0 / 1000) < 1e-15
     assert abs(oracle.lambda_from_table(t, a, 0.6, 1000) - 16.0 / 1000) < 1e-15  # geometric midpoint
     assert abs(oracle.lambda_from_table(t, a, 0.4, 2000) - 4.0 / 2000) < 1e-15
+
+
+# --------------------------------------------------------------- paged cache
+def test_gather_pages_inverts_a_page_scatter():
+    """Writing each sequence's rows page by page into a shuffled pool (an
+    explicit loop here, the inverse operation) and gathering them back
+    returns the original rows; rows past a sequence's length come back 0."""
+    rng = np.random.default_rng(7)
+    B, H, Lmax, d, P = 3, 2, 100, 5, 16
+    lens = [100, 1, 37]
+    cache = rng.standard_normal((B, H, Lmax, d))
+    need = [-(-n // P) for n in lens]
+    order = rng.permutation(sum(need) + 4)
+    pool = np.full((order.size, H, P, d), np.nan)
+    table = np.full((B, -(-Lmax // P)), -1, np.int64)
+    nxt = 0
+    for b in range(B):
+        for i in range(need[b]):
+            page = order[nxt]
+            nxt += 1
+            table[b, i] = page
+            for r in range(i * P, min((i + 1) * P, lens[b])):
+                pool[page, :, r - i * P, :] = cache[b, :, r, :]
+    got = oracle.gather_pages(pool, table, lens, Lmax)
+    for b in range(B):
+        np.testing.assert_array_equal(got[b, :, :lens[b]], cache[b, :, :lens[b]])
+        assert not got[b, :, lens[b]:].any()
+
+
+def test_gather_pages_single_page_per_sequence_is_the_pool():
+    """One page of Lmax rows per sequence with table b -> b: the pool is the cache."""
+    rng = np.random.default_rng(8)
+    pool = rng.standard_normal((3, 2, 64, 4))
+    got = oracle.gather_pages(pool, np.arange(3)[:, None], [64, 64, 64], 64)
+    np.testing.assert_array_equal(got, pool)
+
+
+def test_gather_pages_rejects_a_page_outside_the_pool():
+    pool = np.zeros((2, 1, 16, 4))
+    with pytest.raises(ValueError):
+        oracle.gather_pages(pool, np.array([[0, 2]]), [20], 32)
