@@ -28,11 +28,11 @@ _i64 = ctypes.c_int64
 def _declare(lib):
     lib.oracle_prefill.restype = ctypes.c_int
     lib.oracle_prefill.argtypes = [_i64] * 6 + [_dp] * 3 + [
-        ctypes.c_int, ctypes.c_double, ctypes.c_double, _i64, _i64, _u8p,
+        ctypes.c_int, _i64, ctypes.c_double, ctypes.c_double, _i64, _i64, _u8p,
         _dp, _u8p, _dp, _i64p, ctypes.c_int]
     lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_i64] * 6 + [_dp] * 3 + [
-        _i32p, ctypes.c_double, ctypes.c_double, _i64, _i64, _u8p,
+        _i32p, ctypes.c_double, ctypes.c_double, _i64, _i64, _i64, _u8p,
         _dp, _u8p, _dp, _i64p, ctypes.c_int]
     lib.oracle_lambda_for_target.restype = ctypes.c_double
     lib.oracle_lambda_for_target.argtypes = [_dp, _i64, ctypes.c_double, _dp]
@@ -82,8 +82,10 @@ def _ptr(a, t):
 
 
 def prefill(q, k, v, causal=True, scale=None, lam=0.0, tile_q=64, block_k=64,
-            unit_mask=None, nthreads=0, want_maps=True):
+            unit_mask=None, nthreads=0, want_maps=True, window=0):
     """Blockwise skip attention, prefill form (Lq = Lk = L).
+
+    ``window`` > 0 (causal only): query i sees keys i - window < c <= i.
 
     q [B,Hq,L,d], k [B,Hkv,L,d], v [B,Hkv,L,dv].  Returns a dict with
     ``o`` [B,Hq,L,dv], ``skip`` uint8 [B,Hq,nQT,nKB] (0 executed, 1 skipped,
@@ -103,7 +105,7 @@ def prefill(q, k, v, causal=True, scale=None, lam=0.0, tile_q=64, block_k=64,
     um = None if unit_mask is None else np.ascontiguousarray(unit_mask, dtype=np.uint8)
     cnt = np.zeros(2, np.int64)
     rc = lib.oracle_prefill(B, Hq, Hkv, L, d, dv, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp),
-                            int(bool(causal)), float(scale), float(lam), tile_q, block_k,
+                            int(bool(causal)), int(window), float(scale), float(lam), tile_q, block_k,
                             _ptr(um, _u8p), _ptr(o, _dp), _ptr(skip, _u8p), _ptr(gap, _dp),
                             _ptr(cnt, _i64p), int(nthreads))
     if rc != 0:
@@ -112,8 +114,11 @@ def prefill(q, k, v, causal=True, scale=None, lam=0.0, tile_q=64, block_k=64,
 
 
 def decode(q, k, v, seq_lens, scale=None, lam=0.0, block_k=64, num_splits=1,
-           unit_mask=None, nthreads=0, want_maps=True):
+           unit_mask=None, nthreads=0, want_maps=True, window=0):
     """Blockwise skip attention, decode form (one query token per sequence).
+
+    ``window`` > 0: the query (at position seq_len-1) sees the last ``window``
+    keys; the splits cut the blocks from the first one holding such a key.
 
     q [B,Hq,dqk], k [B,Hkv,Lmax,dqk], v [B,Hkv,Lmax,dv], seq_lens int [B].
     Returns ``o`` [B,Hq,dv], ``skip``/``gap`` [B,Hkv,nKB], ``visited``,
@@ -133,7 +138,7 @@ def decode(q, k, v, seq_lens, scale=None, lam=0.0, block_k=64, num_splits=1,
     um = None if unit_mask is None else np.ascontiguousarray(unit_mask, dtype=np.uint8)
     cnt = np.zeros(2, np.int64)
     rc = lib.oracle_decode(B, Hq, Hkv, Lmax, dqk, dv, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp),
-                           _ptr(sl, _i32p), float(scale), float(lam), block_k, int(num_splits),
+                           _ptr(sl, _i32p), float(scale), float(lam), block_k, int(num_splits), int(window),
                            _ptr(um, _u8p), _ptr(o, _dp), _ptr(skip, _u8p), _ptr(gap, _dp),
                            _ptr(cnt, _i64p), int(nthreads))
     if rc != 0:

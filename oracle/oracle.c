@@ -40,7 +40,15 @@
  *    split s of a sequence with nkb key blocks covers the contiguous run
  *    [s*ceil(nkb/S), min(nkb, (s+1)*ceil(nkb/S))) and starts from m = -inf;
  *    the per-split partials (acc, m, l) are merged by the log-sum-exp rule
- *    O = sum_s e^{m_s-M} acc_s / sum_s e^{m_s-M} l_s with M = max_s m_s.
+ *    O = sum_s e^{m_s-M} acc_s / sum_s e^{m_s-M} l_s with M = max_s m_s;
+ *  - sliding window W (the BLASST reading notes, "问题与动机", list sliding
+ *    window among the supported attention forms and give no further detail):
+ *    a query at position i sees keys c with i - W < c <= i; blocks with no
+ *    visible key are not visited, and the skip test runs unchanged on the
+ *    rest.  In decode the query is at position len-1, so it sees the last W
+ *    keys, and the splits cut the blocks from the first block that holds a
+ *    visible key: split s covers [j0 + s*ceil((nkb - j0)/S), ...), j0 =
+ *    max(0, len - W) div block_k.
  *
  * Arithmetic is IEEE fp64 with libm exp/log, loops in the order written.
  * Inputs are fp64 arrays (the tests pass the exact bf16 values the GPU reads).
@@ -66,7 +74,8 @@ static double oracle_ln_lambda(double lambda)
  * visiting key blocks j_begin .. j_end-1 (block size bc) in ascending order.
  *
  *   q      : row r at q + r*q_stride (d values)
- *   qpos   : causal limit of row r (key c visible iff c <= qpos[r]), or NULL
+ *   qpos   : position of row r (key c visible iff c <= qpos[r]), or NULL
+ *   window : > 0: key c also needs c > qpos[r] - window (sliding window)
  *   k, v   : [klen_alloc][d] and [klen_alloc][dv], contiguous
  *   klen   : keys with index >= klen are masked
  *   m,l,acc: outputs, the unit's final running max, sum and accumulator
@@ -75,7 +84,7 @@ static double oracle_ln_lambda(double lambda)
  *   S      : scratch [R][bc]
  */
 static void oracle_unit(int64_t R, int64_t d, int64_t dv,
-                        const double *q, int64_t q_stride, const int64_t *qpos,
+                        const double *q, int64_t q_stride, const int64_t *qpos, int64_t window,
                         const double *k, const double *v, int64_t klen,
                         int64_t j_begin, int64_t j_end, int64_t bc,
                         double scale, double lnlam,
@@ -99,7 +108,8 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
             mt[r] = -INFINITY;
             for (int64_t c = 0; c < bc; ++c) {
                 int64_t key = c0 + c;
-                int visible = key < klen && (qpos == NULL || key <= qpos[r]);
+                int visible = key < klen &&
+                              (qpos == NULL || (key <= qpos[r] && (window <= 0 || key > qpos[r] - window)));
                 if (!visible) {
                     S[r * bc + c] = -INFINITY;
                     continue;
@@ -174,6 +184,7 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
 /*
  * Prefill (causal or not), Lq = Lk = L, one query tile = tile_q consecutive
  * positions of one query head; query head h reads KV head h / (Hq/Hkv).
+ * window > 0 (causal only): query i sees keys i - window < c <= i.
  *
  *   q [B][Hq][L][d], k [B][Hkv][L][d], v [B][Hkv][L][dv]  (contiguous fp64)
  *   unit_mask [B][Hq][nQT] or NULL: compute only units whose byte is nonzero
@@ -182,13 +193,14 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
  */
 int oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int64_t dv,
                    const double *q, const double *k, const double *v,
-                   int causal, double scale, double lambda,
+                   int causal, int64_t window, double scale, double lambda,
                    int64_t tile_q, int64_t block_k, const uint8_t *unit_mask,
                    double *o, uint8_t *skip_map, double *gap_map,
                    int64_t *counters, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || L < 0 || d <= 0 || dv <= 0 || tile_q <= 0 ||
-        block_k <= 0 || Hq % Hkv != 0 || !(lambda >= 0.0 && lambda < 1.0))
+        block_k <= 0 || Hq % Hkv != 0 || !(lambda >= 0.0 && lambda < 1.0) || window < 0 ||
+        (window > 0 && !causal))
         return ORACLE_EINVAL;
     const int64_t G = Hq / Hkv;
     const int64_t nqt = (L + tile_q - 1) / tile_q;
@@ -228,7 +240,7 @@ int oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int
                 const double *kb = k + (b * Hkv + hk) * L * d;
                 const double *vb = v + (b * Hkv + hk) * L * dv;
                 int64_t vis = 0, skp = 0;
-                oracle_unit(R, d, dv, qb, d, causal ? qpos : NULL, kb, vb, L, 0, nkb, block_k,
+                oracle_unit(R, d, dv, qb, d, causal ? qpos : NULL, window, kb, vb, L, 0, nkb, block_k,
                             scale, lnlam, m, l, acc, sk, gp, S, mt, &vis, &skp);
                 tot_visited += vis;
                 tot_skipped += skp;
@@ -260,17 +272,18 @@ int oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int
  *   q [B][Hq][dqk], k [B][Hkv][Lmax][dqk], v [B][Hkv][Lmax][dv]
  *   seq_lens [B] in 1..Lmax; keys >= seq_lens[b] are masked
  *   num_splits >= 1: contiguous block runs, each from m = -inf, merged by LSE
+ *   window > 0: the query (position len-1) sees the last `window` keys only
  *   unit_mask [B][Hkv] or NULL
  *   o [B][Hq][dv]; skip_map / gap_map [B][Hkv][nKB], nKB = ceil(Lmax/block_k)
  */
 int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk, int64_t dv,
                   const double *q, const double *k, const double *v, const int32_t *seq_lens,
-                  double scale, double lambda, int64_t block_k, int64_t num_splits,
+                  double scale, double lambda, int64_t block_k, int64_t num_splits, int64_t window,
                   const uint8_t *unit_mask, double *o, uint8_t *skip_map, double *gap_map,
                   int64_t *counters, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || dqk <= 0 || dv <= 0 || block_k <= 0 ||
-        num_splits <= 0 || Hq % Hkv != 0 || !(lambda >= 0.0 && lambda < 1.0))
+        num_splits <= 0 || Hq % Hkv != 0 || !(lambda >= 0.0 && lambda < 1.0) || window < 0)
         return ORACLE_EINVAL;
     for (int64_t b = 0; b < B; ++b)
         if (seq_lens[b] < 1 || seq_lens[b] > Lmax)
@@ -293,7 +306,8 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
         double *accs = malloc(sizeof(double) * G * dv * num_splits);
         uint8_t *sk = malloc(nkb);
         double *gp = malloc(sizeof(double) * nkb);
-        if (!S || !mt || !ms || !ls || !accs || !sk || !gp) {
+        int64_t *qpos = malloc(sizeof(int64_t) * G);
+        if (!S || !mt || !ms || !ls || !accs || !sk || !gp || !qpos) {
 #pragma omp atomic write
             err = ORACLE_ENOMEM;
         } else {
@@ -304,7 +318,10 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                 int64_t g = u % Hkv, b = u / Hkv;
                 int64_t len = seq_lens[b];
                 int64_t nkb_b = (len + block_k - 1) / block_k;
-                int64_t per = (nkb_b + num_splits - 1) / num_splits;
+                int64_t j0 = (window > 0 && len > window) ? (len - window) / block_k : 0;
+                int64_t per = (nkb_b - j0 + num_splits - 1) / num_splits;
+                for (int64_t r = 0; r < G; ++r)
+                    qpos[r] = len - 1; /* the query token is the sequence's last position */
                 const double *qb = q + (b * Hq + g * G) * dqk;
                 const double *kb = k + (b * Hkv + g) * Lmax * dqk;
                 const double *vb = v + (b * Hkv + g) * Lmax * dv;
@@ -313,7 +330,7 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                     gp[j] = -INFINITY;
                 }
                 for (int64_t s = 0; s < num_splits; ++s) {
-                    int64_t jb = s * per, je = (s + 1) * per;
+                    int64_t jb = j0 + s * per, je = j0 + (s + 1) * per;
                     if (je > nkb_b)
                         je = nkb_b;
                     double *m = ms + s * G, *l = ls + s * G, *acc = accs + s * G * dv;
@@ -325,7 +342,7 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                         continue;
                     }
                     int64_t vis = 0, skp = 0;
-                    oracle_unit(G, dqk, dv, qb, dqk, NULL, kb, vb, len, jb, je, block_k, scale,
+                    oracle_unit(G, dqk, dv, qb, dqk, window > 0 ? qpos : NULL, window, kb, vb, len, jb, je, block_k, scale,
                                 lnlam, m, l, acc, sk + jb, gp + jb, S, mt, &vis, &skp);
                     tot_visited += vis;
                     tot_skipped += skp;
@@ -358,7 +375,7 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                     memcpy(gap_map + u * nkb, gp, sizeof(double) * nkb);
             }
         }
-        free(S); free(mt); free(ms); free(ls); free(accs); free(sk); free(gp);
+        free(S); free(mt); free(ms); free(ls); free(accs); free(sk); free(gp); free(qpos);
     }
     if (counters) {
         counters[0] = tot_visited;

@@ -18,11 +18,14 @@ def scores(q, k, scale):
     return scale * (q @ k.T)
 
 
-def prefill_mask(L, causal):
-    """Visible[i, c] for Lq = Lk = L."""
+def prefill_mask(L, causal, window=0):
+    """Visible[i, c] for Lq = Lk = L; ``window`` > 0 keeps c > i - window only."""
     if not causal:
         return np.ones((L, L), dtype=bool)
-    return np.tril(np.ones((L, L), dtype=bool))
+    m = np.tril(np.ones((L, L), dtype=bool))
+    if window > 0:
+        m &= ~np.tril(np.ones((L, L), dtype=bool), -window)
+    return m
 
 
 def masked_softmax_attention(S, mask, v):

@@ -29,8 +29,11 @@ MUTANTS = [
     ("scale dropped", "double s = scale * dot;", "double s = dot;"),
     ("V row index", "const double *vc = v + (c0 + c) * dv;", "const double *vc = v + (c0 + c) * dv + (c > 0 ? dv : 0);"),
     ("GQA head mapping", "int64_t hk = h / G;", "int64_t hk = h % Hkv;"),
-    ("split length floor", "int64_t per = (nkb_b + num_splits - 1) / num_splits;",
-     "int64_t per = nkb_b / num_splits > 0 ? nkb_b / num_splits : 1;"),
+    ("split length floor", "int64_t per = (nkb_b - j0 + num_splits - 1) / num_splits;",
+     "int64_t per = (nkb_b - j0) / num_splits > 0 ? (nkb_b - j0) / num_splits : 1;"),
+    ("window edge off by one", "key > qpos[r] - window", "key >= qpos[r] - window"),
+    ("decode splits ignore the window", "int64_t j0 = (window > 0 && len > window) ? (len - window) / block_k : 0;",
+     "int64_t j0 = 0;"),
     ("merge weight sign", "double w = exp(ms[s * G + r] - M);", "double w = exp(M - ms[s * G + r]);"),
     ("quantile midpoint", "lnl = 0.5 * (s[kk - 1] + s[kk]);", "lnl = s[kk];"),
     ("fit uses lambda only", "sum += log(lambda_at_L[i] * (double)L[i]);", "sum += log(lambda_at_L[i]);"),

@@ -85,13 +85,13 @@ def test_decode_lambda0_is_dense_softmax(splits):
 
 
 # ------------------------------------------------------------ skip decisions
-def _prefill_brute_decisions(q, k, lam, causal, tq, bk):
+def _prefill_brute_decisions(q, k, lam, causal, tq, bk, window=0):
     B, Hq, L, d = q.shape
     G = Hq // k.shape[1]
     nqt, nkb = -(-L // tq), -(-L // bk)
     skip = np.zeros((B, Hq, nqt, nkb), np.uint8)
     gap = np.zeros((B, Hq, nqt, nkb))
-    mask = prefill_mask(L, causal)
+    mask = prefill_mask(L, causal, window)
     scale = 1 / math.sqrt(d)
     cols = [(j * bk, min(L, (j + 1) * bk)) for j in range(nkb)]
     for b in range(B):
@@ -402,3 +402,129 @@ def test_gather_pages_rejects_a_page_outside_the_pool():
     pool = np.zeros((2, 1, 16, 4))
     with pytest.raises(ValueError):
         oracle.gather_pages(pool, np.array([[0, 2]]), [20], 32)
+
+
+# ------------------------------------------------------------ sliding window
+# Reading: query i sees keys i - W < c <= i; decode's query sits at len-1 and
+# its splits cut the blocks from the first one that holds a visible key.
+
+@pytest.mark.parametrize("L,W,tq,bk", [(300, 100, 64, 64), (257, 64, 128, 64), (200, 1, 32, 16),
+                                       (130, 129, 64, 32), (90, 7, 16, 8)])
+def test_window_lambda0_is_band_softmax(L, W, tq, bk):
+    q, k, v = _prefill_case(40 + W, B=1, Hq=2, Hkv=1, L=L)
+    r = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=tq, block_k=bk, window=W)
+    mask = prefill_mask(L, True, W)
+    for h in range(2):
+        S = scores(q[0, h], k[0, 0], 1 / math.sqrt(q.shape[-1]))
+        np.testing.assert_allclose(r["o"][0, h], masked_softmax_attention(S, mask, v[0, 0]), rtol=0, atol=1e-10)
+    # a block is visited iff some row of the tile sees one of its keys
+    for t in range(-(-L // tq)):
+        for j in range(-(-L // bk)):
+            seen = mask[t * tq:(t + 1) * tq, j * bk:(j + 1) * bk].any()
+            assert (r["skip"][0, 0, t, j] != 255) == seen
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_window_prefill_decisions_match_bruteforce(seed):
+    rng = np.random.default_rng(500 + seed)
+    L = int(rng.integers(60, 260))
+    tq = int(rng.choice([16, 32, 64]))
+    bk = int(rng.choice([8, 16, 32]))
+    W = int(rng.integers(1, L))
+    q, k, v = _prefill_case(seed + 50, B=1, Hq=2, Hkv=1, L=L, d=8, dv=4, qstd=2.0, blocky=bk)
+    _, g0 = _prefill_brute_decisions(q, k, 0.0, True, tq, bk, W)
+    lam = _lam_at(g0, rng.uniform(0.2, 0.8))
+    r = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=tq, block_k=bk, window=W)
+    skip, gap = _prefill_brute_decisions(q, k, lam, True, tq, bk, W)
+    fin = np.isfinite(gap)
+    np.testing.assert_allclose(r["gap"][fin], gap[fin], rtol=0, atol=1e-9)
+    assert np.array_equal(r["gap"][~fin], gap[~fin])
+    near = np.abs(gap - math.log(lam)) < 1e-9
+    assert np.array_equal(r["skip"][~near], skip[~near])
+    assert r["visited"] == int((skip != 255).sum())
+
+
+def test_window_of_one_returns_the_own_value():
+    """W = 1: every query sees only itself, so O[i] = V[i] whatever lambda is."""
+    q, k, v = _prefill_case(61, B=1, Hq=1, Hkv=1, L=150, d=8, dv=5)
+    for lam in (0.0, 0.5):
+        r = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=64, block_k=16, window=1)
+        np.testing.assert_allclose(r["o"][0, 0], v[0, 0], rtol=0, atol=1e-15)
+
+
+def test_window_covering_the_sequence_is_plain_causal():
+    q, k, v = _prefill_case(62, B=1, Hq=2, Hkv=1, L=200, blocky=16)
+    lam = 0.05
+    a = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=32, block_k=16)
+    for W in (200, 500):
+        b = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=32, block_k=16, window=W)
+        for key in ("o", "skip", "gap"):
+            assert np.array_equal(a[key], b[key])
+    rng = np.random.default_rng(63)
+    qd, kd, vd = _rand(rng, 2, 4, 8, std=2.0), _rand(rng, 2, 2, 300, 8, std=2.0), _rand(rng, 2, 2, 300, 6)
+    lens = np.array([300, 77])
+    a = oracle.decode(qd, kd, vd, lens, lam=lam, block_k=16, num_splits=3)
+    b = oracle.decode(qd, kd, vd, lens, lam=lam, block_k=16, num_splits=3, window=300)
+    for key in ("o", "skip", "gap"):
+        assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("W", [1, 50, 64, 65, 200])
+def test_window_decode_is_the_last_prefill_row(W):
+    """One split, one head per KV head: the decode unit of a sequence of length
+    L is the prefill unit of its last position (tile of one row)."""
+    rng = np.random.default_rng(64 + W)
+    L, d, dv = 300, 8, 6
+    q, k, v = _rand(rng, 1, 1, L, d, std=2.0), _rand(rng, 1, 1, L, d, std=2.0), _rand(rng, 1, 1, L, dv)
+    lam = 0.02
+    p = oracle.prefill(q, k, v, causal=True, lam=lam, tile_q=1, block_k=32, window=W)
+    r = oracle.decode(q[:, :, -1], k, v, np.array([L]), lam=lam, block_k=32, num_splits=1, window=W)
+    np.testing.assert_allclose(r["o"][0, 0], p["o"][0, 0, -1], rtol=0, atol=1e-14)
+    assert np.array_equal(r["skip"][0, 0], p["skip"][0, 0, -1])
+    np.testing.assert_allclose(r["gap"][0, 0], p["gap"][0, 0, -1], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_window_decode_decisions_and_split_origin(seed):
+    """Decisions by the closed form of the running max over the band, with
+    the splits cutting the blocks that meet the window; merged output equals
+    softmax over the executed keys."""
+    rng = np.random.default_rng(700 + seed)
+    B, Hq, Hkv, Lmax, d, dv, bk = 2, 4, 2, int(rng.integers(200, 500)), 8, 6, 16
+    splits = int(rng.integers(2, 5))
+    q = _rand(rng, B, Hq, d, std=2.0)
+    k = _rand(rng, B, Hkv, Lmax, d, std=2.0)
+    v = _rand(rng, B, Hkv, Lmax, dv)
+    lens = rng.integers(Lmax // 2, Lmax + 1, size=B)
+    W = int(rng.integers(bk + 1, Lmax // 2))
+    lam = float(10 ** rng.uniform(-4, -1))
+    r = oracle.decode(q, k, v, lens, lam=lam, block_k=bk, num_splits=splits, window=W)
+    G, scale, nkb = Hq // Hkv, 1 / math.sqrt(d), -(-Lmax // bk)
+    for b in range(B):
+        n = int(lens[b])
+        j0 = max(0, n - W) // bk
+        nkb_b = -(-n // bk)
+        per = -(-(nkb_b - j0) // splits)
+        keys = np.arange(Lmax)
+        for g in range(Hkv):
+            S = scores(q[b, g * G:(g + 1) * G], k[b, g], scale)
+            mask = np.broadcast_to((keys < n) & (keys >= n - W), S.shape)
+            exp_skip, exp_gap = [255] * nkb, [-math.inf] * nkb
+            for s in range(splits):
+                jb, je = j0 + s * per, min(nkb_b, j0 + (s + 1) * per)
+                if jb >= je:
+                    continue
+                cols = [(j * bk, min(Lmax, (j + 1) * bk)) for j in range(jb, je)]
+                exp_skip[jb:je], exp_gap[jb:je] = block_decisions(S, mask, None, cols, lam)
+                assert exp_gap[jb] == math.inf  # each split starts from m = -inf
+            exp_gap = np.array(exp_gap)
+            fin = np.isfinite(exp_gap)
+            np.testing.assert_allclose(r["gap"][b, g][fin], exp_gap[fin], rtol=0, atol=1e-9)
+            assert np.array_equal(r["gap"][b, g][~fin], exp_gap[~fin])
+            near = np.abs(exp_gap - math.log(lam)) < 1e-9
+            assert np.array_equal(r["skip"][b, g][~near], np.array(exp_skip, np.uint8)[~near])
+            # output = softmax over the visible keys of executed blocks
+            ex = np.repeat(r["skip"][b, g] == 0, bk)[:Lmax]
+            for hh in range(G):
+                ref = masked_softmax_attention(S[hh:hh + 1], (mask[hh] & ex)[None], v[b, g])[0]
+                np.testing.assert_allclose(r["o"][b, g * G + hh], ref, rtol=0, atol=1e-10)
