@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BLASST_ABI_VERSION 1
+#define BLASST_ABI_VERSION 2
 
 typedef enum {
     BLASST_OK = 0,
@@ -84,8 +84,15 @@ typedef struct {
  *             nKB = ceil(L/block_k), contiguous.
  *   gap_map : optional device float [B, Hq, nQT, nKB], contiguous.
  *   counters: optional device uint64 [2].
+ *   window  : 0 = none; W > 0 (causal only) = sliding window: query i sees
+ *             keys i - W < c <= i.  The BLASST reading notes
+ *             (papers.lqhl.me/papers/BLASST-MLSys26, "问题与动机") list
+ *             sliding-window attention among the supported forms.  Key blocks
+ *             with no key inside any row's window are not visited (255 in the
+ *             skip map); the skip test runs unchanged on the others.
  * Errors: INVALID_ARG for null q/k/v/o, L < 0, B < 0, Hq or Hkv <= 0,
- * Hq % Hkv != 0, lambda outside [0,1) or NaN, a non-positive stride or a
+ * Hq % Hkv != 0, lambda outside [0,1) or NaN, window < 0 or a window without
+ * causal masking, a non-positive stride or a
  * pointer not aligned to 16 bytes with a token stride not a multiple of 8
  * elements; UNSUPPORTED for other d, dv, tile or dtype; LAUNCH if HIP fails.
  * L = 0 or B = 0 is a valid no-op.
@@ -101,6 +108,7 @@ typedef struct {
     uint8_t *skip_map;
     float *gap_map;
     unsigned long long *counters;
+    int64_t window;
 } blasst_prefill_params;
 
 blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream);
@@ -126,6 +134,11 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream);
  *   (dqk = 576, dv = 512, Hkv = 1, G = 128, v aliasing k).  block_k = 64.
  *   num_splits: 0 lets the library choose; otherwise 1..nKB.
  *   skip_map / gap_map: optional device [B, Hkv, nKB], nKB = ceil(Lmax/64).
+ *   window  : 0 = none; W > 0 = sliding window (see blasst_prefill): the
+ *             query, at position seq_len-1, sees the last W keys.  The splits
+ *             then cut the blocks from the first one holding such a key,
+ *             j0 = max(0, seq_len - W) / 64, into runs of
+ *             ceil((nkb - j0) / num_splits) blocks.
  */
 typedef struct {
     blasst_tensor q, k_cache, v_cache, o;
@@ -138,6 +151,7 @@ typedef struct {
     uint8_t *skip_map;
     float *gap_map;
     unsigned long long *counters;
+    int64_t window;
 } blasst_decode_params;
 
 /* Host-only: the split count a call with *p will use and the device workspace

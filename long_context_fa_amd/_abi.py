@@ -39,7 +39,7 @@ class _PrefillParams(ctypes.Structure):
                 ("causal", ctypes.c_int), ("scale", ctypes.c_double), ("lam", ctypes.c_double),
                 ("tile_q", ctypes.c_int), ("block_k", ctypes.c_int),
                 ("skip_map", ctypes.c_void_p), ("gap_map", ctypes.c_void_p),
-                ("counters", ctypes.c_void_p)]
+                ("counters", ctypes.c_void_p), ("window", ctypes.c_int64)]
 
 
 class _DecodeParams(ctypes.Structure):
@@ -50,7 +50,7 @@ class _DecodeParams(ctypes.Structure):
                 ("scale", ctypes.c_double), ("lam", ctypes.c_double),
                 ("block_k", ctypes.c_int), ("num_splits", ctypes.c_int),
                 ("skip_map", ctypes.c_void_p), ("gap_map", ctypes.c_void_p),
-                ("counters", ctypes.c_void_p)]
+                ("counters", ctypes.c_void_p), ("window", ctypes.c_int64)]
 
 
 class _DecodePagedParams(ctypes.Structure):
@@ -152,8 +152,11 @@ def _check(status, func):
 
 
 def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, scale=None, out=None,
-                   out_dtype=torch.float32, skip_map=None, gap_map=None, counters=None, stream=None):
+                   out_dtype=torch.float32, skip_map=None, gap_map=None, counters=None, stream=None,
+                   window=0):
     """Block-skipping prefill: q [B,Hq,L,d], k [B,Hkv,L,d], v [B,Hkv,L,dv] (bf16, device).
+
+    ``window`` > 0 (causal): sliding window, query i sees keys i - window < c <= i.
 
     Returns O [B,Hq,L,dv] (``out`` if given).  Optional outputs: ``skip_map``
     uint8 and ``gap_map`` float32 of shape [B,Hq,ceil(L/tile_q),ceil(L/block_k)],
@@ -166,29 +169,29 @@ def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, sca
         out = torch.empty(B, Hq, L, dv, dtype=out_dtype, device=q.device)
     p = _PrefillParams(_tensor(q), _tensor(k), _tensor(v), _tensor(out), B, Hq, Hkv, L, d, dv,
                        int(bool(causal)), float(scale) if scale is not None else 0.0, float(lam),
-                       int(tile_q), int(block_k), _ptr(skip_map), _ptr(gap_map), _ptr(counters))
+                       int(tile_q), int(block_k), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
     _check(load_library().blasst_prefill(ctypes.byref(p), _stream(stream, q.device)), "blasst_prefill")
     return out
 
 
 def _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
-                   skip_map, gap_map, counters):
+                   skip_map, gap_map, counters, window=0):
     B, Hq, dqk = q.shape
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
     dv = out.shape[2] if out is not None else (v_cache.shape[3] if v_cache is not None else dqk)
     return _DecodeParams(_tensor(q, True), _tensor(k_cache), _tensor(v_cache), _tensor(out, True),
                          _ptr(seq_lens), B, Hq, Hkv, Lmax, dqk, dv,
                          float(scale) if scale is not None else 0.0, float(lam), int(block_k),
-                         int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters))
+                         int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
 
 
 def blasst_decode_plan(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
-                       dv=None, out_dtype=torch.float32):
+                       dv=None, out_dtype=torch.float32, window=0):
     """(num_splits the call will use, workspace bytes it needs)."""
     B, Hq, _ = q.shape
     dv = dv if dv is not None else v_cache.shape[3]
     p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, None,
-                       None, None, None)
+                       None, None, None, window)
     # the planner reads no device memory: describe O [B,Hq,dv] at q's (aligned) address
     p.o = _Tensor(q.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _FP32, Hq * dv, dv, 0)
     p.dv = dv
@@ -200,8 +203,10 @@ def blasst_decode_plan(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, bl
 
 def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
                   dv=None, out=None, out_dtype=torch.float32, workspace=None, skip_map=None,
-                  gap_map=None, counters=None, stream=None):
+                  gap_map=None, counters=None, stream=None, window=0):
     """Block-skipping decode: q [B,Hq,dqk], caches [B,Hkv,Lmax,*] (bf16, device), seq_lens int32 [B].
+
+    ``window`` > 0: sliding window, the query sees the last ``window`` keys.
 
     For the latent (MLA) form pass ``v_cache = k_cache`` and ``dv=512``.
     ``workspace`` (uint8 device tensor) is allocated here when not given.
@@ -212,7 +217,7 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
     if out is None:
         out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
     p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
-                       skip_map, gap_map, counters)
+                       skip_map, gap_map, counters, window)
     lib = load_library()
     if workspace is None:
         ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
@@ -224,27 +229,27 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
 
 
 def _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits, o,
-                  skip_map, gap_map, counters):
+                  skip_map, gap_map, counters, window=0):
     B, Hq, dqk = q.shape
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
         raise ValueError("page_table must be an int32 [B, pages_per_seq] tensor with unit column stride")
     d = _DecodeParams(_tensor(q, True), _tensor(k_pages), _tensor(v_pages), o,
                       _ptr(seq_lens), B, Hq, k_pages.shape[1], int(Lmax), dqk, 0,
                       float(scale) if scale is not None else 0.0, float(lam), int(block_k),
-                      int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters))
+                      int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
     return _DecodePagedParams(d, page_table.data_ptr(), page_table.stride(0), k_pages.shape[0],
                               k_pages.shape[2])
 
 
 def blasst_decode_paged_plan(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=0.0, scale=None,
-                             block_k=64, num_splits=0, dv=None, out_dtype=torch.float32):
+                             block_k=64, num_splits=0, dv=None, out_dtype=torch.float32, window=0):
     """(num_splits the paged call will use, workspace bytes it needs)."""
     B, Hq, _ = q.shape
     dv = dv if dv is not None else v_pages.shape[3]
     # the planner reads no device memory: describe O [B,Hq,dv] at q's (aligned) address
     o = _Tensor(q.data_ptr(), _BF16 if out_dtype == torch.bfloat16 else _FP32, Hq * dv, dv, 0)
     p = _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits, o,
-                      None, None, None)
+                      None, None, None, window)
     p.d.dv = dv
     ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
     _check(load_library().blasst_decode_paged_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)),
@@ -254,7 +259,7 @@ def blasst_decode_paged_plan(q, k_pages, v_pages, page_table, seq_lens, Lmax, *,
 
 def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=0.0, scale=None, block_k=64,
                         num_splits=0, dv=None, out=None, out_dtype=torch.float32, workspace=None, skip_map=None,
-                        gap_map=None, counters=None, stream=None):
+                        gap_map=None, counters=None, stream=None, window=0):
     """Block-skipping decode over a paged cache.
 
     q [B,Hq,dqk]; k_pages [num_pages,Hkv,page_size,dqk] and v_pages
@@ -269,7 +274,7 @@ def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=
     if out is None:
         out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
     p = _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits,
-                      _tensor(out, True), skip_map, gap_map, counters)
+                      _tensor(out, True), skip_map, gap_map, counters, window)
     p.d.dv = dv
     lib = load_library()
     if workspace is None:

@@ -60,6 +60,14 @@ float log2_lambda(double lambda)
     return lambda == 0.0 ? -INFINITY : (float)std::log2(lambda);
 }
 
+// Kernel form of a sliding window: no window, or one at least as long as the
+// sequence, becomes 2^30 (> any length the library accepts), so the kernels'
+// lower-edge tests are never true.
+int window_arg(int64_t window, int64_t len)
+{
+    return (window <= 0 || window >= len) ? (1 << 30) : (int)window;
+}
+
 } // namespace
 
 extern "C" {
@@ -108,6 +116,8 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
         return fail(BLASST_ERR_UNSUPPORTED, "tile_q must be 64 or 128 (got %d)", p->tile_q);
     if (p->block_k != 64)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
+    if (p->window < 0 || (p->window > 0 && !p->causal))
+        return fail(BLASST_ERR_INVALID_ARG, "window must be >= 0, and a window needs causal masking");
     const int64_t nqt = (p->L + p->tile_q - 1) / p->tile_q;
     const int64_t nkb = (p->L + p->block_k - 1) / p->block_k;
     if (p->L > (int64_t)1 << 30 || nqt * p->Hq * p->B > (int64_t)1 << 31)
@@ -132,6 +142,7 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
     a.skip_map = p->skip_map;
     a.gap_map = p->gap_map;
     a.counters = p->counters;
+    a.win = window_arg(p->window, p->L);
     const bool skip = p->lambda > 0.0;
     hipError_t e = blasst::launch_prefill(a, (int)p->d, p->tile_q, p->causal != 0, skip,
                                           p->o.dtype == BLASST_BF16, (hipStream_t)hip_stream);
@@ -181,6 +192,8 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
         return s;
     if (p->block_k != 64)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
+    if (p->window < 0)
+        return fail(BLASST_ERR_INVALID_ARG, "window must be >= 0");
     const DecodeKind kind = decode_kind(p);
     if (kind == KIND_NONE)
         return fail(BLASST_ERR_UNSUPPORTED,
@@ -214,7 +227,9 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
 
 int choose_splits(const blasst_decode_params *p)
 {
-    const int64_t nkb = (p->Lmax + 63) / 64;
+    int64_t nkb = (p->Lmax + 63) / 64;
+    if (p->window > 0 && (p->window + 63) / 64 + 1 < nkb)
+        nkb = (p->window + 63) / 64 + 1; // blocks a window of this length can touch
     if (p->num_splits > 0)
         return p->num_splits;
     const int64_t units = p->B * p->Hkv;
@@ -296,6 +311,7 @@ blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_page
     a.skip_map = p->skip_map;
     a.gap_map = p->gap_map;
     a.counters = p->counters;
+    a.win = window_arg(p->window, p->Lmax);
     if (pg) {
         a.page_table = pg->page_table;
         a.pt_stride = pg->page_table_stride;

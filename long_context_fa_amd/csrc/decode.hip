@@ -62,15 +62,21 @@ void decode_gqa_kernel(const DecodeArgs a)
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
     const int nkb_b = (len + BC - 1) / BC;
-    const int per = (nkb_b + S - 1) / S;
-    const int jb = s * per;
+    // Sliding window: the query (position len-1) sees keys klo .. len-1, and
+    // the splits cut the blocks j0 .. nkb_b-1 that hold them.
+    const int klo = len - a.win > 0 ? len - a.win : 0;
+    const int j0 = klo / BC;
+    const int per = (nkb_b - j0 + S - 1) / S;
+    const int jb = j0 + s * per;
     const int je = (jb + per < nkb_b) ? jb + per : nkb_b;
 
     // Cache rows.  Contiguous cache: row r of the sequence at kp + r * k_st.
     // Paged cache: pool page page_table[b][r >> page_shift], row r & pmask of
     // that page.  A page holds a power of two >= 16 rows, so the 16 rows of an
-    // aligned group share one page; a row past the sequence is read as row
-    // len-1, which lies in the page of the group's first row clamped to len-1.
+    // aligned group share one page.  Rows outside klo .. len-1 are read as the
+    // nearest row inside (finite data under a zero probability, never a row
+    // of a page that may not exist), which lies in the page of the group's
+    // first row clamped into klo .. len-1.
     // The 4 group ids of a block come from one vector load (lane kt < 4 reads
     // group kt's entry) issued a batch ahead, right behind the K loads of the
     // batch before; they are moved to SGPRs before the next V copy is issued,
@@ -82,7 +88,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         if (!PAGED)
             return 0;
         int g0 = j * BC + 16 * (lane & 3);
-        g0 = (j < je && g0 < len) ? g0 : len - 1;
+        g0 = (j < je && g0 < len) ? (g0 > klo ? g0 : klo) : len - 1;
         return a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
     };
     auto ids_take = [&](int v, int (&ids)[4]) {
@@ -123,7 +129,7 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int key = j * BC + 16 * kt + n;
-            const int kc = (j < je && key < len) ? key : len - 1;
+            const int kc = (j < je && key < len) ? (key > klo ? key : klo) : len - 1;
             const uint16_t *rp = kp + page_off(ids, kt, a.k_sb) + (int64_t)(kc & pmask) * a.k_st;
 #pragma unroll
             for (int st = 0; st < NS; ++st)
@@ -139,7 +145,7 @@ void decode_gqa_kernel(const DecodeArgs a)
             const int row = i * RPI + lane / DG;
             const int c = (lane % DG) ^ swz<DG>(row);
             int key = j * BC + row;
-            key = key < len ? key : len - 1;
+            key = key < len ? (key > klo ? key : klo) : len - 1;
             copy16_to_lds(vp + page_off(ids, (i * RPI) >> 4, a.v_sb) + (int64_t)(key & pmask) * a.v_st + c * 8,
                           vt + i * 1024);
         }
@@ -179,15 +185,15 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
         if (PAGED)
             ids_take(idv, pn); // issued behind the K loads just consumed
-        // Mask keys past the sequence (and the whole block if j >= je).
+        // Mask keys outside klo .. len-1 (and the whole block if j >= je).
         const int k0 = j * BC;
-        if (j >= je || k0 + BC > len) {
+        if (j >= je || k0 + BC > len || k0 < klo) {
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = k0 + 16 * kt + 4 * grp + r;
-                    if (j >= je || key >= len)
+                    if (j >= je || key >= len || key < klo)
                         sc[kt][r] = neg_inf();
                 }
         }
@@ -350,14 +356,23 @@ void decode_gqa_kernel(const DecodeArgs a)
     }
 
     if (tid == 0) {
-        if (want_maps && s == S - 1)
-            for (int j = nkb_b; j < a.nkb; ++j) {
+        // Blocks that no split visits: before the window (first split writes
+        // them) and past the sequence (last split).
+        if (want_maps) {
+            auto unvisited = [&](int j) {
                 const int64_t idx = (int64_t)(b * a.Hkv + g) * a.nkb + j;
                 if (a.skip_map)
                     a.skip_map[idx] = 255;
                 if (a.gap_map)
                     a.gap_map[idx] = neg_inf();
-            }
+            };
+            if (s == 0)
+                for (int j = 0; j < j0; ++j)
+                    unvisited(j);
+            if (s == S - 1)
+                for (int j = nkb_b; j < a.nkb; ++j)
+                    unvisited(j);
+        }
         if (a.counters && je > jb) {
             atomicAdd(a.counters, (unsigned long long)(je - jb));
             atomicAdd(a.counters + 1, (unsigned long long)n_skipped);

@@ -17,6 +17,7 @@ struct PrefillArgs {
     uint8_t *skip_map;
     float *gap_map;
     unsigned long long *counters;
+    int win; // sliding window: query i sees keys > i - win (2^30 when there is none)
 };
 
 // Launches the prefill kernel for (d, tile_q, causal, skip, out dtype).
@@ -30,6 +31,7 @@ struct DecodeArgs {
     int64_t q_sb, q_sh, k_sb, k_sh, k_st, v_sb, v_sh, v_st, o_sb, o_sh;
     const int32_t *seq_lens;
     int B, Hq, Hkv, G, Lmax, nkb, num_splits;
+    int win; // sliding window: the query sees the last win keys (2^30 when there is none)
     float scale_log2;
     float lnlam2;
     float *part_o;  // [B][Hkv][S][G][dv] fp32 (num_splits > 1)

@@ -77,23 +77,27 @@ void decode_mla_kernel(const DecodeArgs a)
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
     const int nkb_b = (len + BC - 1) / BC;
-    const int per = (nkb_b + S - 1) / S;
-    const int jb = s * per;
+    // Sliding window: the query (position len-1) sees keys klo .. len-1, and
+    // the splits cut the blocks j0 .. nkb_b-1 that hold them.
+    const int klo = len - a.win > 0 ? len - a.win : 0;
+    const int j0 = klo / BC;
+    const int per = (nkb_b - j0 + S - 1) / S;
+    const int jb = j0 + s * per;
     const int je = (jb + per < nkb_b) ? jb + per : nkb_b;
 
     // Rows of wave w's copies: the aligned 16-row group 16w.. of a block.  A
     // contiguous cache holds row r at kp + r * k_st; a paged cache holds it in
     // pool page page_table[b][r >> page_shift] at row r & pmask, and a page
-    // of >= 16 rows holds the whole group (rows past len read row len-1, in
-    // the page of the group's first row clamped to len-1): one wave-uniform
-    // page lookup per block.
+    // of >= 16 rows holds the whole group (rows outside klo .. len-1 read the
+    // nearest row inside, in the page of the group's first row clamped into
+    // klo .. len-1): one wave-uniform page lookup per block.
     const uint16_t *kp = a.k + (PAGED ? 0 : b * a.k_sb);
     const int pmask = PAGED ? (1 << a.page_shift) - 1 : -1;
     auto group_base = [&](int j) -> const uint16_t * {
         if (!PAGED)
             return kp;
         int g0 = j * BC + 16 * w;
-        g0 = g0 < len ? g0 : len - 1;
+        g0 = g0 < len ? (g0 > klo ? g0 : klo) : len - 1;
         int id = a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
         id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
         return kp + (int64_t)id * a.k_sb;
@@ -112,8 +116,8 @@ void decode_mla_kernel(const DecodeArgs a)
     // copy i < 16 is the latent part of row 16w+i (lane l loads logical
     // chunk l ^ swzl(i) into physical chunk l), copies 16 and 17 are the rope
     // parts of 8 rows each (lane l: row +l/8, physical chunk l%8, logical
-    // chunk (l%8) ^ swzr(row)).  Rows past len re-read row len-1 (finite
-    // data, masked later).  Offsets are 32-bit from the sequence (or page)
+    // chunk (l%8) ^ swzr(row)).  Rows outside klo .. len-1 re-read the nearest
+    // row inside (finite data, masked later).  Offsets are 32-bit from the sequence (or page)
     // base gb = group_base(j) (the host checks rows * row stride).
     auto tile = [&](int j) { return smem + (j & 1) * TB; };
     const uint32_t rowb = (uint32_t)a.k_st * 2;
@@ -121,7 +125,7 @@ void decode_mla_kernel(const DecodeArgs a)
         char *t = tile(j);
         if (i < 16) {
             int key = j * BC + 16 * w + i;
-            key = key < len ? key : len - 1;
+            key = key < len ? (key > klo ? key : klo) : len - 1;
             copy16_to_lds_s(gb + (int64_t)(key & pmask) * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))),
                             t + (16 * w + i) * LRB);
         } else {
@@ -129,7 +133,7 @@ void decode_mla_kernel(const DecodeArgs a)
             int lr = lane >> 3;
             asm volatile("" : "+v"(lr)); // no loop-carried per-lane key registers
             int key = j * BC + 16 * w + 8 * e + lr;
-            key = key < len ? key : len - 1;
+            key = key < len ? (key > klo ? key : klo) : len - 1;
             const uint32_t off = LRB + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7)); // swzr of the row
             copy16_to_lds_s(gb, (uint32_t)(key & pmask) * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
         }
@@ -210,13 +214,15 @@ void decode_mla_kernel(const DecodeArgs a)
         }
         mfma_v_drain2(sc[0], sc[1]);
         const int k0 = j * BC;
-        if (k0 + BC > len) {
+        if (k0 + BC > len || k0 < klo) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (k0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3) >= len)
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (key >= len || key < klo)
                         sc[kt][r] = neg_inf();
+                }
         }
         float mt = neg_inf();
 #pragma unroll
@@ -361,14 +367,23 @@ void decode_mla_kernel(const DecodeArgs a)
         }
     }
     if (tid == 0) {
-        if (want_maps && s == S - 1)
-            for (int j = nkb_b; j < a.nkb; ++j) {
+        // Blocks that no split visits: before the window (first split writes
+        // them) and past the sequence (last split).
+        if (want_maps) {
+            auto unvisited = [&](int j) {
                 const int64_t idx = (int64_t)b * a.nkb + j;
                 if (a.skip_map)
                     a.skip_map[idx] = 255;
                 if (a.gap_map)
                     a.gap_map[idx] = neg_inf();
-            }
+            };
+            if (s == 0)
+                for (int j = 0; j < j0; ++j)
+                    unvisited(j);
+            if (s == S - 1)
+                for (int j = nkb_b; j < a.nkb; ++j)
+                    unvisited(j);
+        }
         if (a.counters && je > jb) {
             atomicAdd(a.counters, (unsigned long long)(je - jb));
             atomicAdd(a.counters + 1, (unsigned long long)n_skipped);

@@ -113,6 +113,9 @@ void prefill_kernel(const PrefillArgs a)
 
     const int last_row = (r0 + BR < L ? r0 + BR : L) - 1;
     const int nvis = CAUSAL ? (last_row / BC + 1 < a.nkb ? last_row / BC + 1 : a.nkb) : a.nkb;
+    // Sliding window (causal): row i sees keys > i - win, so the tile visits
+    // blocks jlo .. nvis-1, every one of which some row sees.
+    const int jlo = CAUSAL && r0 - a.win + 1 > 0 ? (r0 - a.win + 1) / BC : 0;
 
     // Tile copy: wave w fills rows [w*KI*RPI, (w+1)*KI*RPI); lane -> (row, chunk)
     // with the chunk XOR-swizzled by the row (swz).  Per-lane byte offsets of
@@ -181,13 +184,13 @@ void prefill_kernel(const PrefillArgs a)
                 s[kt] = mfma32(as_bf16x8(ka[kk % 3][kt]), qf[kk], s[kt]);
         }
         const int k0 = j * BC;
-        if ((CAUSAL && k0 + BC - 1 > r0) || k0 + BC > L) {
+        if ((CAUSAL && (k0 + BC - 1 > r0 || k0 <= r0 + BR - 1 - a.win)) || k0 + BC > L) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key >= L || (CAUSAL && key > qrow))
+                    if (key >= L || (CAUSAL && (key > qrow || key <= qrow - a.win)))
                         s[kt][r] = neg_inf();
                 }
         }
@@ -301,9 +304,9 @@ void prefill_kernel(const PrefillArgs a)
     // scores of block j+1 (MFMA); finally vote on block j+1.  The other
     // workgroup on the compute unit fills the matrix / vector gaps.  By the barrier of iteration j+1 the V_j and K_{j+2} copies
     // have had a whole iteration to land.
-    copy_tile(kp, a.k_st, koff, 0, kbuf(0));
-    if (1 < nvis) {
-        copy_tile(kp, a.k_st, koff, 1, kbuf(1));
+    copy_tile(kp, a.k_st, koff, jlo, kbuf(jlo));
+    if (jlo + 1 < nvis) {
+        copy_tile(kp, a.k_st, koff, jlo + 1, kbuf(jlo + 1));
         wait_vmcnt<KI>();
     } else {
         wait_vmcnt<0>();
@@ -311,12 +314,12 @@ void prefill_kernel(const PrefillArgs a)
     lds_barrier();
     f32x16 sc[2];
     float mt2c;
-    scores(0, sc, mt2c);
-    vote_block(0, mt2c);
+    scores(jlo, sc, mt2c);
+    vote_block(jlo, mt2c);
 
     bf16x8 pprev[4];
     bool eprev = false;
-    for (int j = 0; j < nvis; ++j) {
+    for (int j = jlo; j < nvis; ++j) {
         wait_vmcnt<0>();
         lds_barrier(); // votes_j, K_{j+1}, V_{j-1} visible; iteration j-1 done everywhere
         const int par = j & 1;
@@ -385,16 +388,21 @@ void prefill_kernel(const PrefillArgs a)
             }
     }
     if (tid == 0) {
-        if (want_maps)
-            for (int j = nvis; j < a.nkb; ++j) {
+        if (want_maps) {
+            auto unvisited = [&](int j) {
                 const int64_t idx = ((int64_t)(b * a.Hq + h) * a.nqt + t) * a.nkb + j;
                 if (a.skip_map)
                     a.skip_map[idx] = 255;
                 if (a.gap_map)
                     a.gap_map[idx] = neg_inf();
-            }
+            };
+            for (int j = 0; j < jlo; ++j)
+                unvisited(j);
+            for (int j = nvis; j < a.nkb; ++j)
+                unvisited(j);
+        }
         if (a.counters) {
-            atomicAdd(a.counters, (unsigned long long)nvis);
+            atomicAdd(a.counters, (unsigned long long)(nvis - jlo));
             atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
         }
     }

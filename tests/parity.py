@@ -64,19 +64,19 @@ def check_output(o_gpu, o_ref, what=""):
     return mx, mean
 
 
-def gpu_prefill(q, k, v, *, causal, lam, tile_q, maps=True, out_dtype=torch.float32):
+def gpu_prefill(q, k, v, *, causal, lam, tile_q, maps=True, out_dtype=torch.float32, window=0):
     B, Hq, L, _ = q.shape
     nqt, nkb = -(-L // tile_q), -(-L // 64)
     skip = torch.full((B, Hq, nqt, nkb), 7, dtype=torch.uint8, device=q.device) if maps else None
     gap = torch.full((B, Hq, nqt, nkb), float("nan"), dtype=torch.float32, device=q.device) if maps else None
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_prefill(q, k, v, causal=causal, lam=lam, tile_q=tile_q, skip_map=skip, gap_map=gap,
-                          counters=cnt, out_dtype=out_dtype)
+                          counters=cnt, out_dtype=out_dtype, window=window)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 
 
-def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dtype=torch.float32):
+def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dtype=torch.float32, window=0):
     B = q.shape[0]
     Hkv, Lmax = kc.shape[1], kc.shape[2]
     nkb = -(-Lmax // 64)
@@ -84,13 +84,13 @@ def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dt
     gap = torch.full((B, Hkv, nkb), float("nan"), dtype=torch.float32, device=q.device) if maps else None
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_decode(q, kc, vc, lens, lam=lam, num_splits=num_splits, dv=dv, skip_map=skip, gap_map=gap,
-                         counters=cnt, out_dtype=out_dtype)
+                         counters=cnt, out_dtype=out_dtype, window=window)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 
 
 def gpu_decode_paged(q, k_pages, v_pages, table, lens, Lmax, *, lam, num_splits=0, dv=None,
-                     out_dtype=torch.float32):
+                     out_dtype=torch.float32, window=0):
     """blasst_decode_paged with fresh skip/gap maps and counters (as gpu_decode)."""
     B, Hkv = q.shape[0], k_pages.shape[1]
     nkb = -(-Lmax // 64)
@@ -98,7 +98,7 @@ def gpu_decode_paged(q, k_pages, v_pages, table, lens, Lmax, *, lam, num_splits=
     gap = torch.full((B, Hkv, nkb), float("nan"), dtype=torch.float32, device=q.device)
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_decode_paged(q, k_pages, v_pages, table, lens, Lmax, lam=lam, num_splits=num_splits, dv=dv,
-                               skip_map=skip, gap_map=gap, counters=cnt, out_dtype=out_dtype)
+                               skip_map=skip, gap_map=gap, counters=cnt, out_dtype=out_dtype, window=window)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = bl.load_library()
     for name in declared:
         assert hasattr(lib, name), name
-    assert bl.blasst_abi_version() == 1
+    assert bl.blasst_abi_version() == 2
     for s in range(5):
         assert bl.blasst_status_str(s) != "unknown status"
     assert bl.blasst_status_str(99) == "unknown status"

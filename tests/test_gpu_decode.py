@@ -13,11 +13,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _compare(q, kk, vv, lens, got, *, lam, S, what):
+def _compare(q, kk, vv, lens, got, *, lam, S, what, window=0):
     """Whole-call parity: GPU results ``got`` = (o, skip, gap, counters)
     against the oracle over the float64 caches kk, vv [B, Hkv, Lmax, *]."""
     o, skip, gap, cnt = got
-    ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S)
+    ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S, window=window)
     nb = check_decisions(skip.cpu().numpy(), gap.cpu().numpy(), ref["skip"], ref["gap"], lam)
     check_output(o.cpu().numpy(), ref["o"], what)
     gs = skip.cpu().numpy()
@@ -232,3 +232,44 @@ def test_paged_gqa_decode_148_sequences_equals_contiguous():
     say(f"[paged] 148x32/8x32768x128 page=64 splits={S} lam={lam:.4g}")
     got = gpu_decode_paged(q, kp, vp, table, lens, 32768, lam=lam)
     _equal_calls(got, gpu_decode(q, kc, vc, lens, lam=lam, num_splits=S))
+
+
+# ------------------------------------------------------------ sliding window
+@pytest.mark.parametrize("W", [1, 64, 200, 777])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_window_gqa_decode(W, splits):
+    q, kc, vc, _ = inputs.decode_inputs(3, 8, 2, 1000, 128, device=DEV, seed=80 + W + splits)
+    lens = torch.tensor([1000, 1, 333], dtype=torch.int32, device=DEV)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=splits, window=W)
+    lam, _ = lambda_for(gap0, 0.5)
+    say(f"[decode] window {W} splits {splits} lam {lam:.4g}")
+    got = gpu_decode(q, kc, vc, lens, lam=lam, num_splits=splits, window=W)
+    _compare(q, f64(kc), f64(vc), lens, got, lam=lam, S=splits, what=f"gqa window {W}", window=W)
+
+
+@pytest.mark.parametrize("W,splits", [(100, 2), (1000, 1), (65, 5)])
+def test_window_mla_decode(W, splits):
+    q, kc, lens = _mla(3, 2000, seed=90 + W, lens=[2000, 1, 777])
+    _, _, gap0, _ = gpu_decode(q, kc, kc, lens, lam=0.0, num_splits=splits, dv=512, window=W)
+    lam, _ = lambda_for(gap0, 0.5)
+    say(f"[decode] mla window {W} splits {splits} lam {lam:.4g}")
+    got = gpu_decode(q, kc, kc, lens, lam=lam, num_splits=splits, dv=512, window=W)
+    kk = f64(kc)
+    _compare(q, kk, kk[..., :512], lens, got, lam=lam, S=splits, what=f"mla window {W}", window=W)
+
+
+def test_window_paged_decode_ignores_pages_outside_the_window():
+    """A paged cache whose pages below the window hold NaN (freed pages of a
+    sliding-window server) gives the contiguous result bit for bit."""
+    q, kc, vc, _ = inputs.decode_inputs(2, 8, 2, 2048, 128, device=DEV, seed=95)
+    lens = torch.tensor([2048, 1500], dtype=torch.int32, device=DEV)
+    W, P = 300, 16
+    (kp, vp), table = inputs.paged_pool([kc, vc], lens, P, seed=3, spare_pages=2)
+    for b, n in enumerate(lens.tolist()):
+        dead = table[b, :max(0, n - W) // P].long()  # pages wholly below the window
+        kp[dead] = float("nan")
+        vp[dead] = float("nan")
+    lam = 1e-3
+    got = gpu_decode_paged(q, kp, vp, table, lens, 2048, lam=lam, num_splits=2, window=W)
+    _equal_calls(got, gpu_decode(q, kc, vc, lens, lam=lam, num_splits=2, window=W))
+    assert torch.isfinite(got[0]).all()

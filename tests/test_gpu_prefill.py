@@ -14,11 +14,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_full(q, k, v, *, causal, lam, tile_q, what):
+def _run_full(q, k, v, *, causal, lam, tile_q, what, window=0):
     """GPU vs oracle over every unit."""
-    say(f"[prefill] {what}: q{tuple(q.shape)} k{tuple(k.shape)} causal={causal} lam={lam:.4g} tile={tile_q}")
-    o, skip, gap, cnt = gpu_prefill(q, k, v, causal=causal, lam=lam, tile_q=tile_q)
-    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=causal, lam=lam, tile_q=tile_q, block_k=64)
+    say(f"[prefill] {what}: q{tuple(q.shape)} k{tuple(k.shape)} causal={causal} lam={lam:.4g} tile={tile_q}"
+        f" window={window}")
+    o, skip, gap, cnt = gpu_prefill(q, k, v, causal=causal, lam=lam, tile_q=tile_q, window=window)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=causal, lam=lam, tile_q=tile_q, block_k=64,
+                         window=window)
     nb = check_decisions(skip.cpu().numpy(), gap.cpu().numpy(), ref["skip"], ref["gap"], lam)
     check_output(o.cpu().numpy(), ref["o"], what)
     assert cnt[0] == ref["visited"]
@@ -83,17 +85,17 @@ def test_strided_inputs():
     assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(g1, g2)
 
 
-def _sampled(q, k, v, *, lam, tile_q, units, what):
+def _sampled(q, k, v, *, lam, tile_q, units, what, window=0):
     """Full-size GPU run, oracle on a set of (b, h, tile) units."""
     B, Hq, L, _ = q.shape
     nqt = -(-L // tile_q)
-    say(f"[prefill] {what}: full GPU run, oracle on {len(units)} units")
-    o, skip, gap, cnt = gpu_prefill(q, k, v, causal=True, lam=lam, tile_q=tile_q)
+    say(f"[prefill] {what}: full GPU run, oracle on {len(units)} units (window {window})")
+    o, skip, gap, cnt = gpu_prefill(q, k, v, causal=True, lam=lam, tile_q=tile_q, window=window)
     mask = np.zeros((B, Hq, nqt), np.uint8)
     for (b, h, t) in units:
         mask[b, h, t] = 1
     ref = oracle.prefill(f64(q), f64(k), f64(v), causal=True, lam=lam, tile_q=tile_q, block_k=64,
-                         unit_mask=mask)
+                         unit_mask=mask, window=window)
     sel = mask.astype(bool)
     check_decisions(skip.cpu().numpy()[sel], gap.cpu().numpy()[sel], ref["skip"][sel], ref["gap"][sel], lam)
     rows = np.zeros((B, Hq, L), bool)
@@ -130,4 +132,36 @@ def test_parity_long_prefill_32k_sampled():
     say(f"  lambda for 70%: {lam:.4g} (reaches {reached:.4f})")
     units = [(1, 31, 255), (0, 0, 254), (1, 5, 128), (0, 17, 64), (1, 9, 3), (0, 30, 200)]
     cnt = _sampled(q, k, v, lam=lam, tile_q=128, units=units, what="2x32/8x32768x128")
+    assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
+
+
+# ------------------------------------------------------------ sliding window
+@pytest.mark.parametrize("W", [1, 63, 100, 257, 999])
+@pytest.mark.parametrize("d,tile_q", [(128, 128), (64, 64)])
+def test_parity_sliding_window(W, d, tile_q):
+    """Query i sees keys i-W < c <= i; lambda at the 60% quantile of the windowed gaps."""
+    q, k, v = inputs.prefill_inputs(2, 4, 2, 1000, d, device=DEV, seed=20 + W + d)
+    _, _, gap0, _ = gpu_prefill(q, k, v, causal=True, lam=0.0, tile_q=tile_q, window=W)
+    lam, _ = lambda_for(gap0, 0.6)
+    _run_full(q, k, v, causal=True, lam=lam, tile_q=tile_q, what=f"window {W} d={d} tile={tile_q}", window=W)
+
+
+def test_sliding_window_dense_and_covering_window():
+    q, k, v = inputs.prefill_inputs(1, 4, 1, 1500, 128, device=DEV, seed=21)
+    ref = _run_full(q, k, v, causal=True, lam=0.0, tile_q=128, what="window 300 dense", window=300)
+    assert ref["skipped"] == 0
+    # a window covering the sequence is plain causal attention, bit for bit
+    a = gpu_prefill(q, k, v, causal=True, lam=1e-3, tile_q=128)
+    b = gpu_prefill(q, k, v, causal=True, lam=1e-3, tile_q=128, window=1500)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+
+
+def test_parity_sliding_window_8k_sampled():
+    """1x32/8x8192x128, window 2048, lambda for 70% of the windowed pairs."""
+    q, k, v = inputs.prefill_inputs(1, 32, 8, 8192, 128, n_random=6, local_window=1, device=DEV, seed=1001)
+    _, _, gap0, _ = gpu_prefill(q, k, v, causal=True, lam=0.0, tile_q=128, window=2048)
+    lam, reached = lambda_for(gap0, 0.7)
+    units = [(0, 3, 63), (0, 31, 40), (0, 8, 16), (0, 20, 15), (0, 0, 1), (0, 12, 0)]
+    cnt = _sampled(q, k, v, lam=lam, tile_q=128, units=units, what="window 2048, 1x32/8x8192x128", window=2048)
     assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
