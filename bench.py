@@ -13,13 +13,14 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
     d=128, bf16 cache, block 64) at the 70% and 50% lambdas and lambda = 0:
     microseconds per decode step and HBM GB/s on the bytes actually loaded;
     then the same step over a paged cache (64-row pages of a shuffled pool;
-    likewise for the latent decode below);
+    likewise for the latent decode below) and with a 4096-key sliding window;
   * the latent (MLA) decode workload (16 sequences, 128 query heads sharing one
     576-wide latent KV head, V = its first 512 columns, 65536 cached tokens)
     at the 70% lambda and lambda = 0: microseconds per step, GB/s on the
     loaded bytes and MFMA utilisation (the workload sits near the ridge);
   * the long causal prefill (B=2, Hq=32, Hkv=8, L=32768, d=128) over the
-    target sparsities 30/50/70/80% and dense;
+    target sparsities 30/50/70/80% and dense, and with a 4096-key sliding
+    window at 70% and dense;
   * the calibration law lambda = a/L: a fitted on calibration inputs at
     L = 4K..32K, then the sparsity lambda = a/L achieves on fresh inputs;
   * the fp64 CPU oracle on a bounded sample of the prefill workload.
@@ -122,18 +123,18 @@ def long_prefill_workload(seed=1004):
     return (B, Hq, Hkv, L, d), (q, k, v)
 
 
-def calibrate_prefill(q, k, v, targets):
+def calibrate_prefill(q, k, v, targets, window=0):
     B, Hq, L, _ = q.shape
     gap = torch.empty(B, Hq, -(-L // 128), -(-L // 64), dtype=torch.float32, device="cuda")
-    bl.blasst_prefill(q, k, v, causal=True, lam=0.0, tile_q=128, gap_map=gap)
+    bl.blasst_prefill(q, k, v, causal=True, lam=0.0, tile_q=128, gap_map=gap, window=window)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
 
-def calibrate_decode(q, kc, vc, lens, S, targets, dv=None):
+def calibrate_decode(q, kc, vc, lens, S, targets, dv=None, window=0):
     B, Hkv, L = q.shape[0], kc.shape[1], kc.shape[2]
     gap = torch.empty(B, Hkv, -(-L // 64), dtype=torch.float32, device="cuda")
-    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap, dv=dv)
+    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap, dv=dv, window=window)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
@@ -215,7 +216,7 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
     return (q, k, v, lam70), res, dense_flops
 
 
-def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=()):
+def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), window=0):
     (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
     S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -255,6 +256,28 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=()):
             vis, skp = counts(lambda c: pg(c))
             dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis}
             log(f"decode {name} (64-row pages): {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}")
+        del kp, vp, table
+    if window:
+        # The same step with a sliding window of `window` keys (its own lambda).
+        Sw, wsw = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3, window=window)
+        wwork = torch.empty(max(wsw, 1), dtype=torch.uint8, device="cuda")
+        lamw = calibrate_decode(dq, kc, vc, lens, Sw, [0.7], window=window)[0.7][0]
+        for name, lam in (("window_s70", lamw), ("window_dense", 0.0)):
+
+            def wd(cnt=None, lam=lam):
+                return bl.blasst_decode(dq, kc, vc, lens, lam=lam, num_splits=Sw, out=dout, workspace=wwork,
+                                        counters=cnt, window=window)
+
+            mean_ms, _, _ = time_calls(wd, steps, warmup)
+            vis, skp = counts(lambda c: wd(c))
+            blk = 64 * Dd * 2
+            loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
+            if Sw > 1:
+                loaded += 2 * DB * DHq * Sw * (Dd + 2) * 4
+            dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "splits": Sw,
+                          "gbps": loaded / (mean_ms * 1e-3) / 1e9}
+            log(f"decode {name} (window {window}): {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
+                f"{dres[name]['gbps']:.0f} GB/s, splits {Sw}")
     return S, dres
 
 
@@ -322,7 +345,33 @@ def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8)):
     dense_ms = rows[-1]["ms"]
     for r in rows:
         r["speedup_vs_dense"] = dense_ms / r["ms"]
-    return rows
+    return rows, window_prefill(q, k, v, out, 4096, steps, warmup)
+
+
+def window_prefill(q, k, v, out, W, steps, warmup):
+    """The same prefill with a sliding window of W keys, at the 70% lambda of
+    the windowed gaps and at lambda = 0."""
+    B, Hq, L, d = q.shape
+    lam70, _ = calibrate_prefill(q, k, v, [0.7], window=W)[0.7]
+    # dense-equivalent work of windowed attention: row i sees min(i+1, W) keys
+    keys = W * (W + 1) // 2 + (L - W) * W if L > W else L * (L + 1) // 2
+    dense_flops = 4.0 * B * Hq * d * keys
+
+    def pf(lam, cnt=None):
+        return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt,
+                                         window=W)
+
+    res = {"window": W, "dense_equiv_flops": dense_flops}
+    for name, lam in (("s70", lam70), ("dense", 0.0)):
+        mean_ms, _, _ = time_calls(pf(lam), steps, warmup)
+        vis, skp = counts(lambda c: pf(lam, c)())
+        mfma = (vis + (vis - skp)) * 2.0 * 128 * 64 * d
+        res[name] = {"lambda": lam, "ms": mean_ms, "sparsity": skp / vis,
+                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12,
+                     "mfma_util_executed": mfma / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        log(f"windowed prefill W={W} {name}: {mean_ms:.3f} ms, sparsity {skp / vis:.4f}")
+    res["speedup70_vs_dense"] = res["dense"]["ms"] / res["s70"]["ms"]
+    return res
 
 
 def bench_calibration(lengths=(4096, 8192, 16384, 32768), targets=(0.5, 0.7)):
@@ -428,7 +477,7 @@ def main():
     # ------------------------------------------------------------- decode
     decode = mla = long_prefill = None
     if not args.no_decode:
-        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"))
+        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"), window=4096)
         decode = {
             "workload": "GQA decode B=148 Hq=32 Hkv=8 L=32768 d=128 bf16, block 64, one query token per sequence",
             "num_splits": S,
@@ -445,6 +494,11 @@ def main():
                       "us_per_step_dense": dres["paged_dense"]["us"],
                       "overhead70_vs_contiguous": dres["paged_s70"]["us"] / dres["s70"]["us"] - 1.0,
                       "overhead_dense_vs_contiguous": dres["paged_dense"]["us"] / dres["dense"]["us"] - 1.0},
+            "window": {"window": 4096, "num_splits": dres["window_s70"]["splits"],
+                       "us_per_step70": dres["window_s70"]["us"], "sparsity70": dres["window_s70"]["sparsity"],
+                       "us_per_step_dense": dres["window_dense"]["us"],
+                       "speedup70_vs_dense": dres["window_dense"]["us"] / dres["window_s70"]["us"],
+                       "hbm_gbps70": dres["window_s70"]["gbps"], "hbm_gbps_dense": dres["window_dense"]["gbps"]},
         }
         torch.cuda.empty_cache()
         S, mres = bench_mla(steps, warmup, paged_names=("paged_s70", "paged_dense"))
@@ -469,9 +523,11 @@ def main():
                       "overhead_dense_vs_contiguous": mres["paged_dense"]["us"] / mres["dense"]["us"] - 1.0},
         }
         torch.cuda.empty_cache()
+        sweep, wres = bench_long_prefill(max(2, steps // 4), max(1, warmup // 2))
         long_prefill = {
             "workload": "GQA causal prefill B=2 Hq=32 Hkv=8 L=32768 d=128 bf16, query tile 128, key block 64",
-            "sweep": bench_long_prefill(max(2, steps // 4), max(1, warmup // 2)),
+            "sweep": sweep,
+            "window": wres,
         }
         torch.cuda.empty_cache()
 
