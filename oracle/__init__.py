@@ -32,7 +32,7 @@ def _declare(lib):
         _dp, _u8p, _dp, _i64p, ctypes.c_int]
     lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_i64] * 6 + [_dp] * 3 + [
-        _i32p, ctypes.c_double, ctypes.c_double, _i64, _i64, _i64, _u8p,
+        _i32p, ctypes.c_double, ctypes.c_double, _i64, _i64, _i64, ctypes.c_int, _u8p,
         _dp, _u8p, _dp, _i64p, ctypes.c_int]
     lib.oracle_lambda_for_target.restype = ctypes.c_double
     lib.oracle_lambda_for_target.argtypes = [_dp, _i64, ctypes.c_double, _dp]
@@ -114,11 +114,13 @@ def prefill(q, k, v, causal=True, scale=None, lam=0.0, tile_q=64, block_k=64,
 
 
 def decode(q, k, v, seq_lens, scale=None, lam=0.0, block_k=64, num_splits=1,
-           unit_mask=None, nthreads=0, want_maps=True, window=0):
+           unit_mask=None, nthreads=0, want_maps=True, window=0, sink_seed=False):
     """Blockwise skip attention, decode form (one query token per sequence).
 
     ``window`` > 0: the query (at position seq_len-1) sees the last ``window``
     keys; the splits cut the blocks from the first one holding such a key.
+    ``sink_seed``: splits after the first start their running max from the
+    row maxima of the first visible block instead of -inf.
 
     q [B,Hq,dqk], k [B,Hkv,Lmax,dqk], v [B,Hkv,Lmax,dv], seq_lens int [B].
     Returns ``o`` [B,Hq,dv], ``skip``/``gap`` [B,Hkv,nKB], ``visited``,
@@ -139,6 +141,7 @@ def decode(q, k, v, seq_lens, scale=None, lam=0.0, block_k=64, num_splits=1,
     cnt = np.zeros(2, np.int64)
     rc = lib.oracle_decode(B, Hq, Hkv, Lmax, dqk, dv, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp),
                            _ptr(sl, _i32p), float(scale), float(lam), block_k, int(num_splits), int(window),
+                           int(bool(sink_seed)),
                            _ptr(um, _u8p), _ptr(o, _dp), _ptr(skip, _u8p), _ptr(gap, _dp),
                            _ptr(cnt, _i64p), int(nthreads))
     if rc != 0:

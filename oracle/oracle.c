@@ -48,7 +48,17 @@
  *    rest.  In decode the query is at position len-1, so it sees the last W
  *    keys, and the splits cut the blocks from the first block that holds a
  *    visible key: split s covers [j0 + s*ceil((nkb - j0)/S), ...), j0 =
- *    max(0, len - W) div block_k.
+ *    max(0, len - W) div block_k;
+ *  - sink-seeded splits (optional, decode): split s >= 1 starts its running
+ *    max from the row maxima of the sequence's first visible block (block j0,
+ *    the sink block 0 without a window) instead of -inf.  This borrows the
+ *    pseudo-maximum of the FFD summary (gist.science/pt/paper/2609.00097,
+ *    section 2 "A Estratégia de Seleção Top-δ"), estimated there from sink
+ *    and local tokens; here from the sink block alone.  The seed is a real score of a
+ *    visible key, so the running max stays below the true row max and the
+ *    skip test keeps its meaning; a split may then skip every block (l = 0)
+ *    and the merge ignores it.  Split 0 is unseeded (its first block is
+ *    always executed).
  *
  * Arithmetic is IEEE fp64 with libm exp/log, loops in the order written.
  * Inputs are fp64 arrays (the tests pass the exact bf16 values the GPU reads).
@@ -78,6 +88,7 @@ static double oracle_ln_lambda(double lambda)
  *   window : > 0: key c also needs c > qpos[r] - window (sliding window)
  *   k, v   : [klen_alloc][d] and [klen_alloc][dv], contiguous
  *   klen   : keys with index >= klen are masked
+ *   seed   : initial running max per row, or NULL for -inf
  *   m,l,acc: outputs, the unit's final running max, sum and accumulator
  *   skip   : per visited block 0 executed / 1 skipped / 255 not visited
  *   gap    : per block g(unit, j), -inf when not visited
@@ -87,14 +98,14 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
                         const double *q, int64_t q_stride, const int64_t *qpos, int64_t window,
                         const double *k, const double *v, int64_t klen,
                         int64_t j_begin, int64_t j_end, int64_t bc,
-                        double scale, double lnlam,
+                        double scale, double lnlam, const double *seed,
                         double *m, double *l, double *acc,
                         uint8_t *skip, double *gap, double *S, double *mt,
                         int64_t *visited_out, int64_t *skipped_out)
 {
     int64_t visited = 0, skipped = 0;
     for (int64_t r = 0; r < R; ++r) {
-        m[r] = -INFINITY;
+        m[r] = seed ? seed[r] : -INFINITY;
         l[r] = 0.0;
         for (int64_t x = 0; x < dv; ++x)
             acc[r * dv + x] = 0.0;
@@ -241,7 +252,7 @@ int oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int
                 const double *vb = v + (b * Hkv + hk) * L * dv;
                 int64_t vis = 0, skp = 0;
                 oracle_unit(R, d, dv, qb, d, causal ? qpos : NULL, window, kb, vb, L, 0, nkb, block_k,
-                            scale, lnlam, m, l, acc, sk, gp, S, mt, &vis, &skp);
+                            scale, lnlam, NULL, m, l, acc, sk, gp, S, mt, &vis, &skp);
                 tot_visited += vis;
                 tot_skipped += skp;
                 double *ob = o + ((b * Hq + h) * L + r0) * dv;
@@ -273,13 +284,14 @@ int oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int
  *   seq_lens [B] in 1..Lmax; keys >= seq_lens[b] are masked
  *   num_splits >= 1: contiguous block runs, each from m = -inf, merged by LSE
  *   window > 0: the query (position len-1) sees the last `window` keys only
+ *   sink_seed != 0: splits s >= 1 start from the row maxima of block j0
  *   unit_mask [B][Hkv] or NULL
  *   o [B][Hq][dv]; skip_map / gap_map [B][Hkv][nKB], nKB = ceil(Lmax/block_k)
  */
 int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk, int64_t dv,
                   const double *q, const double *k, const double *v, const int32_t *seq_lens,
                   double scale, double lambda, int64_t block_k, int64_t num_splits, int64_t window,
-                  const uint8_t *unit_mask, double *o, uint8_t *skip_map, double *gap_map,
+                  int sink_seed, const uint8_t *unit_mask, double *o, uint8_t *skip_map, double *gap_map,
                   int64_t *counters, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || dqk <= 0 || dv <= 0 || block_k <= 0 ||
@@ -307,7 +319,8 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
         uint8_t *sk = malloc(nkb);
         double *gp = malloc(sizeof(double) * nkb);
         int64_t *qpos = malloc(sizeof(int64_t) * G);
-        if (!S || !mt || !ms || !ls || !accs || !sk || !gp || !qpos) {
+        double *seed = malloc(sizeof(double) * G);
+        if (!S || !mt || !ms || !ls || !accs || !sk || !gp || !qpos || !seed) {
 #pragma omp atomic write
             err = ORACLE_ENOMEM;
         } else {
@@ -329,6 +342,19 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                     sk[j] = 255;
                     gp[j] = -INFINITY;
                 }
+                /* Seed: row max of the scaled scores over the visible keys of block j0. */
+                for (int64_t r = 0; r < G; ++r) {
+                    seed[r] = -INFINITY;
+                    for (int64_t key = j0 * block_k; key < (j0 + 1) * block_k && key < len; ++key) {
+                        if (window > 0 && key <= len - 1 - window)
+                            continue;
+                        double dot = 0.0;
+                        for (int64_t x = 0; x < dqk; ++x)
+                            dot += qb[r * dqk + x] * kb[key * dqk + x];
+                        if (scale * dot > seed[r])
+                            seed[r] = scale * dot;
+                    }
+                }
                 for (int64_t s = 0; s < num_splits; ++s) {
                     int64_t jb = j0 + s * per, je = j0 + (s + 1) * per;
                     if (je > nkb_b)
@@ -343,7 +369,7 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                     }
                     int64_t vis = 0, skp = 0;
                     oracle_unit(G, dqk, dv, qb, dqk, window > 0 ? qpos : NULL, window, kb, vb, len, jb, je, block_k, scale,
-                                lnlam, m, l, acc, sk + jb, gp + jb, S, mt, &vis, &skp);
+                                lnlam, (sink_seed && s > 0) ? seed : NULL, m, l, acc, sk + jb, gp + jb, S, mt, &vis, &skp);
                     tot_visited += vis;
                     tot_skipped += skp;
                 }
@@ -375,7 +401,7 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                     memcpy(gap_map + u * nkb, gp, sizeof(double) * nkb);
             }
         }
-        free(S); free(mt); free(ms); free(ls); free(accs); free(sk); free(gp); free(qpos);
+        free(S); free(mt); free(ms); free(ls); free(accs); free(sk); free(gp); free(qpos); free(seed);
     }
     if (counters) {
         counters[0] = tot_visited;

@@ -46,16 +46,17 @@ def dense_probs(S, mask):
     return p / p.sum(axis=1, keepdims=True)
 
 
-def block_decisions(S, mask, rows_of_unit, block_cols, lam):
+def block_decisions(S, mask, rows_of_unit, block_cols, lam, init=None):
     """Decisions of one unit by the closed form of the running max.
 
     S, mask: [R_all, N] for the unit's rows (already selected); block_cols:
-    list of column ranges, in visiting order.  Returns (skip list, gap list)
-    with 255 / -inf for unvisited blocks.
+    list of column ranges, in visiting order; init: per-row running max before
+    the first block (default -inf).  Returns (skip list, gap list) with 255 /
+    -inf for unvisited blocks.
     """
     lnlam = -math.inf if lam == 0 else math.log(lam)
     R = S.shape[0]
-    prev_max = np.full(R, -np.inf)
+    prev_max = np.full(R, -np.inf) if init is None else np.array(init, dtype=np.float64)
     skips, gaps = [], []
     for (c0, c1) in block_cols:
         m_blk = mask[:, c0:c1]

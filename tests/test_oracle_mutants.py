@@ -32,6 +32,11 @@ MUTANTS = [
     ("split length floor", "int64_t per = (nkb_b - j0 + num_splits - 1) / num_splits;",
      "int64_t per = (nkb_b - j0) / num_splits > 0 ? (nkb_b - j0) / num_splits : 1;"),
     ("window edge off by one", "key > qpos[r] - window", "key >= qpos[r] - window"),
+    ("seed on the first split too", "(sink_seed && s > 0) ? seed : NULL", "sink_seed ? seed : NULL"),
+    ("seed from the block after the first",
+     "key = j0 * block_k; key < (j0 + 1) * block_k && key < len", "key = (j0 + 1) * block_k; key < (j0 + 2) * block_k && key < len"),
+    ("seed without the scale", "if (scale * dot > seed[r])\n                            seed[r] = scale * dot;",
+     "if (dot > seed[r])\n                            seed[r] = dot;"),
     ("decode splits ignore the window", "int64_t j0 = (window > 0 && len > window) ? (len - window) / block_k : 0;",
      "int64_t j0 = 0;"),
     ("merge weight sign", "double w = exp(ms[s * G + r] - M);", "double w = exp(M - ms[s * G + r]);"),

@@ -528,3 +528,124 @@ def test_window_decode_decisions_and_split_origin(seed):
             for hh in range(G):
                 ref = masked_softmax_attention(S[hh:hh + 1], (mask[hh] & ex)[None], v[b, g])[0]
                 np.testing.assert_allclose(r["o"][b, g * G + hh], ref, rtol=0, atol=1e-10)
+
+
+# -------------------------------------------------------- sink-seeded splits
+# Reading: split s >= 1 starts its running max from the row maxima of the
+# sequence's first visible block; split 0 starts from -inf.
+
+def _seed_case(seed, Lmax=400, bk=16, W=0):
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, d, dv = 2, 4, 2, 8, 6
+    q = _rand(rng, B, Hq, d, std=2.0)
+    k = _rand(rng, B, Hkv, Lmax, d, std=2.0)
+    f = rng.uniform(0.05, 1.0, size=(B, Hkv, -(-Lmax // bk)))
+    f[..., 0] = 2.5  # a hot sink block
+    k = k * np.repeat(f, bk, axis=2)[..., :Lmax, None]
+    v = _rand(rng, B, Hkv, Lmax, dv)
+    lens = np.array([Lmax, int(rng.integers(Lmax // 2, Lmax))])
+    return q, k, v, lens
+
+
+@pytest.mark.parametrize("seed,W", [(0, 0), (1, 0), (2, 0), (3, 150), (4, 0), (5, 90)])
+def test_sink_seed_decisions_and_output(seed, W):
+    """Decisions by the closed form with the seeded running max, and the
+    merged output equal to softmax over the executed keys."""
+    q, k, v, lens = _seed_case(800 + seed, W=W)
+    bk, splits = 16, 4
+    B, Hq, dd = q.shape
+    Hkv, Lmax = k.shape[1], k.shape[2]
+    G, scale, nkb = Hq // Hkv, 1 / math.sqrt(dd), -(-Lmax // bk)
+    g0 = oracle.decode(q, k, v, lens, lam=0.0, block_k=bk, num_splits=splits, window=W, sink_seed=True)["gap"]
+    lam = _lam_at(g0, 0.5)
+    r = oracle.decode(q, k, v, lens, lam=lam, block_k=bk, num_splits=splits, window=W, sink_seed=True)
+    keys = np.arange(Lmax)
+    seeded_first_skips = 0
+    for b in range(B):
+        n = int(lens[b])
+        lo = max(0, n - W) if W else 0
+        j0 = lo // bk
+        nkb_b = -(-n // bk)
+        per = -(-(nkb_b - j0) // splits)
+        for g in range(Hkv):
+            S = scores(q[b, g * G:(g + 1) * G], k[b, g], scale)
+            vis = (keys < n) & (keys >= lo)
+            mask = np.broadcast_to(vis, S.shape)
+            blk0 = slice(j0 * bk, (j0 + 1) * bk)
+            seed_max = np.where(mask[:, blk0], S[:, blk0], -np.inf).max(axis=1)
+            exp_skip, exp_gap = [255] * nkb, [-math.inf] * nkb
+            for s in range(splits):
+                jb, je = j0 + s * per, min(nkb_b, j0 + (s + 1) * per)
+                if jb >= je:
+                    continue
+                cols = [(j * bk, min(Lmax, (j + 1) * bk)) for j in range(jb, je)]
+                init = seed_max if s > 0 else None
+                exp_skip[jb:je], exp_gap[jb:je] = block_decisions(S, mask, None, cols, lam, init=init)
+                if s > 0 and exp_skip[jb] == 1:
+                    seeded_first_skips += 1
+            exp_gap = np.array(exp_gap)
+            fin = np.isfinite(exp_gap)
+            np.testing.assert_allclose(r["gap"][b, g][fin], exp_gap[fin], rtol=0, atol=1e-9)
+            assert np.array_equal(r["gap"][b, g][~fin], exp_gap[~fin])
+            near = np.abs(exp_gap - math.log(lam)) < 1e-9
+            assert np.array_equal(r["skip"][b, g][~near], np.array(exp_skip, np.uint8)[~near])
+            ex = np.repeat(r["skip"][b, g] == 0, bk)[:Lmax]
+            for hh in range(G):
+                ref = masked_softmax_attention(S[hh:hh + 1], (vis & ex)[None], v[b, g])[0]
+                np.testing.assert_allclose(r["o"][b, g * G + hh], ref, rtol=0, atol=1e-10)
+    assert seeded_first_skips > 0  # the seed does let a split skip its first block
+
+
+def test_sink_seed_with_one_split_changes_nothing():
+    q, k, v, lens = _seed_case(810)
+    a = oracle.decode(q, k, v, lens, lam=0.05, block_k=16, num_splits=1)
+    b = oracle.decode(q, k, v, lens, lam=0.05, block_k=16, num_splits=1, sink_seed=True)
+    for key in ("o", "skip", "gap"):
+        assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sink_seed_skips_a_superset_and_keeps_the_mass_bound(seed):
+    """The seed only raises the running max: gaps shrink, the skip set grows,
+    and the dropped dense-softmax mass stays below lambda per skipped key."""
+    q, k, v, lens = _seed_case(820 + seed)
+    lam = 0.02
+    a = oracle.decode(q, k, v, lens, lam=lam, block_k=16, num_splits=5)
+    b = oracle.decode(q, k, v, lens, lam=lam, block_k=16, num_splits=5, sink_seed=True)
+    vis = a["skip"] != 255
+    assert np.array_equal(vis, b["skip"] != 255)
+    assert np.all(b["gap"][vis] <= a["gap"][vis])
+    assert np.all(b["skip"][a["skip"] == 1] == 1)
+    assert b["skipped"] > a["skipped"]
+    B, Hq, dd = q.shape
+    G, scale, Lmax = Hq // k.shape[1], 1 / math.sqrt(dd), k.shape[2]
+    for bb in range(B):
+        n = int(lens[bb])
+        for h in range(Hq):
+            S = scores(q[bb, h][None], k[bb, h // G], scale)[0, :n]
+            p = np.exp(S - S.max())
+            p /= p.sum()
+            sk = np.repeat(b["skip"][bb, h // G] == 1, 16)[:n]
+            assert p[sk].sum() < lam * max(1, sk.sum())
+
+
+def test_sink_seed_fully_skipped_split_contributes_nothing():
+    """A split whose blocks are all far colder than the sink skips everything
+    (l = 0); the merge ignores it and O is softmax over the executed keys."""
+    rng = np.random.default_rng(830)
+    Lmax, d, dv, bk = 256, 8, 4, 16
+    q = np.ones((1, 1, d))
+    k = np.zeros((1, 1, Lmax, d))
+    k[0, 0, :bk] = 3.0                        # sink: score 3*8/sqrt(8)
+    k[0, 0, bk:] = rng.standard_normal((Lmax - bk, d)) * 0.01
+    k[0, 0, 192:] = 2.9                       # last split: scores 0.3 below the sink, executed
+    v = rng.standard_normal((1, 1, Lmax, dv))
+    lam = 0.05
+    r = oracle.decode(q, k, v, np.array([Lmax]), lam=lam, block_k=bk, num_splits=4, sink_seed=True)
+    sk = r["skip"][0, 0]
+    assert np.all(sk[4:12] == 1)              # splits 1 and 2: every block skipped
+    assert sk[0] == 0 and np.all(sk[12:] == 0)
+    S = scores(q[0], k[0, 0], 1 / math.sqrt(d))
+    ex = np.repeat(sk == 0, bk)
+    ref = masked_softmax_attention(S, ex[None], v[0, 0])[0]
+    np.testing.assert_allclose(r["o"][0, 0], ref, rtol=0, atol=1e-12)
