@@ -139,6 +139,16 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream);
  *             then cut the blocks from the first one holding such a key,
  *             j0 = max(0, seq_len - W) / 64, into runs of
  *             ceil((nkb - j0) / num_splits) blocks.
+ *   sink_seed: 0 = every split starts its running max from -inf.  Nonzero:
+ *             splits after the first start it from the row maxima of the
+ *             sequence's first visible block (block j0; the sink block 0
+ *             without a window), so a cold split may skip even its first
+ *             blocks, or all of them.  This applies the pseudo-maximum of
+ *             the FFD summary (gist.science/pt/paper/2609.00097, section 2,
+ *             top-delta selection: a max estimated from sink and local
+ *             tokens) to the split start.  The seed is a real score of a
+ *             visible key, so the skip test keeps its bound on the dropped
+ *             mass.  It costs one extra block of scores per seeded split.
  */
 typedef struct {
     blasst_tensor q, k_cache, v_cache, o;
@@ -152,6 +162,7 @@ typedef struct {
     float *gap_map;
     unsigned long long *counters;
     int64_t window;
+    int sink_seed;
 } blasst_decode_params;
 
 /* Host-only: the split count a call with *p will use and the device workspace

@@ -50,7 +50,7 @@ class _DecodeParams(ctypes.Structure):
                 ("scale", ctypes.c_double), ("lam", ctypes.c_double),
                 ("block_k", ctypes.c_int), ("num_splits", ctypes.c_int),
                 ("skip_map", ctypes.c_void_p), ("gap_map", ctypes.c_void_p),
-                ("counters", ctypes.c_void_p), ("window", ctypes.c_int64)]
+                ("counters", ctypes.c_void_p), ("window", ctypes.c_int64), ("sink_seed", ctypes.c_int)]
 
 
 class _DecodePagedParams(ctypes.Structure):
@@ -175,14 +175,15 @@ def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, sca
 
 
 def _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
-                   skip_map, gap_map, counters, window=0):
+                   skip_map, gap_map, counters, window=0, sink_seed=False):
     B, Hq, dqk = q.shape
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
     dv = out.shape[2] if out is not None else (v_cache.shape[3] if v_cache is not None else dqk)
     return _DecodeParams(_tensor(q, True), _tensor(k_cache), _tensor(v_cache), _tensor(out, True),
                          _ptr(seq_lens), B, Hq, Hkv, Lmax, dqk, dv,
                          float(scale) if scale is not None else 0.0, float(lam), int(block_k),
-                         int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
+                         int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window),
+                         int(bool(sink_seed)))
 
 
 def blasst_decode_plan(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
@@ -203,10 +204,12 @@ def blasst_decode_plan(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, bl
 
 def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
                   dv=None, out=None, out_dtype=torch.float32, workspace=None, skip_map=None,
-                  gap_map=None, counters=None, stream=None, window=0):
+                  gap_map=None, counters=None, stream=None, window=0, sink_seed=False):
     """Block-skipping decode: q [B,Hq,dqk], caches [B,Hkv,Lmax,*] (bf16, device), seq_lens int32 [B].
 
     ``window`` > 0: sliding window, the query sees the last ``window`` keys.
+    ``sink_seed``: splits after the first start their running max from the
+    row maxima of the first visible block.
 
     For the latent (MLA) form pass ``v_cache = k_cache`` and ``dv=512``.
     ``workspace`` (uint8 device tensor) is allocated here when not given.
@@ -217,7 +220,7 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
     if out is None:
         out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
     p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
-                       skip_map, gap_map, counters, window)
+                       skip_map, gap_map, counters, window, sink_seed)
     lib = load_library()
     if workspace is None:
         ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
@@ -229,14 +232,15 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
 
 
 def _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits, o,
-                  skip_map, gap_map, counters, window=0):
+                  skip_map, gap_map, counters, window=0, sink_seed=False):
     B, Hq, dqk = q.shape
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
         raise ValueError("page_table must be an int32 [B, pages_per_seq] tensor with unit column stride")
     d = _DecodeParams(_tensor(q, True), _tensor(k_pages), _tensor(v_pages), o,
                       _ptr(seq_lens), B, Hq, k_pages.shape[1], int(Lmax), dqk, 0,
                       float(scale) if scale is not None else 0.0, float(lam), int(block_k),
-                      int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
+                      int(num_splits), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window),
+                      int(bool(sink_seed)))
     return _DecodePagedParams(d, page_table.data_ptr(), page_table.stride(0), k_pages.shape[0],
                               k_pages.shape[2])
 
@@ -259,7 +263,7 @@ def blasst_decode_paged_plan(q, k_pages, v_pages, page_table, seq_lens, Lmax, *,
 
 def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=0.0, scale=None, block_k=64,
                         num_splits=0, dv=None, out=None, out_dtype=torch.float32, workspace=None, skip_map=None,
-                        gap_map=None, counters=None, stream=None, window=0):
+                        gap_map=None, counters=None, stream=None, window=0, sink_seed=False):
     """Block-skipping decode over a paged cache.
 
     q [B,Hq,dqk]; k_pages [num_pages,Hkv,page_size,dqk] and v_pages
@@ -274,7 +278,7 @@ def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=
     if out is None:
         out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
     p = _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits,
-                      _tensor(out, True), skip_map, gap_map, counters, window)
+                      _tensor(out, True), skip_map, gap_map, counters, window, sink_seed)
     p.d.dv = dv
     lib = load_library()
     if workspace is None:

@@ -312,6 +312,7 @@ blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_page
     a.gap_map = p->gap_map;
     a.counters = p->counters;
     a.win = window_arg(p->window, p->Lmax);
+    a.sink_seed = p->sink_seed != 0;
     if (pg) {
         a.page_table = pg->page_table;
         a.pt_stride = pg->page_table_stride;

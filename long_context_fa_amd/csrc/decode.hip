@@ -166,6 +166,34 @@ void decode_gqa_kernel(const DecodeArgs a)
     // Page ids (paged cache): pc for this batch's block (its V copy), pn for
     // the next batch's (its K loads); idv is the vector load in flight.
     int pc[4] = {0, 0, 0, 0}, pn[4] = {0, 0, 0, 0}, idv = 0;
+
+    // Sink seed (splits after the first): the decisions' prefix max starts
+    // from the row maxima of block j0 instead of -inf.  Every wave scores
+    // the block itself (the rows of its K land in L2 once).
+    if (a.sink_seed && s > 0 && jb < je) {
+        ids_take(ids_load(j0), pc);
+        load_k(j0, pc);
+        f32x4 sc[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            sc[kt] = f32x4{};
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+                sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
+        }
+        float mt = neg_inf();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = j0 * BC + 16 * kt + 4 * grp + r;
+                if (key < len && key >= klo)
+                    mt = fmaxf(mt, sc[kt][r]);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        pmax = mt * a.scale_log2;
+    }
     if (jb < je) {
         ids_take(ids_load(jb + w), pc);
         load_k(jb + w, pc);

@@ -32,6 +32,7 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     int B, Hq, Hkv, G, Lmax, nkb, num_splits;
     int win; // sliding window: the query sees the last win keys (2^30 when there is none)
+    int sink_seed; // splits s >= 1 start the running max from the row maxima of block j0
     float scale_log2;
     float lnlam2;
     float *part_o;  // [B][Hkv][S][G][dv] fp32 (num_splits > 1)

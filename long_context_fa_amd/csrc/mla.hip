@@ -119,10 +119,9 @@ void decode_mla_kernel(const DecodeArgs a)
     // chunk (l%8) ^ swzr(row)).  Rows outside klo .. len-1 re-read the nearest
     // row inside (finite data, masked later).  Offsets are 32-bit from the sequence (or page)
     // base gb = group_base(j) (the host checks rows * row stride).
-    auto tile = [&](int j) { return smem + (j & 1) * TB; };
+    auto tile = [&](int it) { return smem + (it & 1) * TB; };
     const uint32_t rowb = (uint32_t)a.k_st * 2;
-    auto copy_one = [&](const uint16_t *gb, int j, int i) {
-        char *t = tile(j);
+    auto copy_one = [&](const uint16_t *gb, int j, char *t, int i) {
         if (i < 16) {
             int key = j * BC + 16 * w + i;
             key = key < len ? (key > klo ? key : klo) : len - 1;
@@ -163,23 +162,31 @@ void decode_mla_kernel(const DecodeArgs a)
     float m2 = neg_inf(), lsum = 0.f;
     int n_skipped = 0;
 
+    // Iteration it handles block jb + it; with a sink seed (splits after the
+    // first), a leading score-only iteration it = -1 handles block j0 and
+    // sets the running max to its row maxima.  Tiles alternate by iteration.
+    const int it0 = (a.sink_seed && s > 0 && jb < je) ? -1 : 0;
     if (jb < je) {
-        const uint16_t *gb = group_base(jb);
+        const int jf = it0 < 0 ? j0 : jb;
+        const uint16_t *gb = group_base(jf);
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            copy_one(gb, jb, i);
+            copy_one(gb, jf, tile(it0), i);
         wait_vmcnt<0>();
         lds_barrier();
     }
-    for (int j = jb; j < je; ++j) {
-        const char *kb = tile(j);
+    for (int it = it0; jb + it < je; ++it) {
+        const int j = it < 0 ? j0 : jb + it;
+        const int jn = jb + it + 1; // block of the next iteration
+        const char *kb = tile(it);
         // S^T = K_j Q^T, K operands read one k-step ahead.  The copy of
-        // K_{j+1} into the other buffer (free since the last barrier) is
+        // K_jn into the other buffer (free since the last barrier) is
         // issued between the score MFMAs, one 1 KB copy every two k-steps
         // (a DMA instruction holds the wave until the address unit accepts
         // it, so a burst would stall the MFMA stream).
-        const bool dma = j + 1 < je;
-        const uint16_t *gbn = group_base(j + 1);
+        const bool dma = jn < je;
+        const uint16_t *gbn = group_base(jn);
+        char *const tn = tile(it + 1);
         f32x16 sc[2];
         // rope offsets are recomputed here (4 per block) to spare registers
         int nl = n;
@@ -203,7 +210,7 @@ void decode_mla_kernel(const DecodeArgs a)
             }
             __builtin_amdgcn_sched_barrier(0);
             if ((kk & 1) == 0 && dma)
-                copy_one(gbn, j + 1, kk >> 1);
+                copy_one(gbn, jn, tn, kk >> 1);
             if (kk == 0) {
                 mfma_v_first2(sc[0], sc[1], ka[0][0], ka[0][1], qf[0]);
             } else {
@@ -232,7 +239,13 @@ void decode_mla_kernel(const DecodeArgs a)
                 mt = fmaxf(mt, sc[kt][r]);
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mt2 = mt * a.scale_log2;
-        const int par = j & 1;
+        if (it < 0) {
+            m2 = mt2; // the seed: no vote, no P.V for this block
+            wait_vmcnt<0>();
+            lds_barrier();
+            continue;
+        }
+        const int par = it & 1;
         if (SKIP || want_maps) {
             const float dgap = mt2 == neg_inf() ? neg_inf() : mt2 - m2;
             if (SKIP) {
@@ -324,8 +337,8 @@ void decode_mla_kernel(const DecodeArgs a)
         } else {
             ++n_skipped;
         }
-        // Own part of K_{j+1} landed; after the barrier every wave is done
-        // with tile j and all of K_{j+1} is visible.
+        // Own part of K_jn landed; after the barrier every wave is done
+        // with this tile and all of K_jn is visible.
         wait_vmcnt<0>();
         lds_barrier();
     }

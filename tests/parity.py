@@ -71,12 +71,13 @@ def gpu_prefill(q, k, v, *, causal, lam, tile_q, maps=True, out_dtype=torch.floa
     gap = torch.full((B, Hq, nqt, nkb), float("nan"), dtype=torch.float32, device=q.device) if maps else None
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_prefill(q, k, v, causal=causal, lam=lam, tile_q=tile_q, skip_map=skip, gap_map=gap,
-                          counters=cnt, out_dtype=out_dtype, window=window)
+                          counters=cnt, out_dtype=out_dtype, window=window, sink_seed=sink_seed)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 
 
-def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dtype=torch.float32, window=0):
+def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dtype=torch.float32, window=0,
+               sink_seed=False):
     B = q.shape[0]
     Hkv, Lmax = kc.shape[1], kc.shape[2]
     nkb = -(-Lmax // 64)
@@ -84,13 +85,13 @@ def gpu_decode(q, kc, vc, lens, *, lam, num_splits=0, dv=None, maps=True, out_dt
     gap = torch.full((B, Hkv, nkb), float("nan"), dtype=torch.float32, device=q.device) if maps else None
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_decode(q, kc, vc, lens, lam=lam, num_splits=num_splits, dv=dv, skip_map=skip, gap_map=gap,
-                         counters=cnt, out_dtype=out_dtype, window=window)
+                         counters=cnt, out_dtype=out_dtype, window=window, sink_seed=sink_seed)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 
 
 def gpu_decode_paged(q, k_pages, v_pages, table, lens, Lmax, *, lam, num_splits=0, dv=None,
-                     out_dtype=torch.float32, window=0):
+                     out_dtype=torch.float32, window=0, sink_seed=False):
     """blasst_decode_paged with fresh skip/gap maps and counters (as gpu_decode)."""
     B, Hkv = q.shape[0], k_pages.shape[1]
     nkb = -(-Lmax // 64)
@@ -98,7 +99,8 @@ def gpu_decode_paged(q, k_pages, v_pages, table, lens, Lmax, *, lam, num_splits=
     gap = torch.full((B, Hkv, nkb), float("nan"), dtype=torch.float32, device=q.device)
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_decode_paged(q, k_pages, v_pages, table, lens, Lmax, lam=lam, num_splits=num_splits, dv=dv,
-                               skip_map=skip, gap_map=gap, counters=cnt, out_dtype=out_dtype, window=window)
+                               skip_map=skip, gap_map=gap, counters=cnt, out_dtype=out_dtype, window=window,
+                               sink_seed=sink_seed)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 

@@ -13,11 +13,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _compare(q, kk, vv, lens, got, *, lam, S, what, window=0):
+def _compare(q, kk, vv, lens, got, *, lam, S, what, window=0, sink_seed=False):
     """Whole-call parity: GPU results ``got`` = (o, skip, gap, counters)
     against the oracle over the float64 caches kk, vv [B, Hkv, Lmax, *]."""
     o, skip, gap, cnt = got
-    ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S, window=window)
+    ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S, window=window,
+                        sink_seed=sink_seed)
     nb = check_decisions(skip.cpu().numpy(), gap.cpu().numpy(), ref["skip"], ref["gap"], lam)
     check_output(o.cpu().numpy(), ref["o"], what)
     gs = skip.cpu().numpy()
@@ -29,16 +30,16 @@ def _compare(q, kk, vv, lens, got, *, lam, S, what, window=0):
     return cnt, S
 
 
-def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=False):
+def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=False, sink_seed=False):
     B, Hq, dqk = q.shape
     Hkv = kc.shape[1]
     say(f"[decode] {what}: q{tuple(q.shape)} cache{tuple(kc.shape)} lam={lam:.4g} splits={splits}")
-    o, skip, gap, cnt = gpu_decode(q, kc, vc, lens, lam=lam, num_splits=splits, dv=dv)
+    o, skip, gap, cnt = gpu_decode(q, kc, vc, lens, lam=lam, num_splits=splits, dv=dv, sink_seed=sink_seed)
     S_used, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=lam, num_splits=splits, dv=dv)
     if unit_mask is None:
         kk = f64(kc)
         vv = kk[..., :dv] if mla else f64(vc)
-        return _compare(q, kk, vv, lens, (o, skip, gap, cnt), lam=lam, S=S_used, what=what)
+        return _compare(q, kk, vv, lens, (o, skip, gap, cnt), lam=lam, S=S_used, what=what, sink_seed=sink_seed)
     # copy only the sampled sequences to the host
     bs = sorted({b for b, _ in unit_mask})
     sub = {b: i for i, b in enumerate(bs)}
@@ -48,7 +49,7 @@ def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=Fal
     for b, g in unit_mask:
         m[sub[b], g] = 1
     ref_sub = oracle.decode(f64(q[bs]), kk, vv, lens[bs].cpu().numpy(), lam=lam, block_k=64,
-                            num_splits=S_used, unit_mask=m)
+                            num_splits=S_used, unit_mask=m, sink_seed=sink_seed)
     sel_u = np.zeros((B, Hkv), bool)
     ref = {"skip": np.full(skip.shape, 255, np.uint8), "gap": np.full(gap.shape, -np.inf),
            "o": np.zeros(o.shape), "visited": ref_sub["visited"], "skipped": ref_sub["skipped"]}
@@ -273,3 +274,57 @@ def test_window_paged_decode_ignores_pages_outside_the_window():
     got = gpu_decode_paged(q, kp, vp, table, lens, 2048, lam=lam, num_splits=2, window=W)
     _equal_calls(got, gpu_decode(q, kc, vc, lens, lam=lam, num_splits=2, window=W))
     assert torch.isfinite(got[0]).all()
+
+
+# -------------------------------------------------------- sink-seeded splits
+@pytest.mark.parametrize("splits,W", [(2, 0), (5, 0), (16, 0), (3, 300)])
+def test_sink_seed_gqa_decode(splits, W):
+    q, kc, vc, _ = inputs.decode_inputs(3, 8, 2, 1000, 128, device=DEV, seed=100 + splits + W)
+    lens = torch.tensor([1000, 1, 333], dtype=torch.int32, device=DEV)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=splits, window=W, sink_seed=True)
+    lam, _ = lambda_for(gap0, 0.6)
+    say(f"[decode] sink seed splits {splits} window {W} lam {lam:.4g}")
+    got = gpu_decode(q, kc, vc, lens, lam=lam, num_splits=splits, window=W, sink_seed=True)
+    _compare(q, f64(kc), f64(vc), lens, got, lam=lam, S=splits, what=f"gqa sink seed S={splits} W={W}",
+             window=W, sink_seed=True)
+
+
+def test_sink_seed_one_split_is_unseeded():
+    q, kc, vc, lens = inputs.decode_inputs(2, 8, 2, 2048, 64, device=DEV, seed=106)
+    _equal_calls(gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=1, sink_seed=True),
+                 gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=1))
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_sink_seed_mla_decode(splits):
+    q, kc, lens = _mla(3, 2000, seed=107 + splits, lens=[2000, 1, 777])
+    _, _, gap0, _ = gpu_decode(q, kc, kc, lens, lam=0.0, num_splits=splits, dv=512, sink_seed=True)
+    lam, _ = lambda_for(gap0, 0.6)
+    say(f"[decode] mla sink seed splits {splits} lam {lam:.4g}")
+    got = gpu_decode(q, kc, kc, lens, lam=lam, num_splits=splits, dv=512, sink_seed=True)
+    kk = f64(kc)
+    _compare(q, kk, kk[..., :512], lens, got, lam=lam, S=splits, what=f"mla sink seed S={splits}", sink_seed=True)
+
+
+def test_sink_seed_paged_equals_contiguous():
+    q, kc, vc, lens = inputs.decode_inputs(2, 8, 2, 3000, 128, device=DEV, seed=109, seq_lens=[3000, 2222])
+    (kp, vp), table = inputs.paged_pool([kc, vc], lens, 16, seed=4, spare_pages=1)
+    _equal_calls(gpu_decode_paged(q, kp, vp, table, lens, 3000, lam=2e-3, num_splits=4, sink_seed=True),
+                 gpu_decode(q, kc, vc, lens, lam=2e-3, num_splits=4, sink_seed=True))
+    q, kc, lens = _mla(2, 3000, seed=110, lens=[3000, 1500])
+    (kp,), table = inputs.paged_pool([kc], lens, 64, seed=5)
+    _equal_calls(gpu_decode_paged(q, kp, kp, table, lens, 3000, lam=2e-3, num_splits=3, dv=512, sink_seed=True),
+                 gpu_decode(q, kc, kc, lens, lam=2e-3, num_splits=3, dv=512, sink_seed=True))
+
+
+def test_sink_seed_gqa_decode_148_sequences_sampled():
+    """The full 148-sequence 32K GQA step with seeded splits at the planner's
+    split count, lambda for 70% of the seeded gaps; oracle on sampled units."""
+    q, kc, vc, lens = inputs.decode_inputs(148, 32, 8, 32768, 128, n_random=8, device=DEV, seed=1002)
+    S, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=0.01)
+    _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=S, sink_seed=True)
+    lam, reached = lambda_for(gap0, 0.7)
+    units = [(0, 0), (63, 7), (147, 2)]
+    cnt, _ = _run(q, kc, vc, lens, lam=lam, splits=S, what="148x32/8x32768x128 sink seed", unit_mask=units,
+                  sink_seed=True)
+    assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
