@@ -13,7 +13,8 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
     d=128, bf16 cache, block 64) at the 70% and 50% lambdas and lambda = 0:
     microseconds per decode step and HBM GB/s on the bytes actually loaded;
     then the same step over a paged cache (64-row pages of a shuffled pool;
-    likewise for the latent decode below) and with a 4096-key sliding window;
+    likewise for the latent decode below), with a 4096-key sliding window,
+    and with sink-seeded splits (likewise for the latent decode);
   * the latent (MLA) decode workload (16 sequences, 128 query heads sharing one
     576-wide latent KV head, V = its first 512 columns, 65536 cached tokens)
     at the 70% lambda and lambda = 0: microseconds per step, GB/s on the
@@ -131,12 +132,39 @@ def calibrate_prefill(q, k, v, targets, window=0):
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
 
-def calibrate_decode(q, kc, vc, lens, S, targets, dv=None, window=0):
+def calibrate_decode(q, kc, vc, lens, S, targets, dv=None, window=0, sink_seed=False):
     B, Hkv, L = q.shape[0], kc.shape[1], kc.shape[2]
     gap = torch.empty(B, Hkv, -(-L // 64), dtype=torch.float32, device="cuda")
-    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap, dv=dv, window=window)
+    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap, dv=dv, window=window, sink_seed=sink_seed)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
+
+
+def seed_leg(q, kc, vc, lens, S, lam70, steps, warmup, dv=None):
+    """Sink-seeded splits against unseeded ones on one decode workload: time
+    and sparsity at the unseeded 70% lambda, time at the seeded 70% lambda,
+    and at equal (70%) sparsity the mean |O - O_dense| of both (fp32 O)."""
+    ws = max(bl.blasst_decode_plan(q, kc, vc, lens, lam=1e-3, num_splits=S, dv=dv)[1], 1)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    lam_s = calibrate_decode(q, kc, vc, lens, S, [0.7], dv=dv, sink_seed=True)[0.7][0]
+
+    def call(lam, seed, cnt=None, out_dtype=torch.bfloat16):
+        return bl.blasst_decode(q, kc, vc, lens, lam=lam, num_splits=S, dv=dv, workspace=work, counters=cnt,
+                                sink_seed=seed, out_dtype=out_dtype)
+
+    res = {"num_splits": S, "lambda70_unseeded": lam70, "lambda70_seeded": lam_s}
+    for name, lam in (("at_unseeded_lambda70", lam70), ("s70", lam_s)):
+        mean_ms, _, _ = time_calls(lambda lam=lam: call(lam, True), steps, warmup)
+        vis, skp = counts(lambda c, lam=lam: call(lam, True, c))
+        res[name] = {"us": mean_ms * 1e3, "sparsity": skp / vis}
+        log(f"  seeded splits, {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}")
+    o_dense = call(0.0, False, out_dtype=torch.float32)
+    e_u = (call(lam70, False, out_dtype=torch.float32) - o_dense).abs().mean().item()
+    e_s = (call(lam_s, True, out_dtype=torch.float32) - o_dense).abs().mean().item()
+    torch.cuda.synchronize()
+    res["mean_abs_err_vs_dense70"] = {"unseeded": e_u, "seeded": e_s}
+    log(f"  mean |O - O_dense| at 70%: unseeded {e_u:.3e}, seeded {e_s:.3e}")
+    return res
 
 
 def counts(fn_with_counters):
@@ -216,7 +244,7 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
     return (q, k, v, lam70), res, dense_flops
 
 
-def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), window=0):
+def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), window=0, seed=False):
     (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
     S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -278,10 +306,12 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), w
                           "gbps": loaded / (mean_ms * 1e-3) / 1e9}
             log(f"decode {name} (window {window}): {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
                 f"{dres[name]['gbps']:.0f} GB/s, splits {Sw}")
+    if seed:
+        dres["sink_seed"] = seed_leg(dq, kc, vc, lens, S, lams["s70"], steps, warmup)
     return S, dres
 
 
-def bench_mla(steps, warmup, names=("s70", "s50", "dense"), paged_names=()):
+def bench_mla(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), seed=False):
     (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
     S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=1e-3, dv=dv)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -322,6 +352,9 @@ def bench_mla(steps, warmup, names=("s70", "s50", "dense"), paged_names=()):
             vis, skp = counts(lambda c: pg(c))
             res[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis}
             log(f"mla decode {name} (64-row pages): {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}")
+        del kp, table
+    if seed:
+        res["sink_seed"] = seed_leg(q, kc, kc, lens, S, lams["s70"], steps, warmup, dv=dv)
     return S, res
 
 
@@ -477,7 +510,7 @@ def main():
     # ------------------------------------------------------------- decode
     decode = mla = long_prefill = None
     if not args.no_decode:
-        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"), window=4096)
+        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"), window=4096, seed=True)
         decode = {
             "workload": "GQA decode B=148 Hq=32 Hkv=8 L=32768 d=128 bf16, block 64, one query token per sequence",
             "num_splits": S,
@@ -499,9 +532,10 @@ def main():
                        "us_per_step_dense": dres["window_dense"]["us"],
                        "speedup70_vs_dense": dres["window_dense"]["us"] / dres["window_s70"]["us"],
                        "hbm_gbps70": dres["window_s70"]["gbps"], "hbm_gbps_dense": dres["window_dense"]["gbps"]},
+            "sink_seed": dres["sink_seed"],
         }
         torch.cuda.empty_cache()
-        S, mres = bench_mla(steps, warmup, paged_names=("paged_s70", "paged_dense"))
+        S, mres = bench_mla(steps, warmup, paged_names=("paged_s70", "paged_dense"), seed=True)
         m70 = mres["s70"]
         mla = {
             "workload": "latent (MLA) decode B=16 Hq=128 sharing one KV head, dqk=576 dv=512 (V = K[..., :512]), "
@@ -521,6 +555,7 @@ def main():
                       "us_per_step_dense": mres["paged_dense"]["us"],
                       "overhead70_vs_contiguous": mres["paged_s70"]["us"] / m70["us"] - 1.0,
                       "overhead_dense_vs_contiguous": mres["paged_dense"]["us"] / mres["dense"]["us"] - 1.0},
+            "sink_seed": mres["sink_seed"],
         }
         torch.cuda.empty_cache()
         sweep, wres = bench_long_prefill(max(2, steps // 4), max(1, warmup // 2))
