@@ -21,7 +21,7 @@
 //    lane) comes from the gfx950 transpose read ds_read_b64_tr_b16.
 //  * K and V tiles are copied global -> LDS with global_load_lds_dwordx4 (no
 //    registers), into a row-major layout whose 16-byte chunks are XOR-swizzled
-//    by row (swz) so that MFMA operand reads are bank-conflict free.  K and V
+//    by row (pswz) so that MFMA operand reads are bank-conflict free.  K and V
 //    each run in a ring of 2 buffers; V is requested only once the block's
 //    vote says it executes, one iteration before its P.V product.
 //  * Software pipeline with one barrier per key block: iteration j finishes
@@ -44,6 +44,23 @@ namespace blasst {
 namespace {
 
 constexpr int BC = 64;       // key block
+
+// Chunk swizzle of the K and V tiles: physical 16-byte chunk = logical chunk ^
+// pswz(row).  The K operand read (ds_read_b128) serves 16 lanes per LDS cycle:
+// 16 consecutive rows at one logical chunk.  The V^T operand read
+// (ds_read_b64_tr_b16) serves 32 lanes: a 4-aligned quad of rows x an aligned
+// group of 4 chunks.  256-byte rows (d = 128) each span all banks, so the
+// swizzle must permute the rows mod 16 and give the 4 rows of a quad distinct
+// bits 2-3.  128-byte rows (d = 64) share a bank line in pairs, so with e =
+// row / 2 it must permute e mod 8 and give e and e+1 (e even) distinct bit 2.
+template <int DG>
+__device__ __forceinline__ int pswz(int row)
+{
+    if (DG > 8)
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int e = row >> 1;
+    return ((e & 1) << 2) | ((e >> 1) & 3);
+}
 
 template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16>
 __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, 2)))
@@ -126,7 +143,7 @@ void prefill_kernel(const PrefillArgs a)
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int row = (w * KI + i) * RPI + lane / DG;
-        const int c = (lane % DG) ^ swz<DG>(row);
+        const int c = (lane % DG) ^ pswz<DG>(row);
         koff[i] = (uint32_t)((row * a.k_st + c * 8) * 2);
         voff[i] = (uint32_t)((row * a.v_st + c * 8) * 2);
     }
@@ -141,7 +158,7 @@ void prefill_kernel(const PrefillArgs a)
             for (int i = 0; i < KI; ++i) {
                 const int ins = w * KI + i;
                 const int row = ins * RPI + lane / DG;
-                const int c = (lane % DG) ^ swz<DG>(row);
+                const int c = (lane % DG) ^ pswz<DG>(row);
                 int key = j * BC + row;
                 key = key < L ? key : L - 1;
                 copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024);
@@ -160,10 +177,14 @@ void prefill_kernel(const PrefillArgs a)
         // K operands are read three k-steps ahead of their MFMAs so that the
         // LDS latency hides behind the matrix work.
         constexpr int NK = D / 16;
+        // Row 32 kt + n, logical chunk 2 kk + hh: since pswz depends on the
+        // row mod 16 only and 2 kk, hh occupy disjoint bits, the byte offset is
+        // n RB + 32 kt RB + (32 kk ^ kx) with one lane constant kx (laundered
+        // per call so that the compiler does not hoist 8 offsets per lane).
+        int kx = 16 * (hh ^ pswz<DG>(n)), nrb = n * RB;
+        asm volatile("" : "+v"(kx), "+v"(nrb));
         auto kread = [&](int kk, int kt) {
-            const int row = 32 * kt + n;
-            const int c = (2 * kk + hh) ^ swz<DG>(row);
-            return *(const u32x4 *)(kb + row * RB + c * 16);
+            return *(const u32x4 *)(kb + nrb + 32 * kt * RB + ((32 * kk) ^ kx));
         };
         u32x4 ka[3][2];
 #pragma unroll
@@ -207,6 +228,8 @@ void prefill_kernel(const PrefillArgs a)
     float m2 = neg_inf(); // running max of this lane's row (base 2)
     float lsum = 0.f;     // running sum over this lane's half of each block
     int n_skipped = 0;
+    bool rescale = false; // O waits for a rescale by alpha_p before the next P.V
+    float alpha_p = 1.f;
 
     // Wave vote on block j against the running max; d = m~ - m with the
     // infinity rules (-inf if the row sees no key in the block, +inf while the
@@ -240,14 +263,28 @@ void prefill_kernel(const PrefillArgs a)
     // The V^T operands are read three MFMAs ahead (flattened over (u, dt)) so
     // that the LDS latency hides behind the matrix work.
     auto pv = [&](int j, const bf16x8 (&pf)[4]) {
+        // The rescale of the accumulator by the previous softmax's alpha,
+        // deferred to here: the MFMAs that last wrote O finished an iteration
+        // ago, so the multiply does not wait for the matrix pipe.
+        if (rescale) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                o[dt] *= alpha_p;
+        }
         const char *Vb = vbuf(j);
         constexpr int NDT = D / 32, NM = 4 * NDT;
+        // Rows ra = 16 u + 4 vh + vj and rb = ra + 8, logical chunk
+        // 4 dt + 2 vmb + vq/2: pswz of both rows does not depend on u and the
+        // chunk's dt bits are disjoint from the rest, so the byte offsets are
+        // vb0 + 16 u RB (+ 8 RB) + (64 dt ^ vxa or vxb) with lane constants.
+        int vb0 = (4 * vh + vj) * RB + (vq & 1) * 8;
+        int vxa = 16 * ((2 * vmb + (vq >> 1)) ^ pswz<DG>(4 * vh + vj));
+        int vxb = 16 * ((2 * vmb + (vq >> 1)) ^ pswz<DG>(4 * vh + vj + 8));
+        asm volatile("" : "+v"(vb0), "+v"(vxa), "+v"(vxb));
         auto vread = [&](int m) {
             const int u = m / NDT, dt = m % NDT;
-            const int c = 4 * dt + 2 * vmb + (vq >> 1);
-            const int ra = 16 * u + 4 * vh + vj, rb = ra + 8;
-            const i16x4 x0 = lds_read_tr16(Vb + ra * RB + ((c ^ swz<DG>(ra)) * 16) + (vq & 1) * 8);
-            const i16x4 x1 = lds_read_tr16(Vb + rb * RB + ((c ^ swz<DG>(rb)) * 16) + (vq & 1) * 8);
+            const i16x4 x0 = lds_read_tr16(Vb + vb0 + 16 * u * RB + ((64 * dt) ^ vxa));
+            const i16x4 x1 = lds_read_tr16(Vb + vb0 + (16 * u + 8) * RB + ((64 * dt) ^ vxb));
             const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
             return u32x4{y0[0], y0[1], y1[0], y1[1]};
         };
@@ -265,8 +302,10 @@ void prefill_kernel(const PrefillArgs a)
     };
 
     // Online-softmax update of an executed block: new running max, P (bf16,
-    // the B operand of the next P.V), row sum, and the rescale of the
-    // accumulator, skipped when no row of the wave raised its max.
+    // the B operand of the next P.V) and row sum.  The accumulator's rescale
+    // by alpha (needed when a row of the wave raised its max) is left to the
+    // block's P.V: until then O only receives nothing, and the P.V of the
+    // previous block, issued just before, would otherwise have to drain first.
     auto softmax = [&](const f32x16 (&s)[2], float mt2, bf16x8 (&pf)[4]) {
         const float mnew = fmaxf(m2, mt2);
         const float msafe = mnew == neg_inf() ? 0.f : mnew;
@@ -287,11 +326,8 @@ void prefill_kernel(const PrefillArgs a)
         }
         const float alpha = mnew > m2 ? exp2_hw(m2 - msafe) : 1.f; // 0 on the first block
         lsum = alpha * lsum + rs;
-        if (__any(mnew > m2)) {
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-                o[dt] *= alpha;
-        }
+        rescale = __any(mnew > m2) != 0;
+        alpha_p = alpha;
         m2 = mnew;
     };
 

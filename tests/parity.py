@@ -71,7 +71,7 @@ def gpu_prefill(q, k, v, *, causal, lam, tile_q, maps=True, out_dtype=torch.floa
     gap = torch.full((B, Hq, nqt, nkb), float("nan"), dtype=torch.float32, device=q.device) if maps else None
     cnt = torch.zeros(2, dtype=torch.int64, device=q.device)
     o = bl.blasst_prefill(q, k, v, causal=causal, lam=lam, tile_q=tile_q, skip_map=skip, gap_map=gap,
-                          counters=cnt, out_dtype=out_dtype, window=window, sink_seed=sink_seed)
+                          counters=cnt, out_dtype=out_dtype, window=window)
     torch.cuda.synchronize()
     return o, skip, gap, cnt.cpu().numpy()
 
