@@ -407,14 +407,16 @@ def window_prefill(q, k, v, out, W, steps, warmup):
     return res
 
 
-def bench_calibration(lengths=(4096, 8192, 16384, 32768), targets=(0.5, 0.7)):
+def bench_calibration(lengths=(4096, 8192, 16384, 32768, 65536), targets=(0.5, 0.7)):
     """The calibration law lambda = a(target) / L on the GQA prefill generator.
 
     For each L, lambda_L is the exact quantile of the gap map of a calibration
     input (seed 2000 + L/1024); a is fitted as ln a = mean(ln(lambda_L * L)).
     Fresh evaluation inputs (seed 1000 + L/1024) are then run with
     lambda = a / L from the fitted table, and the achieved block sparsity is
-    compared with the target."""
+    compared with the target; so is the sparsity that the per-length lambda_L
+    itself reaches on the evaluation input (how well a calibration transfers
+    between inputs of one length, apart from the 1/L law)."""
     B, Hq, Hkv, d = 1, 32, 8, 128
     lam_at = {t: [] for t in targets}
     for L in lengths:
@@ -429,15 +431,22 @@ def bench_calibration(lengths=(4096, 8192, 16384, 32768), targets=(0.5, 0.7)):
     for L in lengths:
         q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda",
                                         seed=1000 + L // 1024)
-        for t in targets:
-            lam = bl.blasst_calibrate(list(targets), a_fit, t, L)
+        def sparsity(lam):
             cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
             bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, counters=cnt)
             torch.cuda.synchronize()
             vis, skp = (int(x) for x in cnt.cpu())
-            rows.append({"L": L, "target": t, "lambda_L_calibrated": lam_at[t][list(lengths).index(L)],
-                         "lambda_from_fit": lam, "achieved": skp / vis, "deviation": skp / vis - t})
-            log(f"calibration L={L} target {t}: lambda(a/L)={lam:.4g} achieved {skp / vis:.4f}")
+            return skp / vis
+
+        for t in targets:
+            lam = bl.blasst_calibrate(list(targets), a_fit, t, L)
+            lam_l = lam_at[t][list(lengths).index(L)]
+            got, got_l = sparsity(lam), sparsity(lam_l)
+            rows.append({"L": L, "target": t, "lambda_L_calibrated": lam_l, "lambda_L_times_L": lam_l * L,
+                         "lambda_from_fit": lam, "achieved": got, "deviation": got - t,
+                         "achieved_with_lambda_L": got_l})
+            log(f"calibration L={L} target {t}: lambda(a/L)={lam:.4g} achieved {got:.4f}; "
+                f"lambda_L={lam_l:.4g} (lambda_L*L={lam_l * L:.4g}) achieves {got_l:.4f}")
         del q, k, v
     torch.cuda.empty_cache()
     return {"workload": "GQA causal prefill B=1 Hq=32 Hkv=8 d=128, tile 128, block 64; calibration seeds "

@@ -35,6 +35,18 @@ namespace {
 constexpr int BC = 64;
 constexpr int NWD = 4; // waves per decode workgroup = blocks per batch
 
+// V tile chunk swizzle (physical chunk = logical chunk ^ dswz(row)).  The
+// transpose read of the 16x16x32 A operand serves 32 lanes per LDS cycle: 8
+// consecutive rows (8-aligned) x an aligned pair of chunks.  256-byte rows
+// each span all banks, so bits 1-3 of the swizzle must differ across the 8
+// rows; 128-byte rows share a bank line in pairs, so they must differ across
+// the 4 rows of each parity.
+template <int DG>
+__device__ __forceinline__ int dswz(int row)
+{
+    return DG > 8 ? (row & 7) << 1 : ((row >> 1) & 3) << 1;
+}
+
 template <int D, bool SKIP, bool OUT_BF16, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_kernel(const DecodeArgs a)
@@ -143,7 +155,7 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int row = i * RPI + lane / DG;
-            const int c = (lane % DG) ^ swz<DG>(row);
+            const int c = (lane % DG) ^ dswz<DG>(row);
             int key = j * BC + row;
             key = key < len ? (key > klo ? key : klo) : len - 1;
             copy16_to_lds(vp + page_off(ids, (i * RPI) >> 4, a.v_sb) + (int64_t)(key & pmask) * a.v_st + c * 8,
@@ -322,8 +334,8 @@ void decode_gqa_kernel(const DecodeArgs a)
                 for (int dt = 0; dt < NDT; ++dt) {
                     const int c = 2 * dt + (vq >> 1);
                     const int ra = 32 * u2 + 4 * vgrp + vj, rb = ra + 16;
-                    const i16x4 x0 = lds_read_tr16(vt + ra * RB + ((c ^ swz<DG>(ra)) * 16) + (vq & 1) * 8);
-                    const i16x4 x1 = lds_read_tr16(vt + rb * RB + ((c ^ swz<DG>(rb)) * 16) + (vq & 1) * 8);
+                    const i16x4 x0 = lds_read_tr16(vt + ra * RB + ((c ^ dswz<DG>(ra)) * 16) + (vq & 1) * 8);
+                    const i16x4 x1 = lds_read_tr16(vt + rb * RB + ((c ^ dswz<DG>(rb)) * 16) + (vq & 1) * 8);
                     const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
                     const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
                     o[dt] = mfma16(as_bf16x8(va), pf[u2], o[dt]);
