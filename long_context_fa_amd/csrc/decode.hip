@@ -423,7 +423,8 @@ void decode_gqa_kernel(const DecodeArgs a)
 // Log-sum-exp merge of split partials.  A thread owns 4 consecutive output
 // columns of one (sequence, query head); a workgroup covers 256 / (dv/4)
 // heads.  Weights are exp2(m_s - M) with M the largest split max among
-// splits that saw keys; splits with l = 0 contribute nothing.
+// splits that saw keys (kept as a running max, one chunk of splits at a
+// time); splits with l = 0 contribute nothing.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a, int dv)
 {
@@ -435,23 +436,38 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a,
     const int d = 4 * ((int)threadIdx.x % tph);
     const int G = a.G, g = hq / G, hd = hq % G, S = a.num_splits;
     const int64_t pu0 = ((int64_t)(b * a.Hkv + g) * S) * G + hd;
-    float M = neg_inf();
-    for (int s = 0; s < S; ++s) {
-        const float2 ml = *(const float2 *)(a.part_ml + 2 * (pu0 + (int64_t)s * G));
-        if (ml.y > 0.f)
-            M = fmaxf(M, ml.x);
-    }
-    const float Ms = M == neg_inf() ? 0.f : M;
+    // One pass over the splits, CH at a time: the loads of a chunk are all
+    // issued before any is used, and the running (M, num, den) is rescaled
+    // when a chunk raises the max.  Indices past S re-read split S-1 and are
+    // masked.
+    constexpr int CH = 8;
+    float M = neg_inf(), den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < S; ++s) {
-        const int64_t pu = pu0 + (int64_t)s * G;
-        const float2 ml = *(const float2 *)(a.part_ml + 2 * pu);
-        const f32x4 po = *(const f32x4 *)(a.part_o + pu * dv + d);
-        const float wgt = ml.y > 0.f ? exp2_hw(ml.x - Ms) : 0.f;
-        num += wgt * po;
-        den += wgt * ml.y;
+    for (int s0 = 0; s0 < S; s0 += CH) {
+        float2 ml[CH];
+        f32x4 po[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int64_t pu = pu0 + (int64_t)(s0 + i < S ? s0 + i : S - 1) * G;
+            ml[i] = *(const float2 *)(a.part_ml + 2 * pu);
+            po[i] = *(const f32x4 *)(a.part_o + pu * dv + d);
+        }
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (s0 + i < S && ml[i].y > 0.f)
+                Mc = fmaxf(Mc, ml[i].x);
+        const float Ms = Mc == neg_inf() ? 0.f : Mc;
+        const float r = M == neg_inf() ? 0.f : exp2_hw(M - Ms);
+        num *= r;
+        den *= r;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float wgt = (s0 + i < S && ml[i].y > 0.f) ? exp2_hw(ml[i].x - Ms) : 0.f;
+            num += wgt * po[i];
+            den += wgt * ml[i].y;
+        }
+        M = Mc;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const f32x4 val = num * inv;
