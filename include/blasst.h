@@ -95,7 +95,8 @@ typedef struct {
  * causal masking, a non-positive stride or a
  * pointer not aligned to 16 bytes with a token stride not a multiple of 8
  * elements; UNSUPPORTED for other d, dv, tile or dtype; LAUNCH if HIP fails.
- * L = 0 or B = 0 is a valid no-op.
+ * L = 0 or B = 0 is a valid no-op: only the scalar arguments are checked and
+ * the tensor pointers may be null.
  */
 typedef struct {
     blasst_tensor q, k, v, o;
@@ -134,6 +135,8 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream);
  *   (dqk = 576, dv = 512, Hkv = 1, G = 128, v aliasing k).  block_k = 64.
  *   num_splits: 0 lets the library choose; otherwise 1..nKB.
  *   skip_map / gap_map: optional device [B, Hkv, nKB], nKB = ceil(Lmax/64).
+ *   B = 0 is a valid no-op: only the scalar arguments are checked, the
+ *             pointers may be null and the planned workspace is 0 bytes.
  *   window  : 0 = none; W > 0 = sliding window (see blasst_prefill): the
  *             query, at position seq_len-1, sees the last W keys.  The splits
  *             then cut the blocks from the first one holding such a key,

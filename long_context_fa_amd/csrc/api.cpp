@@ -101,6 +101,10 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
         return s;
     if (std::isnan(p->scale) || std::isinf(p->scale))
         return fail(BLASST_ERR_INVALID_ARG, "scale must be finite");
+    if (p->window < 0 || (p->window > 0 && !p->causal))
+        return fail(BLASST_ERR_INVALID_ARG, "window must be >= 0, and a window needs causal masking");
+    if (p->B == 0 || p->L == 0)
+        return BLASST_OK; // empty problem: nothing to read or write, buffers may be null
     if (blasst_status s = check_tensor(p->q, "q", false, false))
         return s;
     if (blasst_status s = check_tensor(p->k, "k", false, false))
@@ -116,14 +120,10 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
         return fail(BLASST_ERR_UNSUPPORTED, "tile_q must be 64 or 128 (got %d)", p->tile_q);
     if (p->block_k != 64)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
-    if (p->window < 0 || (p->window > 0 && !p->causal))
-        return fail(BLASST_ERR_INVALID_ARG, "window must be >= 0, and a window needs causal masking");
     const int64_t nqt = (p->L + p->tile_q - 1) / p->tile_q;
     const int64_t nkb = (p->L + p->block_k - 1) / p->block_k;
     if (p->L > (int64_t)1 << 30 || nqt * p->Hq * p->B > (int64_t)1 << 31)
         return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
-    if (p->B == 0 || p->L == 0)
-        return BLASST_OK;
 
     blasst::PrefillArgs a{};
     a.q = (const uint16_t *)p->q.ptr;
@@ -180,6 +180,12 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
         return s;
     if (std::isnan(p->scale) || std::isinf(p->scale))
         return fail(BLASST_ERR_INVALID_ARG, "scale must be finite");
+    if (p->window < 0)
+        return fail(BLASST_ERR_INVALID_ARG, "window must be >= 0");
+    if (p->num_splits < 0 || p->num_splits > (p->Lmax + 63) / 64)
+        return fail(BLASST_ERR_INVALID_ARG, "num_splits must be in 0..ceil(Lmax/64)");
+    if (p->B == 0)
+        return BLASST_OK; // empty batch: nothing to read or write, buffers may be null
     if (p->seq_lens == nullptr)
         return fail(BLASST_ERR_INVALID_ARG, "seq_lens: null pointer");
     if (blasst_status s = check_tensor(p->q, "q", true, false))
@@ -192,8 +198,6 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
         return s;
     if (p->block_k != 64)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
-    if (p->window < 0)
-        return fail(BLASST_ERR_INVALID_ARG, "window must be >= 0");
     const DecodeKind kind = decode_kind(p);
     if (kind == KIND_NONE)
         return fail(BLASST_ERR_UNSUPPORTED,
@@ -217,9 +221,6 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
     if (kind == KIND_MLA && span * p->k_cache.st * 2 >= ((int64_t)1 << 31))
         return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs rows * token stride * 2 < 2^31 bytes "
                                             "(rows = Lmax, or the page size of a paged cache)");
-    const int64_t nkb = (p->Lmax + 63) / 64;
-    if (p->num_splits < 0 || p->num_splits > nkb)
-        return fail(BLASST_ERR_INVALID_ARG, "num_splits must be in 0..ceil(Lmax/64)");
     if (p->Lmax > (int64_t)1 << 30 || p->B > 65535 || p->Hkv > 65535)
         return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
     return BLASST_OK;
@@ -248,7 +249,7 @@ int choose_splits(const blasst_decode_params *p)
 
 size_t workspace_for(const blasst_decode_params *p, int S)
 {
-    if (S <= 1)
+    if (S <= 1 || p->B == 0)
         return 0;
     const int64_t G = p->Hq / p->Hkv;
     const int64_t units = p->B * p->Hkv * S * G;

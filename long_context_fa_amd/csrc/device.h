@@ -98,21 +98,6 @@ __device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff
 // explicit wait_vmcnt for copies the compiler does not track.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// XOR swizzle of the 16-byte chunks of one row of an LDS K/V tile (DG chunks
-// per row): physical chunk = logical chunk ^ swz(row).  Chosen so that both
-// operand reads are bank-conflict free: 8 consecutive rows at one chunk
-// (ds_read_b128 of the K operand) and 4 consecutive rows (4-aligned) x 2
-// adjacent chunks (ds_read_b64_tr_b16 of the V operand) each land on
-// distinct chunks.
-template <int DG>
-__device__ __forceinline__ int swz(int row)
-{
-    int g = ((row & 3) << 1) | ((row >> 2) & 1);
-    if (DG > 8)
-        g |= row & 8;
-    return g;
-}
-
 // Workgroup barrier that orders LDS accesses only: global memory is not
 // fenced, so outstanding global->LDS copies and global stores are not drained
 // (the kernels wait for their copies explicitly before the barrier).

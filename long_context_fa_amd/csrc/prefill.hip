@@ -135,7 +135,7 @@ void prefill_kernel(const PrefillArgs a)
     const int jlo = CAUSAL && r0 - a.win + 1 > 0 ? (r0 - a.win + 1) / BC : 0;
 
     // Tile copy: wave w fills rows [w*KI*RPI, (w+1)*KI*RPI); lane -> (row, chunk)
-    // with the chunk XOR-swizzled by the row (swz).  Per-lane byte offsets of
+    // with the chunk XOR-swizzled by the row (pswz).  Per-lane byte offsets of
     // a whole tile are computed once: a block that lies entirely below L
     // costs one scalar add per tile copy.  Rows past L re-read row L-1
     // (finite data; those keys are masked to -inf).

@@ -111,6 +111,24 @@ def test_decode_plan_host_only():
     assert S2 == 7
 
 
+def test_empty_calls_are_noops():
+    """L = 0 or B = 0 check the scalars only and return OK: empty torch
+    tensors arrive as null pointers and nothing is launched or written."""
+    base = _bf16(2, 2, 256, 128)
+    out = torch.full((2, 2, 0, 128), 7.0)
+    assert bl.blasst_prefill(base[:, :, :0], base[:, :1, :0], base[:, :1, :0], out=out, lam=0.01,
+                             stream=0) is out
+    bl.blasst_prefill(base[:0], base[:0, :1], base[:0, :1], out=torch.empty(0, 2, 256, 128), lam=0.01, stream=0)
+    with pytest.raises(bl.BlasstError):  # scalars are still checked
+        bl.blasst_prefill(base[:0], base[:0, :1], base[:0, :1], lam=1.5, stream=0)
+    qd, kc = _bf16(2, 8, 128), _bf16(2, 2, 256, 128)
+    lens = torch.full((2,), 256, dtype=torch.int32)
+    assert bl.blasst_decode_plan(qd[:0], kc[:0], kc[:0], lens[:0], lam=0.01, num_splits=4) == (4, 0)
+    bl.blasst_decode(qd[:0], kc[:0], kc[:0], lens[:0], lam=0.01, stream=0)
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_decode(qd[:0], kc[:0], kc[:0], lens[:0], lam=0.01, window=-1, stream=0)
+
+
 # ------------------------------------------------------------- paged decode
 def _paged_err(page_size=64, pages=8, table_cols=4, Lmax=256, **kw):
     q = _bf16(2, 8, 128)

@@ -328,3 +328,26 @@ def test_sink_seed_gqa_decode_148_sequences_sampled():
     cnt, _ = _run(q, kc, vc, lens, lam=lam, splits=S, what="148x32/8x32768x128 sink seed", unit_mask=units,
                   sink_seed=True)
     assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("mla", [False, True])
+def test_zero_length_sequence(mla):
+    """A sequence of length 0 yields O = 0 and an all-unvisited map; the other
+    sequences are unaffected (bit-equal to a call without it)."""
+    if mla:
+        q, kc, _ = _mla(3, 1000, seed=120, lens=[1000, 1, 333])
+        vc, dv = kc, 512
+    else:
+        q, kc, vc, _ = inputs.decode_inputs(3, 8, 2, 1000, 128, device=DEV, seed=121)
+        dv = None
+    lens = torch.tensor([1000, 0, 333], dtype=torch.int32, device=DEV)
+    got = gpu_decode(q, kc, vc, lens, lam=1e-3, num_splits=3, dv=dv)
+    assert torch.count_nonzero(got[0][1]) == 0
+    assert (got[1][1] == 255).all() and torch.isinf(got[2][1]).all() and (got[2][1] < 0).all()
+    keep = torch.tensor([0, 2], device=DEV)
+    kk = kc[keep]
+    vk = kk if mla else vc[keep]  # the latent V must alias K
+    ref = gpu_decode(q[keep], kk, vk, lens[keep], lam=1e-3, num_splits=3, dv=dv)
+    for x, y in zip(got[:3], ref[:3]):
+        assert torch.equal(x[keep], y)
