@@ -202,8 +202,7 @@ void decode_gqa_kernel(const DecodeArgs a)
                 if (key < len && key >= klo)
                     mt = fmaxf(mt, sc[kt][r]);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_xor32(max_xor16(mt));
         pmax = mt * a.scale_log2;
     }
     if (jb < je) {
@@ -243,8 +242,7 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 mt = fmaxf(mt, sc[kt][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_xor32(max_xor16(mt));
         const float mt2 = mt * a.scale_log2;
         if (grp == 0)
             mblk[par][w][n] = mt2;

@@ -47,6 +47,26 @@ __device__ __forceinline__ float wave_max(float x)
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// max(x, x of lane i ^ 32) with the gfx950 v_permlane32_swap, which swaps the
+// upper half-wave of one copy of x with the lower half of another: each lane
+// ends up holding its own value and its partner's, in either order, with no
+// LDS round trip.
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// max(x, x of lane i ^ 16) with v_permlane16_swap (odd 16-lane rows of one
+// copy swapped with the even rows of another), likewise without LDS.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 } // namespace blasst
 
 namespace blasst {

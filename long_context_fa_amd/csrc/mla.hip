@@ -237,7 +237,7 @@ void decode_mla_kernel(const DecodeArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mt = fmaxf(mt, sc[kt][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_xor32(mt);
         const float mt2 = mt * a.scale_log2;
         if (it < 0) {
             m2 = mt2; // the seed: no vote, no P.V for this block

@@ -221,8 +221,7 @@ void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mt = fmaxf(mt, s[kt][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        mt2 = mt * a.scale_log2;
+        mt2 = max_xor32(mt) * a.scale_log2;
     };
 
     float m2 = neg_inf(); // running max of this lane's row (base 2)
@@ -335,29 +334,22 @@ void prefill_kernel(const PrefillArgs a)
     //   S_j and its row max are in registers and its vote is in LDS;
     //   K_{j+1} and (if block j-1 executed) V_{j-1} are in flight;
     //   P_{j-1} is in registers if block j-1 executed.
-    // Iteration j: barrier; decide j; request V_j (if executed) and K_{j+2};
-    // then O += V_{j-1} P_{j-1} (MFMA), the softmax of block j (VALU) and the
-    // scores of block j+1 (MFMA); finally vote on block j+1.  The other
-    // workgroup on the compute unit fills the matrix / vector gaps.  By the barrier of iteration j+1 the V_j and K_{j+2} copies
-    // have had a whole iteration to land.
-    copy_tile(kp, a.k_st, koff, jlo, kbuf(jlo));
-    if (jlo + 1 < nvis) {
-        copy_tile(kp, a.k_st, koff, jlo + 1, kbuf(jlo + 1));
-        wait_vmcnt<KI>();
-    } else {
-        wait_vmcnt<0>();
-    }
-    lds_barrier();
-    f32x16 sc[2];
-    float mt2c;
-    scores(jlo, sc, mt2c);
-    vote_block(jlo, mt2c);
-
+    // Iteration j: barrier; request K_{j+2} (no decision needed) and read
+    // the votes on block j; request V_j if it executes; then O += V_{j-1}
+    // P_{j-1} (MFMA), the softmax of block j (VALU) and the scores of block
+    // j+1 (MFMA); finally vote on block j+1.  The other workgroup on the
+    // compute unit fills the matrix / vector gaps.  By the barrier of
+    // iteration j+1 the V_j and K_{j+2} copies have had a whole iteration to
+    // land.  S_j and S_{j+1} live in two register sets that alternate between
+    // consecutive blocks (the loop is unrolled by two), so the loop carries no
+    // register copies.
     bf16x8 pprev[4];
     bool eprev = false;
-    for (int j = jlo; j < nvis; ++j) {
+    auto iter = [&](int j, f32x16(&sc)[2], float mtc, f32x16(&sn)[2], float &mtn) {
         wait_vmcnt<0>();
         lds_barrier(); // votes_j, K_{j+1}, V_{j-1} visible; iteration j-1 done everywhere
+        if (j + 2 < nvis)
+            copy_tile(kp, a.k_st, koff, j + 2, kbuf(j)); // K ring refill
         const int par = j & 1;
         bool skip = false;
         if (SKIP) {
@@ -365,7 +357,7 @@ void prefill_kernel(const PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < NW; ++i)
                 all &= vote[par][i];
-            skip = all != 0;
+            skip = __builtin_amdgcn_readfirstlane(all) != 0; // uniform across the workgroup
         }
         if (want_maps && tid == 0) {
             float g = neg_inf();
@@ -382,19 +374,34 @@ void prefill_kernel(const PrefillArgs a)
         const bool ecur = !skip;
         if (ecur)
             copy_tile(vp, a.v_st, voff, j, vbuf(j)); // V_j only for an executed block
-        if (j + 2 < nvis)
-            copy_tile(kp, a.k_st, koff, j + 2, kbuf(j)); // K ring refill
-        const bool has_next = j + 1 < nvis;
 
         if (eprev)
             pv(j - 1, pprev); // P_{j-1} is dead afterwards
         if (ecur)
-            softmax(sc, mt2c, pprev); // P_j reuses its registers
-        if (has_next) {
-            scores(j + 1, sc, mt2c); // S_j is dead: S_{j+1} takes its registers
-            vote_block(j + 1, mt2c);
+            softmax(sc, mtc, pprev); // P_j reuses its registers
+        if (j + 1 < nvis) {
+            scores(j + 1, sn, mtn); // into the other register set
+            vote_block(j + 1, mtn);
         }
         eprev = ecur;
+    };
+
+    copy_tile(kp, a.k_st, koff, jlo, kbuf(jlo));
+    if (jlo + 1 < nvis) {
+        copy_tile(kp, a.k_st, koff, jlo + 1, kbuf(jlo + 1));
+        wait_vmcnt<KI>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    lds_barrier();
+    f32x16 sa[2], sb[2];
+    float mta, mtb;
+    scores(jlo, sa, mta);
+    vote_block(jlo, mta);
+    for (int j = jlo; j < nvis; j += 2) {
+        iter(j, sa, mta, sb, mtb);
+        if (j + 1 < nvis)
+            iter(j + 1, sb, mtb, sa, mta);
     }
     if (eprev) {
         wait_vmcnt<0>();
