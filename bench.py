@@ -218,7 +218,14 @@ def cpu_baseline_prefill(q, k, v, lam, budget_s=20.0):
                       f"{done_s:.1f} s of fp64 work on {threads} threads"}
 
 
-def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
+# A lambda so small that no visited block can meet the test (log2 of it is
+# about -997, far below any score gap), but above 0, so the call runs the
+# skip-enabled kernels: their time against the lambda = 0 kernels is the cost
+# of the skip logic itself.
+LAM_TINY = 1e-300
+
+
+def bench_prefill(steps, warmup, names=("s70", "s50", "dense", "skip0")):
     (B, Hq, Hkv, L, d), (q, k, v) = prefill_workload()
     cal = calibrate_prefill(q, k, v, [0.5, 0.7])
     lam70, reach70 = cal[0.7]
@@ -230,7 +237,7 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
         return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
 
     dense_flops = 4.0 * B * Hq * L * L * d / 2
-    lams = {"s70": lam70, "s50": lam50, "dense": 0.0}
+    lams = {"s70": lam70, "s50": lam50, "dense": 0.0, "skip0": LAM_TINY}
     res = {}
     for name in names:
         lam = lams[name]
@@ -244,7 +251,7 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense")):
     return (q, k, v, lam70), res, dense_flops
 
 
-def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), window=0, seed=False):
+def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), window=0, seed=False):
     (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
     S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -255,7 +262,7 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), w
         return lambda: bl.blasst_decode(dq, kc, vc, lens, lam=lam, num_splits=S, out=dout,
                                         workspace=work, counters=cnt)
 
-    lams = {"s70": dcal[0.7][0], "s50": dcal[0.5][0], "dense": 0.0}
+    lams = {"s70": dcal[0.7][0], "s50": dcal[0.5][0], "dense": 0.0, "skip0": LAM_TINY}
     dres = {}
     for name in names:
         lam = lams[name]
@@ -311,7 +318,7 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), w
     return S, dres
 
 
-def bench_mla(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), seed=False):
+def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), seed=False):
     (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
     S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=1e-3, dv=dv)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -322,7 +329,7 @@ def bench_mla(steps, warmup, names=("s70", "s50", "dense"), paged_names=(), seed
         return lambda: bl.blasst_decode(q, kc, kc, lens, lam=lam, num_splits=S, out=out, dv=dv,
                                         workspace=work, counters=cnt)
 
-    lams = {"s70": cal[0.7][0], "s50": cal[0.5][0], "dense": 0.0}
+    lams = {"s70": cal[0.7][0], "s50": cal[0.5][0], "dense": 0.0, "skip0": LAM_TINY}
     res = {}
     for name in names:
         lam = lams[name]
@@ -514,6 +521,8 @@ def main():
         "speedup50_vs_dense": res["dense"]["ms"] / res["s50"]["ms"],
         "mfma_util_executed70": achieved / PEAK_BF16_TFLOPS,
         "mfma_util_dense": dense_flops / (res["dense"]["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "ms_skip_logic_nothing_skipped": res["skip0"]["ms"],
+        "skip_logic_overhead_vs_dense": res["skip0"]["ms"] / res["dense"]["ms"] - 1.0,
     }
 
     # ------------------------------------------------------------- decode
@@ -528,6 +537,8 @@ def main():
             "us_per_step_dense": dres["dense"]["us"],
             "speedup70_vs_dense": dres["dense"]["us"] / dres["s70"]["us"],
             "speedup50_vs_dense": dres["dense"]["us"] / dres["s50"]["us"],
+            "us_skip_logic_nothing_skipped": dres["skip0"]["us"],
+            "skip_logic_overhead_vs_dense": dres["skip0"]["us"] / dres["dense"]["us"] - 1.0,
             "roofline": {"bound": "hbm", "achieved": dres["s70"]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": dres["s70"]["gbps"] / PEAK_HBM_GBS, "traffic": measured_traffic("decode70"),
                          "algorithmic_bytes": dres["s70"]["bytes"]},
@@ -554,6 +565,8 @@ def main():
             "us_per_step50": mres["s50"]["us"], "sparsity50": mres["s50"]["sparsity"],
             "us_per_step_dense": mres["dense"]["us"],
             "speedup70_vs_dense": mres["dense"]["us"] / m70["us"],
+            "us_skip_logic_nothing_skipped": mres["skip0"]["us"],
+            "skip_logic_overhead_vs_dense": mres["skip0"]["us"] / mres["dense"]["us"] - 1.0,
             "hbm_gbps70": m70["gbps"], "mfma_tflops70": m70["tflops"],
             "mfma_tflops_dense": mres["dense"]["tflops"], "hbm_gbps_dense": mres["dense"]["gbps"],
             "roofline": {"bound": "hbm", "achieved": m70["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
