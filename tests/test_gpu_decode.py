@@ -90,6 +90,23 @@ def test_dense_decode_matches_oracle():
     assert cnt[1] == 0
 
 
+@pytest.mark.parametrize("mla", [False, True])
+def test_skip_kernel_at_unreachable_lambda_matches_dense(mla):
+    """lambda = 1e-300 runs the skip-enabled decode kernels although no block can
+    meet the test: nothing is skipped and O equals the lambda = 0 kernels'."""
+    if mla:
+        q, kc, lens = _mla(2, 3000, seed=32)
+        vc, dv = kc, 512
+    else:
+        q, kc, vc, lens = inputs.decode_inputs(3, 8, 2, 3000, 128, device=DEV, seed=32)
+        dv = None
+    cnt, S = _run(q, kc, vc, lens, lam=1e-300, splits=3, dv=dv, mla=mla, what=f"unreachable lambda mla={mla}")
+    assert cnt[1] == 0
+    o_skip, _, _, _ = gpu_decode(q, kc, vc, lens, lam=1e-300, num_splits=3, dv=dv)
+    o_dense, _, _, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=3, dv=dv)
+    assert (o_skip - o_dense).abs().max().item() <= 1e-6
+
+
 def test_parity_gqa_decode_full_length():
     """4 sequences of the 32K GQA decode shape (32/8 heads, d 128), every unit checked."""
     q, kc, vc, lens = inputs.decode_inputs(4, 32, 8, 32768, 128, n_random=8, device=DEV, seed=1002)

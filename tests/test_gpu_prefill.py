@@ -64,6 +64,19 @@ def test_dense_path_matches_oracle():
     assert ref["skipped"] == 0
 
 
+def test_skip_kernel_at_unreachable_lambda_matches_dense():
+    """lambda = 1e-300 runs the skip-enabled kernel (votes, decisions, predicated
+    V loads) although no block can meet the test: every visited block executes,
+    and O equals the lambda = 0 kernel's to rounding of the same operations."""
+    q, k, v = inputs.prefill_inputs(1, 4, 2, 1000, 128, device=DEV, seed=31)
+    ref = _run_full(q, k, v, causal=True, lam=1e-300, tile_q=128, what="skip kernel, unreachable lambda")
+    assert ref["skipped"] == 0
+    o_skip, skip, _, cnt = gpu_prefill(q, k, v, causal=True, lam=1e-300, tile_q=128)
+    o_dense, _, _, _ = gpu_prefill(q, k, v, causal=True, lam=0.0, tile_q=128)
+    assert cnt[1] == 0 and not (skip.cpu().numpy() == 1).any()
+    assert (o_skip - o_dense).abs().max().item() <= 1e-6
+
+
 def test_bf16_output_matches_fp32_output():
     q, k, v = inputs.prefill_inputs(1, 2, 1, 1024, 128, device=DEV, seed=4)
     o32, _, _, _ = gpu_prefill(q, k, v, causal=True, lam=1e-6, tile_q=128, maps=False)
