@@ -19,7 +19,9 @@
 //     decisions (a skipped block has m~ < m + ln(lambda) <= m), so the
 //     decision of block i uses the exclusive prefix max of the block maxima;
 //  3. a wave whose block is executed copies V global -> LDS into its own slice
-//     (global_load_lds, no registers), then issues the next batch's K loads,
+//     (global_load_lds, no registers; K and V loads carry the non-temporal
+//     hint, since a step reads each cache row once), then issues the next
+//     batch's K loads,
 //     computes the exponentials while both are in flight, and accumulates
 //     O^T += V^T P^T with the V^T operand taken by the gfx950 transpose read.
 //     A skipped block issues no V load at all.
@@ -158,7 +160,7 @@ void decode_gqa_kernel(const DecodeArgs a)
             const int c = (lane % DG) ^ dswz<DG>(row);
             int key = j * BC + row;
             key = key < len ? (key > klo ? key : klo) : len - 1;
-            copy16_to_lds(vp + page_off(ids, (i * RPI) >> 4, a.v_sb) + (int64_t)(key & pmask) * a.v_st + c * 8,
+            copy16_to_lds<true>(vp + page_off(ids, (i * RPI) >> 4, a.v_sb) + (int64_t)(key & pmask) * a.v_st + c * 8,
                           vt + i * 1024);
         }
     };

@@ -94,14 +94,21 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // these kernels, so the clobber is honoured in practice.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// NT = true adds the non-temporal hint, for data that is streamed once (a
+// decode step reads each cache row once).
+template <bool NT = false>
 __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+    if (NT)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(src) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
 }
 
 // Same copy with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
 // byte offset: the per-block address arithmetic becomes one scalar add.
+template <bool NT = false>
 __device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff, void *lds_base)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
@@ -110,7 +117,12 @@ __device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff
     // half would turn the base into an invalid address).
     const uint64_t bs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(bs) : "memory", "m0");
+    if (NT)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0), "v"(voff), "s"(bs)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(bs)
+                     : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

@@ -15,7 +15,8 @@
 // AGPRs) walks the key blocks of one (sequence, split):
 //  * the 64 x 576 bf16 K tile (72 KB) is copied global -> LDS with
 //    global_load_lds_dwordx4 into a double buffer, issued between the score
-//    MFMAs of the previous block.  In LDS a tile is a latent region (64 rows
+//    MFMAs of the previous block, with the non-temporal hint (a step reads
+//    each cache row once).  In LDS a tile is a latent region (64 rows
 //    of 512 columns, one 1 KB copy per row) and a rope region (64 rows of 64
 //    columns); 16-byte chunks are XOR-swizzled by row so that the operand
 //    reads hit distinct banks;
@@ -125,7 +126,7 @@ void decode_mla_kernel(const DecodeArgs a)
         if (i < 16) {
             int key = j * BC + 16 * w + i;
             key = key < len ? (key > klo ? key : klo) : len - 1;
-            copy16_to_lds_s(gb + (int64_t)(key & pmask) * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))),
+            copy16_to_lds_s<true>(gb + (int64_t)(key & pmask) * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))),
                             t + (16 * w + i) * LRB);
         } else {
             const int e = i - 16;
@@ -134,7 +135,7 @@ void decode_mla_kernel(const DecodeArgs a)
             int key = j * BC + 16 * w + 8 * e + lr;
             key = key < len ? (key > klo ? key : klo) : len - 1;
             const uint32_t off = LRB + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7)); // swzr of the row
-            copy16_to_lds_s(gb, (uint32_t)(key & pmask) * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
+            copy16_to_lds_s<true>(gb, (uint32_t)(key & pmask) * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
         }
     };
 
