@@ -218,6 +218,74 @@ def cpu_baseline_prefill(q, k, v, lam, budget_s=20.0):
                       f"{done_s:.1f} s of fp64 work on {threads} threads"}
 
 
+def cpu_oracle_decode(q, kc, vc, lens, lam, S, *, dv=None, n_seq=2, seed=8):
+    """The fp64 oracle on every (sequence, KV head) unit of n_seq random
+    sequences of a decode step; the step time is extrapolated from the wall
+    time per wave of `threads` units to all units."""
+    import oracle
+
+    B, Hq, _ = q.shape
+    Hkv = kc.shape[1]
+    threads = min(16, len(os.sched_getaffinity(0)))
+    bs = sorted(np.random.default_rng(seed).choice(B, size=min(n_seq, B), replace=False).tolist())
+    f = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    qh, kh = f(q[bs]), f(kc[bs])
+    vh = kh[..., :dv] if dv is not None else f(vc[bs])
+    t0 = time.perf_counter()
+    oracle.decode(qh, kh, vh, lens[bs].cpu().numpy(), lam=lam, block_k=64, num_splits=S, nthreads=threads,
+                  want_maps=False)
+    wall = time.perf_counter() - t0
+    units, total = len(bs) * Hkv, B * Hkv
+    waves = lambda n: -(-n // threads)  # noqa: E731
+    us = wall / waves(units) * waves(total) * 1e6
+    log(f"  cpu oracle decode: {units} units in {wall:.2f} s -> {us:.4g} us/step extrapolated")
+    return {"value": us, "unit": "us/step (extrapolated)", "cores": threads, "kind": "oracle",
+            "sample": f"all {units} (sequence, KV head) units of {len(bs)} random sequences of {B} at the 70% "
+                      f"lambda, {wall:.2f} s on {threads} threads; step time = wall time per wave of {threads} "
+                      f"units x the {waves(total)} waves of the {total} units"}
+
+
+def cpu_oracle_long_prefill(q, k, v, lam, budget_s=6.0, seed=9):
+    """The fp64 oracle on random query tiles of two query heads (one KV head)
+    of the long prefill; dense-equivalent throughput and the extrapolated
+    time of the whole launch."""
+    import oracle
+
+    B, Hq, L, d = q.shape
+    G = Hq // k.shape[1]
+    threads = min(16, len(os.sched_getaffinity(0)))
+    f = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    qh, kh, vh = f(q[:1, :2]), f(k[:1, :1]), f(v[:1, :1])
+    assert G >= 2
+    tile, nqt = 128, L // 128
+    units = [(h, t) for h in range(2) for t in range(nqt)]
+    order = np.random.default_rng(seed).permutation(len(units))
+    done_flops, done_s, n, batch = 0.0, 0.0, 0, threads
+    while n < len(units):
+        mask = np.zeros((1, 2, nqt), np.uint8)
+        picks = [units[i] for i in order[n:n + batch]]
+        flops = 0.0
+        for h, t in picks:
+            mask[0, h, t] = 1
+            r0 = t * tile
+            flops += 4.0 * d * (tile * r0 + tile * (tile + 1) / 2)  # dense-equivalent
+        t0 = time.perf_counter()
+        oracle.prefill(qh, kh, vh, causal=True, lam=lam, tile_q=tile, block_k=64, unit_mask=mask,
+                       nthreads=threads, want_maps=False)
+        dt = time.perf_counter() - t0
+        done_flops, done_s, n = done_flops + flops, done_s + dt, n + len(picks)
+        if done_s + 2 * dt > budget_s:
+            break
+        batch *= 2
+    tflops = done_flops / done_s / 1e12
+    full_ms = 4.0 * B * Hq * L * L * d / 2 / (tflops * 1e12) * 1e3
+    log(f"  cpu oracle long prefill: {n} tiles in {done_s:.1f} s -> {tflops:.4f} TFLOP/s, {full_ms:.4g} ms extrapolated")
+    return {"value": tflops, "unit": "TFLOP/s (dense-equivalent)", "ms_extrapolated": full_ms, "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} random query tiles (128 rows) of 2 query heads sharing one KV head, of "
+                      f"{B * Hq * nqt} tiles, at the 70% lambda: {done_s:.1f} s on {threads} threads"}
+
+
 # A lambda so small that no visited block can meet the test (log2 of it is
 # about -997, far below any score gap), but above 0, so the call runs the
 # skip-enabled kernels: their time against the lambda = 0 kernels is the cost
@@ -251,7 +319,8 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense", "skip0")):
     return (q, k, v, lam70), res, dense_flops
 
 
-def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), window=0, seed=False):
+def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), window=0, seed=False,
+                 oracle_cpu=False):
     (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
     S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -315,10 +384,12 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_na
                 f"{dres[name]['gbps']:.0f} GB/s, splits {Sw}")
     if seed:
         dres["sink_seed"] = seed_leg(dq, kc, vc, lens, S, lams["s70"], steps, warmup)
+    if oracle_cpu:
+        dres["cpu_oracle"] = cpu_oracle_decode(dq, kc, vc, lens, lams["s70"], S)
     return S, dres
 
 
-def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), seed=False):
+def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), seed=False, oracle_cpu=False):
     (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
     S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=1e-3, dv=dv)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
@@ -362,10 +433,12 @@ def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names
         del kp, table
     if seed:
         res["sink_seed"] = seed_leg(q, kc, kc, lens, S, lams["s70"], steps, warmup, dv=dv)
+    if oracle_cpu:
+        res["cpu_oracle"] = cpu_oracle_decode(q, kc, kc, lens, lams["s70"], S, dv=dv, n_seq=1)
     return S, res
 
 
-def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8)):
+def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8), oracle_cpu=False):
     (B, Hq, Hkv, L, d), (q, k, v) = long_prefill_workload()
     cal = calibrate_prefill(q, k, v, list(targets))
     out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
@@ -385,7 +458,8 @@ def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8)):
     dense_ms = rows[-1]["ms"]
     for r in rows:
         r["speedup_vs_dense"] = dense_ms / r["ms"]
-    return rows, window_prefill(q, k, v, out, 4096, steps, warmup)
+    cpu = cpu_oracle_long_prefill(q, k, v, cal[0.7][0]) if oracle_cpu and 0.7 in cal else None
+    return rows, window_prefill(q, k, v, out, 4096, steps, warmup), cpu
 
 
 def window_prefill(q, k, v, out, W, steps, warmup):
@@ -528,7 +602,9 @@ def main():
     # ------------------------------------------------------------- decode
     decode = mla = long_prefill = None
     if not args.no_decode:
-        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"), window=4096, seed=True)
+        oc = not args.no_cpu_baseline
+        S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"), window=4096, seed=True,
+                               oracle_cpu=oc)
         decode = {
             "workload": "GQA decode B=148 Hq=32 Hkv=8 L=32768 d=128 bf16, block 64, one query token per sequence",
             "num_splits": S,
@@ -553,9 +629,10 @@ def main():
                        "speedup70_vs_dense": dres["window_dense"]["us"] / dres["window_s70"]["us"],
                        "hbm_gbps70": dres["window_s70"]["gbps"], "hbm_gbps_dense": dres["window_dense"]["gbps"]},
             "sink_seed": dres["sink_seed"],
+            "cpu_oracle": dres.get("cpu_oracle"),
         }
         torch.cuda.empty_cache()
-        S, mres = bench_mla(steps, warmup, paged_names=("paged_s70", "paged_dense"), seed=True)
+        S, mres = bench_mla(steps, warmup, paged_names=("paged_s70", "paged_dense"), seed=True, oracle_cpu=oc)
         m70 = mres["s70"]
         mla = {
             "workload": "latent (MLA) decode B=16 Hq=128 sharing one KV head, dqk=576 dv=512 (V = K[..., :512]), "
@@ -578,13 +655,15 @@ def main():
                       "overhead70_vs_contiguous": mres["paged_s70"]["us"] / m70["us"] - 1.0,
                       "overhead_dense_vs_contiguous": mres["paged_dense"]["us"] / mres["dense"]["us"] - 1.0},
             "sink_seed": mres["sink_seed"],
+            "cpu_oracle": mres.get("cpu_oracle"),
         }
         torch.cuda.empty_cache()
-        sweep, wres = bench_long_prefill(max(2, steps // 4), max(1, warmup // 2))
+        sweep, wres, lcpu = bench_long_prefill(max(2, steps // 4), max(1, warmup // 2), oracle_cpu=oc)
         long_prefill = {
             "workload": "GQA causal prefill B=2 Hq=32 Hkv=8 L=32768 d=128 bf16, query tile 128, key block 64",
             "sweep": sweep,
             "window": wres,
+            "cpu_oracle": lcpu,
         }
         torch.cuda.empty_cache()
 
