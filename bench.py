@@ -286,6 +286,43 @@ def cpu_oracle_long_prefill(q, k, v, lam, budget_s=6.0, seed=9):
                       f"{B * Hq * nqt} tiles, at the 70% lambda: {done_s:.1f} s on {threads} threads"}
 
 
+def measured_peaks(reps=20):
+    """Attainable rates on this GPU, for reading the roofline fractions beside
+    the spec peaks: a 2 GiB device-to-device copy (bytes read + written per
+    second) and a 8192^3 bf16 GEMM through torch (the vendor GEMM library)."""
+    src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    log(f"measured peaks: device copy {copy_gbps:.0f} GB/s (read + write), bf16 GEMM 8192^3 {gemm_tflops:.0f} TFLOP/s")
+    return {"device_copy_gbps": copy_gbps, "bf16_gemm_8192_tflops": gemm_tflops,
+            "spec_hbm_gbps": PEAK_HBM_GBS, "spec_bf16_tflops": PEAK_BF16_TFLOPS,
+            "note": "attainable rates measured in this run; the roofline fractions use the spec peaks"}
+
+
 # A lambda so small that no visited block can meet the test (log2 of it is
 # about -997, far below any score gap), but above 0, so the call runs the
 # skip-enabled kernels: their time against the lambda = 0 kernels is the cost
@@ -667,6 +704,8 @@ def main():
         }
         torch.cuda.empty_cache()
 
+    peaks = measured_peaks()
+
     calibration = None
     if not args.no_calibration:
         calibration = bench_calibration()
@@ -696,6 +735,7 @@ def main():
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill70"),
                      "algorithmic_flops": mfma_flops70},
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
 
