@@ -289,7 +289,7 @@ def cpu_oracle_long_prefill(q, k, v, lam, budget_s=6.0, seed=9):
 def measured_peaks(reps=20):
     """Attainable rates on this GPU, for reading the roofline fractions beside
     the spec peaks: a 2 GiB device-to-device copy (bytes read + written per
-    second) and a 8192^3 bf16 GEMM through torch (the vendor GEMM library)."""
+    second) and a 16384^3 bf16 GEMM through torch (the vendor GEMM library)."""
     src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -303,22 +303,22 @@ def measured_peaks(reps=20):
     torch.cuda.synchronize()
     copy_gbps = 2 * src.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
-    n = 8192
+    n = 16384
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    for _ in range(3):
+    for _ in range(8):
         c = a @ b
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(reps):
+    for _ in range(reps // 2):
         c = a @ b
     e1.record()
     torch.cuda.synchronize()
-    gemm_tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    gemm_tflops = 2.0 * n ** 3 * (reps // 2) / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del a, b, c
     torch.cuda.empty_cache()
-    log(f"measured peaks: device copy {copy_gbps:.0f} GB/s (read + write), bf16 GEMM 8192^3 {gemm_tflops:.0f} TFLOP/s")
-    return {"device_copy_gbps": copy_gbps, "bf16_gemm_8192_tflops": gemm_tflops,
+    log(f"measured peaks: device copy {copy_gbps:.0f} GB/s (read + write), bf16 GEMM 16384^3 {gemm_tflops:.0f} TFLOP/s")
+    return {"device_copy_gbps": copy_gbps, "bf16_gemm_16384_tflops": gemm_tflops,
             "spec_hbm_gbps": PEAK_HBM_GBS, "spec_bf16_tflops": PEAK_BF16_TFLOPS,
             "note": "attainable rates measured in this run; the roofline fractions use the spec peaks"}
 
