@@ -124,6 +124,10 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
     const int64_t nkb = (p->L + p->block_k - 1) / p->block_k;
     if (p->L > (int64_t)1 << 30 || nqt * p->Hq * p->B > (int64_t)1 << 31)
         return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
+    // The tile copies address the 64 rows of a K/V block with 32-bit byte
+    // offsets from the block's first row.
+    if (p->k.st > ((int64_t)1 << 24) || p->v.st > ((int64_t)1 << 24))
+        return fail(BLASST_ERR_UNSUPPORTED, "k/v token strides above 2^24 elements are not supported");
 
     blasst::PrefillArgs a{};
     a.q = (const uint16_t *)p->q.ptr;

@@ -64,6 +64,24 @@ def test_prefill_rejects_shapes_and_tiles():
     assert qs.stride(2) == 136
 
 
+def test_prefill_rejects_huge_kv_token_stride():
+    """The tile copies use 32-bit offsets over a 64-row block: K/V token strides
+    above 2^24 elements are refused before any launch (raw ABI call, the fake
+    device pointer is never touched)."""
+    fake = 1 << 20  # 16-byte aligned, never dereferenced
+    def t(st, sh):
+        return _abi._Tensor(fake, 0, 0, sh, st)
+    for kst in ((1 << 24) + 8, 1 << 26):
+        p = _abi._PrefillParams()
+        p.q, p.o = t(128, 128 * 128), t(128, 128 * 128)
+        p.k, p.v = t(kst, 0), t(128, 128 * 128)
+        p.B, p.Hq, p.Hkv, p.L, p.d, p.dv = 1, 2, 1, 128, 128, 128
+        p.causal, p.scale, p.lam, p.tile_q, p.block_k = 1, 0.0, 0.01, 128, 64
+        lib = bl.load_library()
+        assert lib.blasst_prefill(ctypes.byref(p), None) == 2
+        assert "stride" in bl.blasst_last_error()
+
+
 def test_prefill_error_message_names_argument():
     _prefill_err(lam=2.0)
     assert "lambda" in bl.blasst_last_error()
