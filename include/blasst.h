@@ -177,7 +177,15 @@ blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_
 
 /* workspace: caller-owned device buffer of at least the planned size (may be
  * NULL when the planned size is 0).  Calls that share one workspace must be
- * ordered on one stream. */
+ * ordered on one stream.
+ * Errors: INVALID_ARG for null q/k_cache/v_cache/o/seq_lens, B < 0, Lmax < 1,
+ * Hq or Hkv <= 0, Hq % Hkv != 0, lambda outside [0,1) or NaN, a non-finite
+ * scale, window < 0,
+ * num_splits outside 0..nKB, a non-positive stride or a pointer or stride not
+ * aligned to 16 bytes; UNSUPPORTED for other head shapes or dtypes, a latent
+ * cache whose v_cache does not alias k_cache, a latent cache with
+ * Lmax * token stride * 2 >= 2^31 bytes, Lmax > 2^30, or B or Hkv > 65535;
+ * WORKSPACE for a missing or too small workspace; LAUNCH if HIP fails. */
 blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes,
                             void *hip_stream);
 
