@@ -1,0 +1,109 @@
+"""GPU parity over seeded random configurations: shapes, GQA ratios, head
+dims, tiles, ragged lengths, split counts, windows, sink seeds and paged
+caches drawn from fixed seeds, each checked against the fp64 oracle with the
+parity bar of ``parity.py``.  The draws are deterministic; each case prints
+its configuration before it runs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_fa_amd import blasst_decode_plan, inputs
+from parity import (check_decisions, check_output, f64, gpu_decode, gpu_decode_paged, gpu_prefill,
+                    lambda_for, say, SPARSITY_ABS)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _prefill_cfg(i):
+    r = np.random.default_rng(5000 + i)
+    d = int(r.choice([64, 128]))
+    tile = int(r.choice([64, 128]))
+    causal = bool(r.random() < 0.75)
+    L = int(r.integers(1, 700))
+    window = int(r.integers(1, L + 1)) if causal and r.random() < 0.35 else 0
+    return dict(B=int(r.integers(1, 3)), Hkv=int(r.choice([1, 2])), G=int(r.choice([1, 2, 4])), L=L, d=d,
+                tile=tile, causal=causal, window=window, target=float(r.choice([0.0, 0.3, 0.5, 0.7, 0.85])))
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_prefill(i):
+    c = _prefill_cfg(i)
+    say(f"[random prefill {i}] {c}")
+    q, k, v = inputs.prefill_inputs(c["B"], c["G"] * c["Hkv"], c["Hkv"], c["L"], c["d"], device=DEV,
+                                    seed=6000 + i)
+    lam = 0.0
+    if c["target"] > 0:
+        _, _, gap0, _ = gpu_prefill(q, k, v, causal=c["causal"], lam=0.0, tile_q=c["tile"], window=c["window"])
+        lam, _ = lambda_for(gap0, c["target"])
+    o, skip, gap, cnt = gpu_prefill(q, k, v, causal=c["causal"], lam=lam, tile_q=c["tile"], window=c["window"])
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=c["causal"], lam=lam, tile_q=c["tile"], block_k=64,
+                         window=c["window"])
+    nb = check_decisions(skip.cpu().numpy(), gap.cpu().numpy(), ref["skip"], ref["gap"], lam)
+    check_output(o.cpu().numpy(), ref["o"], f"random prefill {i}")
+    assert cnt[0] == ref["visited"] and abs(cnt[1] - ref["skipped"]) <= nb
+
+
+def _decode_cfg(i, mla):
+    r = np.random.default_rng(7000 + i + (100 if mla else 0))
+    Lmax = int(r.integers(64, 1500))
+    B = int(r.integers(1, 3 if mla else 5))
+    lens = [int(x) for x in r.integers(1, Lmax + 1, size=B)]
+    lens[0] = Lmax
+    return dict(B=B, Lmax=Lmax, lens=lens, d=int(r.choice([64, 128])),
+                Hkv=1 if mla else int(r.choice([1, 2])), G=128 if mla else int(r.choice([1, 2, 4, 8, 16])),
+                splits=min(int(r.choice([0, 1, 2, 3, 7])), -(-Lmax // 64)),  # at most one split per block
+                window=int(r.integers(1, Lmax + 1)) if r.random() < 0.3 else 0,
+                sink_seed=bool(r.random() < 0.3), page=int(r.choice([0, 0, 16, 32, 64])),
+                target=float(r.choice([0.0, 0.4, 0.7])))
+
+
+def _decode_case(i, mla):
+    c = _decode_cfg(i, mla)
+    say(f"[random {'latent' if mla else 'gqa'} decode {i}] {c}")
+    if mla:
+        q, kc, _, lens = inputs.decode_inputs(c["B"], 128, 1, c["Lmax"], 576, 512, n_random=8, mla=True,
+                                              device=DEV, seed=8000 + i, seq_lens=c["lens"])
+        vc, dv = kc, 512
+    else:
+        q, kc, vc, _ = inputs.decode_inputs(c["B"], c["G"] * c["Hkv"], c["Hkv"], c["Lmax"], c["d"], device=DEV,
+                                            seed=8000 + i)
+        lens = torch.tensor(c["lens"], dtype=torch.int32, device=DEV)
+        dv = None
+    kw = dict(num_splits=c["splits"], dv=dv, window=c["window"], sink_seed=c["sink_seed"])
+    lam = 0.0
+    if c["target"] > 0:
+        _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, **kw)
+        lam, _ = lambda_for(gap0, c["target"])
+    if c["page"]:
+        caches = [kc] if mla else [kc, vc]
+        pools, table = inputs.paged_pool(caches, lens, c["page"], seed=9000 + i, spare_pages=2)
+        kp = pools[0]
+        vp = kp if mla else pools[1]
+        o, skip, gap, cnt = gpu_decode_paged(q, kp, vp, table, lens, c["Lmax"], lam=lam, **kw)
+        oc = gpu_decode(q, kc, vc, lens, lam=lam, **kw)[0]
+        assert torch.equal(o, oc), "paged call differs from the contiguous one"
+    else:
+        o, skip, gap, cnt = gpu_decode(q, kc, vc, lens, lam=lam, **kw)
+    S, _ = blasst_decode_plan(q, kc, vc, lens, lam=lam, num_splits=c["splits"], dv=dv, window=c["window"])
+    kk = f64(kc)
+    vv = kk[..., :dv] if mla else f64(vc)
+    ref = oracle.decode(f64(q), kk, vv, lens.cpu().numpy(), lam=lam, block_k=64, num_splits=S,
+                        window=c["window"], sink_seed=c["sink_seed"])
+    nb = check_decisions(skip.cpu().numpy(), gap.cpu().numpy(), ref["skip"], ref["gap"], lam)
+    check_output(o.cpu().numpy(), ref["o"], f"random decode {i}")
+    gs = skip.cpu().numpy()
+    g_frac = (gs == 1).sum() / max(1, (gs != 255).sum())
+    assert abs(g_frac - ref["skipped"] / max(1, ref["visited"])) <= SPARSITY_ABS
+    assert cnt[0] == ref["visited"] and abs(cnt[1] - ref["skipped"]) <= nb
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_gqa_decode(i):
+    _decode_case(i, mla=False)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_latent_decode(i):
+    _decode_case(i, mla=True)
