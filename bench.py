@@ -475,7 +475,7 @@ def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names
     return S, res
 
 
-def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8), oracle_cpu=False):
+def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8), oracle_cpu=False, window_leg=True):
     (B, Hq, Hkv, L, d), (q, k, v) = long_prefill_workload()
     cal = calibrate_prefill(q, k, v, list(targets))
     out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
@@ -496,7 +496,8 @@ def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8), oracle_cpu=F
     for r in rows:
         r["speedup_vs_dense"] = dense_ms / r["ms"]
     cpu = cpu_oracle_long_prefill(q, k, v, cal[0.7][0]) if oracle_cpu and 0.7 in cal else None
-    return rows, window_prefill(q, k, v, out, 4096, steps, warmup), cpu
+    win = window_prefill(q, k, v, out, 4096, steps, warmup) if window_leg else None
+    return rows, win, cpu
 
 
 def window_prefill(q, k, v, out, W, steps, warmup):
@@ -584,7 +585,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and long-prefill sections")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "decode70", "decode_dense", "mla70",
-                                       "mla_dense", "decode_paged70", "mla_paged70"],
+                                       "mla_dense", "decode_paged70", "mla_paged70", "long_prefill70",
+                                       "long_prefill_dense"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -604,6 +606,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only in ("long_prefill70", "long_prefill_dense"):
+        t = (0.7,) if args.only == "long_prefill70" else ()
+        rows, _, _ = bench_long_prefill(steps, warmup, targets=t, window_leg=False)
+        print(json.dumps({"only": args.only, "result": rows}, default=str), flush=True)
+        return
     if args.only in ("decode_paged70", "mla_paged70"):
         fn = bench_decode if args.only == "decode_paged70" else bench_mla
         r = fn(steps, warmup, names=(), paged_names=("paged_s70",))
