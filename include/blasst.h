@@ -9,7 +9,8 @@
  * row max m; for every key block it forms the block-local row max m~ and skips
  * the block when m~ - m < ln(lambda).  A skipped block does no exponential, no
  * V-block load and no P.V product.  The threshold follows lambda = a / L, with
- * a fitted per target sparsity (page 1 "Calibração Automática"; BLASST reading
+ * a fitted per target sparsity (BLASST summary, gist.science/pt/paper/2512.12087,
+ * section 2 "Calibração Automática"; BLASST reading
  * notes, papers.lqhl.me/papers/BLASST-MLSys26, "关键观察" observation 2).
  *
  * Conventions shared by every entry point

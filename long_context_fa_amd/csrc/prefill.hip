@@ -6,7 +6,7 @@
 // block, form the block-local row max m~ from the scores the FlashAttention
 // loop already computes; when m~ - m < ln(lambda) against the running row max
 // m the block is skipped: no exponential, no V-block load, no P.V product.
-// Prefill is compute bound (page 1 section 3; Hindi explainer, section 2
+// Prefill is compute bound (BLASST summary, section 3; Hindi explainer, section 2
 // "kernel optimisation"), so the savings are the exp work and the P.V MFMAs;
 // here the V load is also predicated on the decision.
 //

@@ -113,7 +113,7 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
     for (int64_t j = j_begin; j < j_end; ++j) {
         int64_t c0 = j * bc;
         int any = 0;
-        /* Scores of the block and the block-local row max m~ (page 1, sec. 2). */
+        /* Scores of the block and the block-local row max m~ (BLASST summary, section 2). */
         for (int64_t r = 0; r < R; ++r) {
             const double *qr = q + r * q_stride;
             mt[r] = -INFINITY;
@@ -157,7 +157,7 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
                 g = dr;
         }
         gap[jj] = g;
-        /* Skip test (page 1, sec. 2; page 4, sec. 2): m~ - m < ln(lambda). */
+        /* Skip test (BLASST summary, section 2; Hindi explainer, section 2): m~ - m < ln(lambda). */
         if (g < lnlam) {
             skip[jj] = 1;
             ++skipped;
@@ -411,8 +411,8 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
 }
 
 /*
- * Threshold calibration (page 1 sec. 2 "Calibração Automática"; page 3
- * "关键观察" observation 2 and "核心方法"): lambda = a / L, with a fitted per
+ * Threshold calibration (BLASST summary, section 2 "Calibração Automática";
+ * BLASST reading notes, "关键观察" observation 2 and "核心方法"): lambda = a / L, with a fitted per
  * target sparsity on calibration data.
  *
  * oracle_lambda_for_target: given the gaps g of the visited (unit, block)
