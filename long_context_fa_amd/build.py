@@ -40,6 +40,22 @@ def _compile(src, verbose):
     return obj
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "c_abi_demo.c")
+DEMO_OUT = os.path.join(ROOT, "tests", "c_abi_demo")
+
+
+def build_c_demo(verbose=False):
+    """The plain-C program of the tests that calls libblasst.so through the C
+    ABI alone (no Python, no torch); built next to its source."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", "/opt/rocm/include",
+           DEMO_SRC, "-L", HERE, "-lblasst", "-L", "/opt/rocm/lib", "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../long_context_fa_amd", "-Wl,-rpath,/opt/rocm/lib", "-o", DEMO_OUT]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return DEMO_OUT
+
+
 def build(verbose=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
@@ -50,6 +66,7 @@ def build(verbose=False):
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, OUT)
+    build_c_demo(verbose)
     return OUT
 
 
