@@ -500,6 +500,38 @@ def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8), oracle_cpu=F
     return rows, win, cpu
 
 
+def bench_prefill_lengths(steps, warmup, lengths=(2048, 4096, 8192, 16384, 32768), tokens=65536):
+    """The 70% speedup over dense as a function of sequence length: causal GQA
+    prefill (32 query / 8 KV heads, d = 128, the 8K workload's input recipe)
+    at a fixed 65536 tokens per launch (B = tokens / L), lambda calibrated to
+    70% block sparsity at each length."""
+    rows = []
+    for L in lengths:
+        B, Hq, Hkv, d = tokens // L, 32, 8, 128
+        q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda",
+                                        seed=1100 + L // 1024)
+        lam70, _ = calibrate_prefill(q, k, v, [0.7])[0.7]
+        out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
+        dense_flops = 4.0 * B * Hq * L * L * d / 2
+        row = {"L": L, "B": B, "lambda70": lam70}
+        for name, lam in (("s70", lam70), ("dense", 0.0)):
+            def pf(cnt=None, lam=lam):
+                return bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
+            mean_ms, _, _ = time_calls(pf, steps, warmup)
+            vis, skp = counts(lambda c: pf(c))
+            mfma = (vis + (vis - skp)) * 2.0 * 128 * 64 * d
+            row[name] = {"ms": mean_ms, "sparsity": skp / vis,
+                         "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12,
+                         "mfma_util_executed": mfma / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        row["speedup70_vs_dense"] = row["dense"]["ms"] / row["s70"]["ms"]
+        log(f"prefill L={L} B={B}: dense {row['dense']['ms']:.3f} ms, 70% {row['s70']['ms']:.3f} ms "
+            f"(sparsity {row['s70']['sparsity']:.4f}), speedup {row['speedup70_vs_dense']:.3f}")
+        rows.append(row)
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def window_prefill(q, k, v, out, W, steps, warmup):
     """The same prefill with a sliding window of W keys, at the 70% lambda of
     the windowed gaps and at lambda = 0."""
@@ -586,7 +618,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "decode70", "decode_dense", "mla70",
                                        "mla_dense", "decode_paged70", "mla_paged70", "long_prefill70",
-                                       "long_prefill_dense"],
+                                       "long_prefill_dense", "prefill_lengths"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -606,6 +638,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only == "prefill_lengths":
+        print(json.dumps({"only": args.only, "result": bench_prefill_lengths(steps, warmup)}, default=str),
+              flush=True)
+        return
     if args.only in ("long_prefill70", "long_prefill_dense"):
         t = (0.7,) if args.only == "long_prefill70" else ()
         rows, _, _ = bench_long_prefill(steps, warmup, targets=t, window_leg=False)
