@@ -66,6 +66,9 @@ class _CalibTable(ctypes.Structure):
 
 _lib = None
 
+# The parameter structs above mirror include/blasst.h at this ABI version.
+ABI_VERSION = 2
+
 
 def library_path():
     return os.environ.get("BLASST_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
@@ -111,6 +114,10 @@ def load_library():
     lib.blasst_last_error.argtypes = []
     lib.blasst_abi_version.restype = ctypes.c_int
     lib.blasst_abi_version.argtypes = []
+    found = lib.blasst_abi_version()
+    if found != ABI_VERSION:
+        raise ImportError(f"{path} implements C ABI version {found}; this binding's structs are version "
+                          f"{ABI_VERSION}: rebuild the library")
     _lib = lib
     return lib
 

@@ -249,3 +249,12 @@ def test_calibrate_fit_matches_oracle():
     Ls = [4096, 8192, 16384, 32768, 65536]
     lams = [1.1e-3, 6e-4, 2.7e-4, 1.4e-4, 6.9e-5]
     assert abs(bl.blasst_calibrate_fit(lams, Ls) - oracle.fit_a(lams, Ls)) < 1e-12
+
+
+def test_binding_structs_match_the_header_abi_version():
+    """The ctypes structs are written for one ABI version; the binding
+    refuses a library of another (checked in load_library)."""
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "blasst.h")).read()
+    v = int(re.search(r"#define BLASST_ABI_VERSION (\d+)", hdr).group(1))
+    assert _abi.ABI_VERSION == v
+    assert _abi.load_library().blasst_abi_version() == v
