@@ -122,7 +122,11 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
     const int64_t nqt = (p->L + p->tile_q - 1) / p->tile_q;
     const int64_t nkb = (p->L + p->block_k - 1) / p->block_k;
-    if (p->L > (int64_t)1 << 30 || nqt * p->Hq * p->B > (int64_t)1 << 31)
+    // One workgroup per (query tile, head, batch), at most 2^31 - 1 of them
+    // (B, Hq and the count all fit an int).  The bound is divided out so that
+    // no product of caller sizes overflows.
+    const int64_t max_units = INT32_MAX;
+    if (p->L > (int64_t)1 << 30 || p->Hq > max_units || p->B > max_units / (nqt * p->Hq))
         return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
     // The tile copies address the 64 rows of a K/V block with 32-bit byte
     // offsets from the block's first row.
@@ -208,6 +212,8 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
                     "decode supports dqk = dv in {64,128} with Hq/Hkv <= 16, or dqk=576, dv=512, Hkv=1, Hq=128");
     if (kind == KIND_MLA && p->v_cache.ptr != p->k_cache.ptr)
         return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs v_cache to alias k_cache");
+    if (p->Lmax > (int64_t)1 << 30 || p->B > 65535 || p->Hkv > 65535)
+        return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
     if (pg) {
         if (pg->page_table == nullptr)
             return fail(BLASST_ERR_INVALID_ARG, "page_table: null pointer");
@@ -220,13 +226,11 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
             return fail(BLASST_ERR_INVALID_ARG, "page_table_stride must be >= ceil(Lmax / page_size)");
     }
     // the latent kernel addresses a sequence's (or a page's) cache rows with
-    // 32-bit byte offsets
-    const int64_t span = pg ? std::min(pg->page_size, p->Lmax) : p->Lmax;
-    if (kind == KIND_MLA && span * p->k_cache.st * 2 >= ((int64_t)1 << 31))
+    // 32-bit byte offsets: rows * token stride * 2 < 2^31, tested by division
+    const int64_t span = std::max<int64_t>(pg ? std::min(pg->page_size, p->Lmax) : p->Lmax, 1);
+    if (kind == KIND_MLA && p->k_cache.st > (((int64_t)1 << 31) - 1) / (2 * span))
         return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs rows * token stride * 2 < 2^31 bytes "
                                             "(rows = Lmax, or the page size of a paged cache)");
-    if (p->Lmax > (int64_t)1 << 30 || p->B > 65535 || p->Hkv > 65535)
-        return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
     return BLASST_OK;
 }
 

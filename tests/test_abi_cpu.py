@@ -82,6 +82,34 @@ def test_prefill_rejects_huge_kv_token_stride():
         assert "stride" in bl.blasst_last_error()
 
 
+def test_size_limits_reject_overflowing_products():
+    """Absurd sizes are refused as too large, with no overflowing product of
+    caller sizes on the way (raw ABI calls; the fake device pointer is never
+    touched): prefill unit counts past 2^31 - 1, and a latent cache whose
+    rows * token stride * 2 does not fit 32 bits (checked by the planner)."""
+    fake = 1 << 20
+    lib = bl.load_library()
+    def t(st, sh, sb=0):
+        return _abi._Tensor(fake, 0, sb, sh, st)
+    for B, Hq, L in ((1 << 40, 1 << 40, 128), (1 << 31, 1, 64), (1 << 20, 1 << 20, 1 << 20), (1, 1 << 62, 128)):
+        p = _abi._PrefillParams()
+        p.q = p.k = p.v = p.o = t(128, 128 * 128)
+        p.B, p.Hq, p.Hkv, p.L, p.d, p.dv = B, Hq, 1, L, 128, 128
+        p.causal, p.scale, p.lam, p.tile_q, p.block_k = 1, 0.0, 0.01, 128, 64
+        assert lib.blasst_prefill(ctypes.byref(p), None) == 2, (B, Hq, L)
+        assert "too large" in bl.blasst_last_error()
+    for kst, lmax in ((1 << 40, 4096), (1 << 62, 1), (576, 1 << 22)):
+        p = _abi._DecodeParams()
+        p.q, p.o = t(0, 576, 128 * 576), t(0, 512, 128 * 512)
+        p.k_cache = p.v_cache = t(kst, 0)
+        p.seq_lens = fake
+        p.B, p.Hq, p.Hkv, p.Lmax, p.dqk, p.dv = 1, 128, 1, lmax, 576, 512
+        p.lam, p.block_k = 0.01, 64
+        splits, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+        assert lib.blasst_decode_plan(ctypes.byref(p), ctypes.byref(splits), ctypes.byref(ws)) == 2, (kst, lmax)
+        assert "2^31" in bl.blasst_last_error()
+
+
 def test_prefill_error_message_names_argument():
     _prefill_err(lam=2.0)
     assert "lambda" in bl.blasst_last_error()
