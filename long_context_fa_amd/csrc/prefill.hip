@@ -85,7 +85,12 @@ void prefill_kernel(const PrefillArgs a)
 
     // Unit mapping.  Longest (latest) query tiles first.  Consecutive
     // workgroups go to the 8 XCDs in turn; when the KV groups divide evenly,
-    // XCD x only sees KV groups x, x+8, ... so their K/V stay in its L2.
+    // an XCD serves one KV group in each of four phases of the tile order
+    // (of equal work for a causal head, whose tile t visits ~t+1 blocks), so
+    // that group's K/V stays in its L2.  The group changes with the phase --
+    // XCD x serves groups x, x^4, x^2, x^6 (+8k) in turn -- so that groups
+    // that skip less do not all land on one XCD: each XCD carries a quarter
+    // of four groups' work.
     const int G = a.Hq / a.Hkv;
     const int nkvg = a.B * a.Hkv;
     int t, h, b;
@@ -96,7 +101,14 @@ void prefill_kernel(const PrefillArgs a)
             const int per_t = (nkvg / 8) * G;
             t = a.nqt - 1 - s / per_t;
             const int r = s % per_t;
-            const int kvg = (r / G) * 8 + xcd;
+            // Phase edges: for a causal head the work of tiles >= t is
+            // ~nqt^2 - t^2, so the quarters end at nqt * sqrt(3/4, 1/2, 1/4).
+            const int nq = a.nqt;
+            const int t1 = CAUSAL ? (int)(((int64_t)nq * 222) >> 8) : (int)(((int64_t)nq * 3) >> 2);
+            const int t2 = CAUSAL ? (int)(((int64_t)nq * 181) >> 8) : nq >> 1;
+            const int t3 = CAUSAL ? nq >> 1 : nq >> 2;
+            const int c = t >= t1 ? 0 : t >= t2 ? 4 : t >= t3 ? 2 : 6;
+            const int kvg = (r / G) * 8 + (xcd ^ c);
             b = kvg / a.Hkv;
             h = (kvg % a.Hkv) * G + r % G;
         } else {
