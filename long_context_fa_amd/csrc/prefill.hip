@@ -346,8 +346,8 @@ void prefill_kernel(const PrefillArgs a)
     //   S_j and its row max are in registers and its vote is in LDS;
     //   K_{j+1} and (if block j-1 executed) V_{j-1} are in flight;
     //   P_{j-1} is in registers if block j-1 executed.
-    // Iteration j: barrier; request K_{j+2} (no decision needed) and read
-    // the votes on block j; request V_j if it executes; then O += V_{j-1}
+    // Iteration j: barrier; read the votes on block j and request K_{j+2}
+    // (no decision needed); request V_j if it executes; then O += V_{j-1}
     // P_{j-1} (MFMA), the softmax of block j (VALU) and the scores of block
     // j+1 (MFMA); finally vote on block j+1.  The other workgroup on the
     // compute unit fills the matrix / vector gaps.  By the barrier of
@@ -360,17 +360,20 @@ void prefill_kernel(const PrefillArgs a)
     auto iter = [&](int j, f32x16(&sc)[2], float mtc, f32x16(&sn)[2], float &mtn) {
         wait_vmcnt<0>();
         lds_barrier(); // votes_j, K_{j+1}, V_{j-1} visible; iteration j-1 done everywhere
-        if (j + 2 < nvis)
-            copy_tile(kp, a.k_st, koff, j + 2, kbuf(j)); // K ring refill
         const int par = j & 1;
-        bool skip = false;
+        // The votes are read before the K refill is issued, so that their LDS
+        // latency passes while the copies are accepted.
+        int all = 1;
         if (SKIP) {
-            int all = 1;
 #pragma unroll
             for (int i = 0; i < NW; ++i)
                 all &= vote[par][i];
-            skip = __builtin_amdgcn_readfirstlane(all) != 0; // uniform across the workgroup
         }
+        if (j + 2 < nvis)
+            copy_tile(kp, a.k_st, koff, j + 2, kbuf(j)); // K ring refill
+        bool skip = false;
+        if (SKIP)
+            skip = __builtin_amdgcn_readfirstlane(all) != 0; // uniform across the workgroup
         if (want_maps && tid == 0) {
             float g = neg_inf();
 #pragma unroll
