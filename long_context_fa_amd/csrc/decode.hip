@@ -69,8 +69,13 @@ void decode_gqa_kernel(const DecodeArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, grp = lane >> 4;
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int S = a.num_splits, G = a.G;
+    // Split index rotated by the sequence: workgroups reach the 8 XCDs in
+    // linear-id order, and with an unrotated split index XCD x would only see
+    // splits x mod S (the first split of a sequence, seeded by the sink
+    // block, skips far more than the others).
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int s = (int)((blockIdx.x + blockIdx.z) % (unsigned)S);
     const bool want_maps = a.skip_map != nullptr || a.gap_map != nullptr;
 
     int len = a.seq_lens[b];
