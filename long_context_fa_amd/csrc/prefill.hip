@@ -97,10 +97,14 @@ void prefill_kernel(const PrefillArgs a)
     {
         const int k = blockIdx.x;
         if (nkvg % 8 == 0) {
+            // Group-major within an XCD: with several KV groups per XCD
+            // (B * Hkv > 8), column j -- one group per phase -- is walked
+            // longest tile first before column j + 1, so the XCD's L2 holds
+            // one group's K/V at a time and the grid still ends on short tiles.
             const int xcd = k & 7, s = k >> 3;
-            const int per_t = (nkvg / 8) * G;
-            t = a.nqt - 1 - s / per_t;
-            const int r = s % per_t;
+            const int per_col = a.nqt * G;
+            const int jcol = s / per_col, rem = s % per_col;
+            t = a.nqt - 1 - rem / G;
             // Phase edges: for a causal head the work of tiles >= t is
             // ~nqt^2 - t^2, so the quarters end at nqt * sqrt(3/4, 1/2, 1/4).
             const int nq = a.nqt;
@@ -108,9 +112,9 @@ void prefill_kernel(const PrefillArgs a)
             const int t2 = CAUSAL ? (int)(((int64_t)nq * 181) >> 8) : nq >> 1;
             const int t3 = CAUSAL ? nq >> 1 : nq >> 2;
             const int c = t >= t1 ? 0 : t >= t2 ? 4 : t >= t3 ? 2 : 6;
-            const int kvg = (r / G) * 8 + (xcd ^ c);
+            const int kvg = jcol * 8 + (xcd ^ c);
             b = kvg / a.Hkv;
-            h = (kvg % a.Hkv) * G + r % G;
+            h = (kvg % a.Hkv) * G + rem % G;
         } else {
             const int per_t = a.Hq * a.B;
             t = a.nqt - 1 - k / per_t;

@@ -124,6 +124,22 @@ def _sampled(q, k, v, *, lam, tile_q, units, what, window=0):
     return cnt
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,tile_q,causal", [
+    (1, 8, 8, 700, 64, 64, True),       # 8 KV groups: one per XCD, 11 tiles over the four phases
+    (2, 16, 4, 520, 128, 128, True),    # B * Hkv = 8 with GQA 4
+    (2, 16, 8, 900, 128, 128, True),    # 16 groups: two per XCD
+    (1, 16, 8, 600, 128, 64, False),    # non-causal phase edges
+])
+def test_parity_xcd_mapped_units_full(B, Hq, Hkv, L, d, tile_q, causal):
+    """When B * Hkv is a multiple of 8 the kernel maps workgroups to (tile,
+    head, batch) through the XCD-aware rotation; every unit is checked
+    against the oracle, so a unit computed twice or never fails here."""
+    q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, device=DEV, seed=40 + L + d)
+    _, _, gap0, _ = gpu_prefill(q, k, v, causal=causal, lam=0.0, tile_q=tile_q)
+    lam, _ = lambda_for(gap0, 0.6)
+    _run_full(q, k, v, causal=causal, lam=lam, tile_q=tile_q, what=f"xcd-mapped {B}x{Hq}/{Hkv}x{L}x{d}")
+
+
 def test_parity_gqa_prefill_8k_full_size():
     """1x32/8x8192x128, tile 128: lambda calibrated on the GPU gap map for 70%."""
     q, k, v = inputs.prefill_inputs(1, 32, 8, 8192, 128, n_random=6, local_window=1, device=DEV, seed=1001)
