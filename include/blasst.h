@@ -95,8 +95,9 @@ typedef struct {
  * Hq % Hkv != 0, lambda outside [0,1) or NaN, window < 0 or a window without
  * causal masking, a non-positive stride or a
  * pointer not aligned to 16 bytes with a token stride not a multiple of 8
- * elements; UNSUPPORTED for other d, dv, tile or dtype, for L > 2^30, and
- * for k or v token strides above 2^24 elements; LAUNCH if HIP fails.
+ * elements; UNSUPPORTED for other d, dv, tile or dtype, for L > 2^30, for
+ * B * Hq * nQT above 2^31 - 1 (one workgroup each), and for k or v token
+ * strides above 2^24 elements; LAUNCH if HIP fails.
  * L = 0 or B = 0 is a valid no-op: only the scalar arguments are checked and
  * the tensor pointers may be null.
  */
