@@ -90,7 +90,8 @@ void prefill_kernel(const PrefillArgs a)
     // that group's K/V stays in its L2.  The group changes with the phase --
     // XCD x serves groups x, x^4, x^2, x^6 (+8k) in turn -- so that groups
     // that skip less do not all land on one XCD: each XCD carries a quarter
-    // of four groups' work.
+    // of four groups' work.  With fewer than 8 groups, each group is spread
+    // over 8 / (B * Hkv) XCDs by head slices, with the same rotation.
     const int G = a.Hq / a.Hkv;
     const int nkvg = a.B * a.Hkv;
     int t, h, b;
@@ -115,6 +116,22 @@ void prefill_kernel(const PrefillArgs a)
             const int kvg = jcol * 8 + (xcd ^ c);
             b = kvg / a.Hkv;
             h = (kvg % a.Hkv) * G + rem % G;
+        } else if (8 % nkvg == 0 && G % (8 / nkvg) == 0) {
+            // Fewer than 8 KV groups (B * Hkv in {1, 2, 4}): each group is
+            // spread over 8 / (B * Hkv) XCDs, each taking an equal slice of
+            // its query heads, so an XCD's L2 holds one group's K/V.  The
+            // group of a slice rotates with the same four phases as above.
+            const int xcd = k & 7, s = k >> 3;
+            const int gh = G * nkvg / 8; // heads per XCD
+            t = a.nqt - 1 - s / gh;
+            const int nq = a.nqt;
+            const int t1 = CAUSAL ? (int)(((int64_t)nq * 222) >> 8) : (int)(((int64_t)nq * 3) >> 2);
+            const int t2 = CAUSAL ? (int)(((int64_t)nq * 181) >> 8) : nq >> 1;
+            const int t3 = CAUSAL ? nq >> 1 : nq >> 2;
+            const int p = t >= t1 ? 0 : t >= t2 ? 1 : t >= t3 ? 2 : 3;
+            const int kvg = (xcd + p) % nkvg, slice = xcd / nkvg;
+            b = kvg / a.Hkv;
+            h = (kvg % a.Hkv) * G + slice * gh + s % gh;
         } else {
             const int per_t = a.Hq * a.B;
             t = a.nqt - 1 - k / per_t;

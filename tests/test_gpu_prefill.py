@@ -129,11 +129,16 @@ def _sampled(q, k, v, *, lam, tile_q, units, what, window=0):
     (2, 16, 4, 520, 128, 128, True),    # B * Hkv = 8 with GQA 4
     (2, 16, 8, 900, 128, 128, True),    # 16 groups: two per XCD
     (1, 16, 8, 600, 128, 64, False),    # non-causal phase edges
+    (1, 32, 4, 700, 64, 64, True),      # 4 KV groups, each over 2 XCDs
+    (1, 16, 2, 600, 128, 128, True),    # 2 groups over 4 XCDs each
+    (1, 8, 1, 500, 128, 128, True),     # MQA: one group over all 8 XCDs
+    (2, 16, 1, 520, 64, 64, False),     # B * Hkv = 2, non-causal
 ])
 def test_parity_xcd_mapped_units_full(B, Hq, Hkv, L, d, tile_q, causal):
-    """When B * Hkv is a multiple of 8 the kernel maps workgroups to (tile,
-    head, batch) through the XCD-aware rotation; every unit is checked
-    against the oracle, so a unit computed twice or never fails here."""
+    """When B * Hkv is a multiple or a divisor of 8 the kernel maps
+    workgroups to (tile, head, batch) through the XCD-aware rotation; every
+    unit is checked against the oracle, so a unit computed twice or never
+    fails here."""
     q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, device=DEV, seed=40 + L + d)
     _, _, gap0, _ = gpu_prefill(q, k, v, causal=causal, lam=0.0, tile_q=tile_q)
     lam, _ = lambda_for(gap0, 0.6)
