@@ -62,6 +62,19 @@ __device__ __forceinline__ int pswz(int row)
     return ((e & 1) << 2) | ((e >> 1) & 3);
 }
 
+// Phase 0..3 of query tile t in the unit order: four stretches of equal work.
+// A causal head's tiles >= t carry work ~nqt^2 - t^2, so the quarters end at
+// nqt * sqrt(3/4), sqrt(1/2), sqrt(1/4); without causal masking, at 3/4, 1/2,
+// 1/4 of nqt.
+template <bool CAUSAL>
+__device__ __forceinline__ int tile_phase(int t, int nqt)
+{
+    const int t1 = CAUSAL ? (int)(((int64_t)nqt * 222) >> 8) : (int)(((int64_t)nqt * 3) >> 2);
+    const int t2 = CAUSAL ? (int)(((int64_t)nqt * 181) >> 8) : nqt >> 1;
+    const int t3 = CAUSAL ? nqt >> 1 : nqt >> 2;
+    return t >= t1 ? 0 : t >= t2 ? 1 : t >= t3 ? 2 : 3;
+}
+
 template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16>
 __global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, 2)))
 void prefill_kernel(const PrefillArgs a)
@@ -86,7 +99,7 @@ void prefill_kernel(const PrefillArgs a)
     // Unit mapping.  Longest (latest) query tiles first.  Consecutive
     // workgroups go to the 8 XCDs in turn; when the KV groups divide evenly,
     // an XCD serves one KV group in each of four phases of the tile order
-    // (of equal work for a causal head, whose tile t visits ~t+1 blocks), so
+    // (of equal work, tile_phase), so
     // that group's K/V stays in its L2.  The group changes with the phase --
     // XCD x serves groups x, x^4, x^2, x^6 (+8k) in turn -- so that groups
     // that skip less do not all land on one XCD: each XCD carries a quarter
@@ -106,13 +119,8 @@ void prefill_kernel(const PrefillArgs a)
             const int per_col = a.nqt * G;
             const int jcol = s / per_col, rem = s % per_col;
             t = a.nqt - 1 - rem / G;
-            // Phase edges: for a causal head the work of tiles >= t is
-            // ~nqt^2 - t^2, so the quarters end at nqt * sqrt(3/4, 1/2, 1/4).
-            const int nq = a.nqt;
-            const int t1 = CAUSAL ? (int)(((int64_t)nq * 222) >> 8) : (int)(((int64_t)nq * 3) >> 2);
-            const int t2 = CAUSAL ? (int)(((int64_t)nq * 181) >> 8) : nq >> 1;
-            const int t3 = CAUSAL ? nq >> 1 : nq >> 2;
-            const int c = t >= t1 ? 0 : t >= t2 ? 4 : t >= t3 ? 2 : 6;
+            const int p = tile_phase<CAUSAL>(t, a.nqt);
+            const int c = ((p & 1) << 2) | (p & 2); // 0, 4, 2, 6
             const int kvg = jcol * 8 + (xcd ^ c);
             b = kvg / a.Hkv;
             h = (kvg % a.Hkv) * G + rem % G;
@@ -124,11 +132,7 @@ void prefill_kernel(const PrefillArgs a)
             const int xcd = k & 7, s = k >> 3;
             const int gh = G * nkvg / 8; // heads per XCD
             t = a.nqt - 1 - s / gh;
-            const int nq = a.nqt;
-            const int t1 = CAUSAL ? (int)(((int64_t)nq * 222) >> 8) : (int)(((int64_t)nq * 3) >> 2);
-            const int t2 = CAUSAL ? (int)(((int64_t)nq * 181) >> 8) : nq >> 1;
-            const int t3 = CAUSAL ? nq >> 1 : nq >> 2;
-            const int p = t >= t1 ? 0 : t >= t2 ? 1 : t >= t3 ? 2 : 3;
+            const int p = tile_phase<CAUSAL>(t, a.nqt);
             const int kvg = (xcd + p) % nkvg, slice = xcd / nkvg;
             b = kvg / a.Hkv;
             h = (kvg % a.Hkv) * G + slice * gh + s % gh;
