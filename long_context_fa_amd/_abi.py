@@ -158,6 +158,41 @@ def _check(status, func):
         raise BlasstError(status, func)
 
 
+# Host-side argument checks.  The library validates sizes, strides and scalars
+# itself, but it receives bare pointers: it cannot see a host tensor, a tensor
+# on another GPU, a K/V shorter than the query length, a map or counter buffer
+# of the wrong type or size, or a length array of the wrong width.  Those are
+# refused here, before any launch, with ValueError.
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_map(t, name, dtype, numel):
+    if t is None:
+        return
+    _need(t.dtype == dtype, f"{name} must be {dtype} (got {t.dtype})")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.numel() >= numel, f"{name} needs at least {numel} elements (got {t.numel()})")
+
+
+def _check_counters(t):
+    if t is None:
+        return
+    _need(t.dtype in (torch.int64, getattr(torch, "uint64", torch.int64)),
+          f"counters must be a 64-bit integer tensor (got {t.dtype})")
+    _need(t.is_contiguous() and t.numel() >= 2, "counters needs 2 contiguous elements (visited, skipped)")
+
+
+def _check_devices(ref, **tensors):
+    """Every tensor that is passed must live on the GPU of ``ref``."""
+    _need(ref.is_cuda, f"tensors must be on a GPU (got {ref.device})")
+    for name, t in tensors.items():
+        if t is not None:
+            _need(t.device == ref.device, f"{name} is on {t.device}, the query on {ref.device}")
+
+
 def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, scale=None, out=None,
                    out_dtype=torch.float32, skip_map=None, gap_map=None, counters=None, stream=None,
                    window=0):
@@ -170,22 +205,65 @@ def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, sca
     ``counters`` uint64-compatible int64 tensor of 2 elements (visited, skipped),
     accumulated (zero it first).
     """
-    B, Hq, L, d = q.shape
-    Hkv, dv = k.shape[1], v.shape[3]
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k and v must be 4-D [B, H, L, d]")
+    B, Hq, L, _ = q.shape
     if out is None:
-        out = torch.empty(B, Hq, L, dv, dtype=out_dtype, device=q.device)
-    p = _PrefillParams(_tensor(q), _tensor(k), _tensor(v), _tensor(out), B, Hq, Hkv, L, d, dv,
-                       int(bool(causal)), float(scale) if scale is not None else 0.0, float(lam),
-                       int(tile_q), int(block_k), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
+        out = torch.empty(B, Hq, L, v.shape[3], dtype=out_dtype, device=q.device)
+    p = _prefill_params(q, k, v, out, causal, lam, tile_q, block_k, scale, skip_map, gap_map, counters, window)
+    if B > 0 and L > 0:
+        _check_devices(q, k=k, v=v, out=out, skip_map=skip_map, gap_map=gap_map, counters=counters)
     _check(load_library().blasst_prefill(ctypes.byref(p), _stream(stream, q.device)), "blasst_prefill")
     return out
 
 
+def _prefill_params(q, k, v, out, causal, lam, tile_q, block_k, scale, skip_map, gap_map, counters, window):
+    """blasst_prefill_params for the tensors, after the host-side shape checks."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4 and out.dim() == 4,
+          "q, k, v and out must be 4-D [B, H, L, d]")
+    B, Hq, L, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    _need(k.shape[0] == B and k.shape[2] >= L and k.shape[3] == d,
+          f"k must be [B={B}, Hkv, >= L={L}, d={d}] (got {list(k.shape)})")
+    _need(v.shape[0] == B and v.shape[1] == Hkv and v.shape[2] >= L,
+          f"v must be [B={B}, Hkv={Hkv}, >= L={L}, dv] (got {list(v.shape)})")
+    _need(list(out.shape) == [B, Hq, L, dv], f"out must be [{B}, {Hq}, {L}, {dv}] (got {list(out.shape)})")
+    if tile_q > 0 and block_k > 0:
+        n = B * Hq * -(-L // tile_q) * -(-L // block_k)
+        _check_map(skip_map, "skip_map", torch.uint8, n)
+        _check_map(gap_map, "gap_map", torch.float32, n)
+    _check_counters(counters)
+    return _PrefillParams(_tensor(q), _tensor(k), _tensor(v), _tensor(out), B, Hq, Hkv, L, d, dv,
+                          int(bool(causal)), float(scale) if scale is not None else 0.0, float(lam),
+                          int(tile_q), int(block_k), _ptr(skip_map), _ptr(gap_map), _ptr(counters), int(window))
+
+
+def _check_lens(seq_lens, B):
+    if seq_lens is None:
+        return
+    _need(seq_lens.dtype == torch.int32, f"seq_lens must be int32 (got {seq_lens.dtype})")
+    _need(seq_lens.is_contiguous() and seq_lens.numel() == B, f"seq_lens must hold {B} contiguous entries")
+
+
 def _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
                    skip_map, gap_map, counters, window=0, sink_seed=False):
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
     B, Hq, dqk = q.shape
+    _need(k_cache.dim() == 4 and k_cache.shape[0] == B and k_cache.shape[3] == dqk,
+          f"k_cache must be [B={B}, Hkv, Lmax, dqk={dqk}] (got {list(k_cache.shape)})")
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if v_cache is not None:
+        _need(v_cache.dim() == 4 and list(v_cache.shape[:3]) == [B, Hkv, Lmax],
+              f"v_cache must be [B={B}, Hkv={Hkv}, Lmax={Lmax}, dv] (got {list(v_cache.shape)})")
     dv = out.shape[2] if out is not None else (v_cache.shape[3] if v_cache is not None else dqk)
+    if out is not None:
+        _need(out.dim() == 3 and list(out.shape[:2]) == [B, Hq], f"out must be [{B}, {Hq}, dv]")
+        _need(v_cache is None or dv <= v_cache.shape[3], f"dv = {dv} exceeds the v_cache width")
+    _check_lens(seq_lens, B)
+    if block_k > 0:
+        n = B * Hkv * -(-Lmax // block_k)
+        _check_map(skip_map, "skip_map", torch.uint8, n)
+        _check_map(gap_map, "gap_map", torch.float32, n)
+    _check_counters(counters)
     return _DecodeParams(_tensor(q, True), _tensor(k_cache), _tensor(v_cache), _tensor(out, True),
                          _ptr(seq_lens), B, Hq, Hkv, Lmax, dqk, dv,
                          float(scale) if scale is not None else 0.0, float(lam), int(block_k),
@@ -196,6 +274,7 @@ def _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_split
 def blasst_decode_plan(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
                        dv=None, out_dtype=torch.float32, window=0):
     """(num_splits the call will use, workspace bytes it needs)."""
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
     B, Hq, _ = q.shape
     dv = dv if dv is not None else v_cache.shape[3]
     p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, None,
@@ -222,6 +301,7 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
     ``workspace`` (uint8 device tensor) is allocated here when not given.
     Returns O [B,Hq,dv].
     """
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
     B, Hq, _ = q.shape
     dv = dv if dv is not None else v_cache.shape[3]
     if out is None:
@@ -233,6 +313,9 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
         ns, ws = ctypes.c_int(0), ctypes.c_size_t(0)
         _check(lib.blasst_decode_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)), "blasst_decode_plan")
         workspace = torch.empty(max(ws.value, 1), dtype=torch.uint8, device=q.device)
+    if B > 0:
+        _check_devices(q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, out=out, workspace=workspace,
+                       skip_map=skip_map, gap_map=gap_map, counters=counters)
     _check(lib.blasst_decode(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                              _stream(stream, q.device)), "blasst_decode")
     return out
@@ -240,9 +323,21 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
 
 def _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits, o,
                   skip_map, gap_map, counters, window=0, sink_seed=False):
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
     B, Hq, dqk = q.shape
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.stride(1) != 1:
         raise ValueError("page_table must be an int32 [B, pages_per_seq] tensor with unit column stride")
+    _need(page_table.shape[0] == B, f"page_table needs {B} rows (got {page_table.shape[0]})")
+    _need(k_pages.dim() == 4 and k_pages.shape[3] == dqk,
+          f"k_pages must be [pages, Hkv, page_size, dqk={dqk}] (got {list(k_pages.shape)})")
+    _need(v_pages.dim() == 4 and list(v_pages.shape[:3]) == list(k_pages.shape[:3]),
+          f"v_pages must be [pages, Hkv, page_size, dv] like k_pages (got {list(v_pages.shape)})")
+    _check_lens(seq_lens, B)
+    if block_k > 0:
+        n = B * k_pages.shape[1] * -(-int(Lmax) // block_k)
+        _check_map(skip_map, "skip_map", torch.uint8, n)
+        _check_map(gap_map, "gap_map", torch.float32, n)
+    _check_counters(counters)
     d = _DecodeParams(_tensor(q, True), _tensor(k_pages), _tensor(v_pages), o,
                       _ptr(seq_lens), B, Hq, k_pages.shape[1], int(Lmax), dqk, 0,
                       float(scale) if scale is not None else 0.0, float(lam), int(block_k),
@@ -255,6 +350,7 @@ def _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, b
 def blasst_decode_paged_plan(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=0.0, scale=None,
                              block_k=64, num_splits=0, dv=None, out_dtype=torch.float32, window=0):
     """(num_splits the paged call will use, workspace bytes it needs)."""
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
     B, Hq, _ = q.shape
     dv = dv if dv is not None else v_pages.shape[3]
     # the planner reads no device memory: describe O [B,Hq,dv] at q's (aligned) address
@@ -280,10 +376,13 @@ def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=
     sizes the skip/gap maps [B,Hkv,ceil(Lmax/64)]).  Latent form: pass
     ``v_pages = k_pages`` and ``dv=512``.  Returns O [B,Hq,dv].
     """
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
     B, Hq, _ = q.shape
     dv = dv if dv is not None else v_pages.shape[3]
     if out is None:
         out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
+    _need(out.dim() == 3 and list(out.shape) == [B, Hq, dv], f"out must be [{B}, {Hq}, {dv}]")
+    _need(dv <= v_pages.shape[3], f"dv = {dv} exceeds the v_pages width")
     p = _paged_params(q, k_pages, v_pages, page_table, seq_lens, Lmax, lam, scale, block_k, num_splits,
                       _tensor(out, True), skip_map, gap_map, counters, window, sink_seed)
     p.d.dv = dv
@@ -293,6 +392,9 @@ def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=
         _check(lib.blasst_decode_paged_plan(ctypes.byref(p), ctypes.byref(ns), ctypes.byref(ws)),
                "blasst_decode_paged_plan")
         workspace = torch.empty(max(ws.value, 1), dtype=torch.uint8, device=q.device)
+    if B > 0:
+        _check_devices(q, k_pages=k_pages, v_pages=v_pages, page_table=page_table, seq_lens=seq_lens, out=out,
+                       workspace=workspace, skip_map=skip_map, gap_map=gap_map, counters=counters)
     _check(lib.blasst_decode_paged(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                    _stream(stream, q.device)), "blasst_decode_paged")
     return out

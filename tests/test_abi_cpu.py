@@ -38,12 +38,19 @@ def _bf16(*shape):
 
 
 def _prefill_err(**kw):
+    """Status of blasst_prefill for host tensors that pass the binding's shape
+    checks: the C ABI's own validation, called directly (the library must
+    refuse the call before any launch, so the host pointers are never read)."""
     q, k, v = _bf16(1, 2, 128, 128), _bf16(1, 1, 128, 128), _bf16(1, 1, 128, 128)
-    args = dict(q=q, k=k, v=v, causal=True, lam=0.01, tile_q=128, block_k=64, stream=0)
+    args = dict(q=q, k=k, v=v, causal=True, lam=0.01, tile_q=128, block_k=64)
     args.update(kw)
-    with pytest.raises(bl.BlasstError) as ei:
-        bl.blasst_prefill(**args)
-    return ei.value.status
+    B, Hq, L, _ = args["q"].shape
+    out = torch.empty(B, Hq, L, args["v"].shape[3])
+    p = _abi._prefill_params(args["q"], args["k"], args["v"], out, args["causal"], args["lam"], args["tile_q"],
+                             args["block_k"], None, None, None, None, 0)
+    status = bl.load_library().blasst_prefill(ctypes.byref(p), None)
+    assert status != 0
+    return status
 
 
 @pytest.mark.parametrize("lam", [-0.1, 1.0, 1.5, float("nan")])
@@ -116,15 +123,22 @@ def test_prefill_error_message_names_argument():
 
 
 def _decode_err(**kw):
+    """Status of blasst_decode through the C ABI for host tensors (see _prefill_err)."""
     q = _bf16(2, 8, 128)
     kc, vc = _bf16(2, 2, 256, 128), _bf16(2, 2, 256, 128)
     lens = torch.full((2,), 256, dtype=torch.int32)
-    args = dict(q=q, k_cache=kc, v_cache=vc, seq_lens=lens, lam=0.01, stream=0,
+    args = dict(q=q, k_cache=kc, v_cache=vc, seq_lens=lens, lam=0.01, block_k=64, num_splits=0, dv=None,
                 workspace=torch.zeros(16, dtype=torch.uint8))
     args.update(kw)
-    with pytest.raises(bl.BlasstError) as ei:
-        bl.blasst_decode(**args)
-    return ei.value.status
+    q = args["q"]
+    dv = args["dv"] if args["dv"] is not None else args["v_cache"].shape[3]
+    out = torch.empty(q.shape[0], q.shape[1], dv)
+    p = _abi._decode_params(q, args["k_cache"], args["v_cache"], args["seq_lens"], args["lam"], None,
+                            args["block_k"], args["num_splits"], out, None, None, None)
+    ws = args["workspace"]
+    status = bl.load_library().blasst_decode(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert status != 0
+    return status
 
 
 def test_decode_rejects():
@@ -177,15 +191,21 @@ def test_empty_calls_are_noops():
 
 # ------------------------------------------------------------- paged decode
 def _paged_err(page_size=64, pages=8, table_cols=4, Lmax=256, **kw):
+    """Status of blasst_decode_paged through the C ABI for host tensors (see _prefill_err)."""
     q = _bf16(2, 8, 128)
     pool = _bf16(max(pages, 0), 2, page_size, 128)
     table = torch.zeros(2, table_cols, dtype=torch.int32)
     lens = torch.full((2,), Lmax, dtype=torch.int32)
-    args = dict(lam=0.01, stream=0, workspace=torch.zeros(16, dtype=torch.uint8))
+    args = dict(lam=0.01, num_splits=0, workspace=torch.zeros(16, dtype=torch.uint8))
     args.update(kw)
-    with pytest.raises(bl.BlasstError) as ei:
-        bl.blasst_decode_paged(q, pool, pool, table, lens, Lmax, **args)
-    return ei.value.status
+    out = torch.empty(2, 8, 128)
+    p = _abi._paged_params(q, pool, pool, table, lens, Lmax, args["lam"], None, 64, args["num_splits"],
+                           _abi._tensor(out, True), None, None, None)
+    p.d.dv = 128
+    ws = args["workspace"]
+    status = bl.load_library().blasst_decode_paged(ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert status != 0
+    return status
 
 
 def test_decode_paged_rejects():
@@ -286,3 +306,70 @@ def test_binding_structs_match_the_header_abi_version():
     v = int(re.search(r"#define BLASST_ABI_VERSION (\d+)", hdr).group(1))
     assert _abi.ABI_VERSION == v
     assert _abi.load_library().blasst_abi_version() == v
+
+
+# ------------------------------------------------- binding argument checks
+def test_binding_refuses_host_tensors_before_any_launch():
+    """The library receives bare pointers: a host tensor, or one on another
+    device than the query, is refused by the binding with ValueError."""
+    q, k, v = _bf16(1, 2, 128, 128), _bf16(1, 1, 128, 128), _bf16(1, 1, 128, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        bl.blasst_prefill(q, k, v, lam=0.01, stream=0)
+    qd, kc = _bf16(2, 8, 128), _bf16(2, 2, 256, 128)
+    lens = torch.full((2,), 256, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        bl.blasst_decode(qd, kc, kc, lens, lam=0.01, stream=0, workspace=torch.zeros(16, dtype=torch.uint8))
+    pool, table = _bf16(8, 2, 64, 128), torch.zeros(2, 4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        bl.blasst_decode_paged(qd, pool, pool, table, lens, 256, lam=0.01, stream=0,
+                               workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_binding_refuses_inconsistent_prefill_arguments():
+    q, k, v = _bf16(1, 2, 128, 128), _bf16(1, 1, 128, 128), _bf16(1, 1, 128, 128)
+    def err(**kw):
+        args = dict(q=q, k=k, v=v, lam=0.01, stream=0)
+        args.update(kw)
+        with pytest.raises(ValueError) as ei:
+            bl.blasst_prefill(**args)
+        return str(ei.value)
+    assert "k must be" in err(k=_bf16(1, 1, 64, 128))                      # fewer keys than queries
+    assert "k must be" in err(k=_bf16(2, 1, 128, 128))                     # other batch
+    assert "v must be" in err(v=_bf16(1, 2, 128, 128))                     # other KV head count
+    assert "out must be" in err(out=torch.empty(1, 2, 128, 64))
+    assert "4-D" in err(q=_bf16(2, 128, 128))
+    n = 1 * 2 * 1 * 2  # B * Hq * nQT * nKB
+    assert "skip_map" in err(skip_map=torch.zeros(n, dtype=torch.int32))
+    assert "skip_map" in err(skip_map=torch.zeros(n - 1, dtype=torch.uint8))
+    assert "gap_map" in err(gap_map=torch.zeros(n, dtype=torch.float64))
+    assert "counters" in err(counters=torch.zeros(2, dtype=torch.int32))
+    assert "counters" in err(counters=torch.zeros(1, dtype=torch.int64))
+
+
+def test_binding_refuses_inconsistent_decode_arguments():
+    q, kc = _bf16(2, 8, 128), _bf16(2, 2, 256, 128)
+    lens = torch.full((2,), 256, dtype=torch.int32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    def err(**kw):
+        args = dict(q=q, k_cache=kc, v_cache=kc, seq_lens=lens, lam=0.01, stream=0, workspace=ws)
+        args.update(kw)
+        with pytest.raises(ValueError) as ei:
+            bl.blasst_decode(**args)
+        return str(ei.value)
+    assert "seq_lens" in err(seq_lens=lens.to(torch.int64))                 # read as int32 pairs otherwise
+    assert "seq_lens" in err(seq_lens=torch.full((3,), 256, dtype=torch.int32))
+    assert "v_cache" in err(v_cache=_bf16(2, 2, 128, 128))                  # shorter than k_cache
+    assert "k_cache" in err(k_cache=_bf16(1, 2, 256, 128))
+    assert "skip_map" in err(skip_map=torch.zeros(2 * 2 * 4 - 1, dtype=torch.uint8))
+    assert "gap_map" in err(gap_map=torch.zeros(2 * 2 * 4, dtype=torch.float16))
+    assert "counters" in err(counters=torch.zeros(2, dtype=torch.float32))
+    assert "out must be" in err(out=torch.empty(2, 4, 128))
+    pool, table = _bf16(8, 2, 64, 128), torch.zeros(2, 4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="page_table"):
+        bl.blasst_decode_paged(q, pool, pool, torch.zeros(3, 4, dtype=torch.int32), lens, 256, lam=0.01,
+                               stream=0, workspace=ws)
+    with pytest.raises(ValueError, match="v_pages"):
+        bl.blasst_decode_paged(q, pool, _bf16(8, 2, 32, 128), table, lens, 256, lam=0.01, stream=0, workspace=ws)
+    with pytest.raises(ValueError, match="seq_lens"):
+        bl.blasst_decode_paged(q, pool, pool, table, lens.to(torch.int64), 256, lam=0.01, stream=0, workspace=ws)
+
