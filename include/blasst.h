@@ -17,8 +17,10 @@
  *  - Tensors are described by blasst_tensor: a DEVICE pointer, an element type
  *    and strides IN ELEMENTS for the batch, head and token dimensions; the
  *    last (feature) dimension is always contiguous.  Every device buffer is
- *    allocated and owned by the caller; the library never allocates device
- *    memory and keeps no pointer after a call returns.
+ *    allocated and owned by the caller; the library allocates no device
+ *    memory in any call and keeps no pointer after a call returns (the one
+ *    array it owns, the scratch of blasst_decode_noalloc, exists from the
+ *    loading of its device code).
  *  - Calls are asynchronous: they validate their arguments on the host,
  *    enqueue kernels on the given HIP stream (a hipStream_t passed as void*;
  *    NULL = the default stream) and return.  Outputs are valid once the stream
@@ -240,6 +242,30 @@ blasst_status blasst_decode_paged_plan(const blasst_decode_paged_params *p, int 
 
 blasst_status blasst_decode_paged(const blasst_decode_paged_params *p, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------- no-allocation decode
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * blasst_decode_noalloc is blasst_decode (same parameters, kernels, split plan,
+ * decisions and outputs) with the split partials kept in a device array that
+ * the library owns instead of a caller workspace.  Each GPU the library runs
+ * on holds its own array of BLASST_NOALLOC_SCRATCH_BYTES from the loading of
+ * the library's device code until the process ends; the call itself allocates
+ * nothing.  Its device address is looked up on the first call on each device
+ * (the current device, which must be the device of hip_stream).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its partials in
+ * it.  Calls ordered on one stream are safe; calls that overlap on one GPU
+ * (several streams, or threads without ordering) race and give wrong outputs.
+ * The caller still passes every input and output buffer.
+ * Errors: as blasst_decode, plus WORKSPACE when the split partials of the
+ * planned split count (blasst_decode_plan) exceed BLASST_NOALLOC_SCRATCH_BYTES
+ * (pass a smaller num_splits), and LAUNCH when no current device exists or the
+ * array's address cannot be found.
+ */
+#define BLASST_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+
+blasst_status blasst_decode_noalloc(const blasst_decode_params *p, void *hip_stream);
 
 /* ---------------------------------------------------------------- calibrate
  * blasst_calibrate(target_sparsity, L) -> lambda = a(target) / L.  The table

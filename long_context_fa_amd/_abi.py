@@ -99,6 +99,8 @@ def load_library():
     lib.blasst_decode_paged.restype = st
     lib.blasst_decode_paged.argtypes = [ctypes.POINTER(_DecodePagedParams), ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
+    lib.blasst_decode_noalloc.restype = st
+    lib.blasst_decode_noalloc.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.c_void_p]
     lib.blasst_calibrate.restype = st
     lib.blasst_calibrate.argtypes = [ctypes.POINTER(_CalibTable), ctypes.c_double, ctypes.c_int64,
                                      ctypes.POINTER(ctypes.c_double)]
@@ -318,6 +320,26 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
                        skip_map=skip_map, gap_map=gap_map, counters=counters)
     _check(lib.blasst_decode(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                              _stream(stream, q.device)), "blasst_decode")
+    return out
+
+
+def blasst_decode_noalloc(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,
+                          dv=None, out=None, out_dtype=torch.float32, skip_map=None, gap_map=None, counters=None,
+                          stream=None, window=0, sink_seed=False):
+    """blasst_decode without a workspace: the split partials live in the
+    library's own device array (BLASST_NOALLOC_SCRATCH_BYTES per GPU).  Calls
+    that overlap on one GPU race.  Returns O [B,Hq,dv]."""
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
+    B, Hq, _ = q.shape
+    dv = dv if dv is not None else v_cache.shape[3]
+    if out is None:
+        out = torch.empty(B, Hq, dv, dtype=out_dtype, device=q.device)
+    p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, out,
+                       skip_map, gap_map, counters, window, sink_seed)
+    if B > 0:
+        _check_devices(q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, out=out,
+                       skip_map=skip_map, gap_map=gap_map, counters=counters)
+    _check(load_library().blasst_decode_noalloc(ctypes.byref(p), _stream(stream, q.device)), "blasst_decode_noalloc")
     return out
 
 

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -371,6 +372,62 @@ blasst_status blasst_decode_paged(const blasst_decode_paged_params *p, void *wor
         return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
     return run_decode(&p->d, p, workspace, workspace_bytes, hip_stream);
 }
+
+} // extern "C"
+
+// ------------------------------------------------------ no-allocation decode
+// Split partials of blasst_decode_noalloc live in this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy from module load until the process ends.  In host code the name is
+// only a stand-in: its device address is taken once per device with
+// hipGetSymbolAddress and that address is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[BLASST_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+blasst_status scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(BLASST_ERR_LAUNCH, "no current HIP device (or device id >= %d)", kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(BLASST_ERR_LAUNCH, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BLASST_OK;
+}
+
+} // namespace
+
+extern "C" blasst_status blasst_decode_noalloc(const blasst_decode_params *p, void *hip_stream)
+{
+    if (blasst_status s = validate_decode(p))
+        return s;
+    const size_t need = workspace_for(p, choose_splits(p));
+    if (need > (size_t)BLASST_NOALLOC_SCRATCH_BYTES)
+        return fail(BLASST_ERR_WORKSPACE,
+                    "the split partials need %zu bytes but the no-allocation scratch holds %zu: pass a smaller "
+                    "num_splits, or call blasst_decode with a workspace",
+                    need, (size_t)BLASST_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0)
+        if (blasst_status s = scratch_for_current_device(&ws))
+            return s;
+    return run_decode(p, nullptr, ws, need, hip_stream);
+}
+
+extern "C" {
 
 // ------------------------------------------------------------- calibration
 blasst_status blasst_calibrate(const blasst_calib_table *t, double target, int64_t L, double *lambda_out)

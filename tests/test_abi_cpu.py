@@ -373,3 +373,23 @@ def test_binding_refuses_inconsistent_decode_arguments():
     with pytest.raises(ValueError, match="seq_lens"):
         bl.blasst_decode_paged(q, pool, pool, table, lens.to(torch.int64), 256, lam=0.01, stream=0, workspace=ws)
 
+
+def test_noalloc_decode_refuses_partials_beyond_the_scratch_before_any_launch():
+    """blasst_decode_noalloc plans like blasst_decode and refuses, on the host,
+    a split plan whose partials exceed BLASST_NOALLOC_SCRATCH_BYTES (raw ABI
+    call; the fake device pointers are never touched)."""
+    hdr = open(os.path.join(ROOT, "include", "blasst.h")).read()
+    cap = eval(re.search(r"#define BLASST_NOALLOC_SCRATCH_BYTES \(([^)]*)\)", hdr).group(1).replace("u", ""))
+    fake = 1 << 20
+    lib = bl.load_library()
+    p = _abi._DecodeParams()
+    B, Hq, Hkv, L, d, S = 4096, 32, 8, 8192, 128, 32
+    p.q, p.o = _abi._Tensor(fake, 0, Hq * d, d, 0), _abi._Tensor(fake, 1, Hq * d, d, 0)
+    p.k_cache = p.v_cache = _abi._Tensor(fake, 0, Hkv * L * d, L * d, d)
+    p.seq_lens = fake
+    p.B, p.Hq, p.Hkv, p.Lmax, p.dqk, p.dv = B, Hq, Hkv, L, d, d
+    p.lam, p.block_k, p.num_splits = 0.01, 64, S
+    ws = ctypes.c_size_t(0)
+    assert lib.blasst_decode_plan(ctypes.byref(p), None, ctypes.byref(ws)) == 0 and ws.value > cap
+    assert lib.blasst_decode_noalloc(ctypes.byref(p), None) == 3
+    assert "scratch" in bl.blasst_last_error()
