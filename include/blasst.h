@@ -98,7 +98,8 @@ typedef struct {
  * causal masking, a non-positive stride or a
  * pointer not aligned to 16 bytes with a token stride not a multiple of 8
  * elements; UNSUPPORTED for other d, dv, tile or dtype, for L > 2^30, for
- * B * Hq * nQT above 2^31 - 1 (one workgroup each), and for k or v token
+ * B * Hq * nQT above (2^32 - 1) / (2 tile_q) (one workgroup of 2 tile_q
+ * threads each; a launch counts threads in 32 bits), and for k or v token
  * strides above 2^24 elements; LAUNCH if HIP fails.
  * L = 0 or B = 0 is a valid no-op: only the scalar arguments are checked and
  * the tensor pointers may be null.

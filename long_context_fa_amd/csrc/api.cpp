@@ -123,10 +123,11 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
     const int64_t nqt = (p->L + p->tile_q - 1) / p->tile_q;
     const int64_t nkb = (p->L + p->block_k - 1) / p->block_k;
-    // One workgroup per (query tile, head, batch), at most 2^31 - 1 of them
-    // (B, Hq and the count all fit an int).  The bound is divided out so that
-    // no product of caller sizes overflows.
-    const int64_t max_units = INT32_MAX;
+    // One workgroup of 2 * tile_q threads per (query tile, head, batch).  A
+    // launch counts work-items in 32 bits, so at most (2^32 - 1) / (2 tile_q)
+    // workgroups fit (below 2^31 - 1, so B, Hq and the count also fit an int).
+    // The bound is divided out so that no product of caller sizes overflows.
+    const int64_t max_units = (int64_t)UINT32_MAX / (2 * p->tile_q);
     if (p->L > (int64_t)1 << 30 || p->Hq > max_units || p->B > max_units / (nqt * p->Hq))
         return fail(BLASST_ERR_UNSUPPORTED, "problem too large for one launch");
     // The tile copies address the 64 rows of a K/V block with 32-bit byte

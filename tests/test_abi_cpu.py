@@ -98,13 +98,23 @@ def test_size_limits_reject_overflowing_products():
     lib = bl.load_library()
     def t(st, sh, sb=0):
         return _abi._Tensor(fake, 0, sb, sh, st)
-    for B, Hq, L in ((1 << 40, 1 << 40, 128), (1 << 31, 1, 64), (1 << 20, 1 << 20, 1 << 20), (1, 1 << 62, 128)):
+    # (2^32 - 1) / 256 = 16777215 workgroups of 256 threads fit one launch at tile 128; 16777216 do not
+    for B, Hq, L in ((1 << 40, 1 << 40, 128), (1 << 31, 1, 64), (1 << 20, 1 << 20, 1 << 20), (1, 1 << 62, 128),
+                     (1 << 24, 1, 128), (1 << 12, 1 << 12, 128), (1 << 10, 1 << 10, 128 * 16)):
         p = _abi._PrefillParams()
         p.q = p.k = p.v = p.o = t(128, 128 * 128)
         p.B, p.Hq, p.Hkv, p.L, p.d, p.dv = B, Hq, 1, L, 128, 128
         p.causal, p.scale, p.lam, p.tile_q, p.block_k = 1, 0.0, 0.01, 128, 64
         assert lib.blasst_prefill(ctypes.byref(p), None) == 2, (B, Hq, L)
         assert "too large" in bl.blasst_last_error()
+    # just inside the limit the size check passes; the K token stride check,
+    # which comes after it, then refuses the call, so nothing is launched
+    p = _abi._PrefillParams()
+    p.q = p.v = p.o = t(128, 128 * 128)
+    p.k = t((1 << 24) + 8, 0)
+    p.B, p.Hq, p.Hkv, p.L, p.d, p.dv = (1 << 24) - 1, 1, 1, 128, 128, 128
+    p.causal, p.scale, p.lam, p.tile_q, p.block_k = 1, 0.0, 0.01, 128, 64
+    assert lib.blasst_prefill(ctypes.byref(p), None) == 2 and "stride" in bl.blasst_last_error()
     for kst, lmax in ((1 << 40, 4096), (1 << 62, 1), (576, 1 << 22)):
         p = _abi._DecodeParams()
         p.q, p.o = t(0, 576, 128 * 576), t(0, 512, 128 * 512)
