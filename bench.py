@@ -125,17 +125,15 @@ def long_prefill_workload(seed=1004):
 
 
 def calibrate_prefill(q, k, v, targets, window=0):
-    B, Hq, L, _ = q.shape
-    gap = torch.empty(B, Hq, -(-L // 128), -(-L // 64), dtype=torch.float32, device="cuda")
-    bl.blasst_prefill(q, k, v, causal=True, lam=0.0, tile_q=128, gap_map=gap, window=window)
+    """lambda for each target sparsity: the gap pass (no O), then the exact quantile."""
+    gap = bl.blasst_prefill_gaps(q, k, v, causal=True, lam=0.0, tile_q=128, window=window)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
 
 def calibrate_decode(q, kc, vc, lens, S, targets, dv=None, window=0, sink_seed=False):
-    B, Hkv, L = q.shape[0], kc.shape[1], kc.shape[2]
-    gap = torch.empty(B, Hkv, -(-L // 64), dtype=torch.float32, device="cuda")
-    bl.blasst_decode(q, kc, vc, lens, lam=0.0, num_splits=S, gap_map=gap, dv=dv, window=window, sink_seed=sink_seed)
+    """lambda for each target sparsity: the decode gap pass (no O), then the exact quantile."""
+    gap = bl.blasst_decode_gaps(q, kc, vc, lens, lam=0.0, num_splits=S, dv=dv, window=window, sink_seed=sink_seed)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 

@@ -120,6 +120,21 @@ typedef struct {
 
 blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream);
 
+/* The gap pass of blasst_prefill, for calibration (BLASST summary,
+ * gist.science/pt/paper/2512.12087, section 2 "Calibração Automática": the
+ * threshold for a target sparsity is found by a search over the sparsity it
+ * achieves; BLASST reading notes, "核心方法": automatic lambda search).  It
+ * forms the same scores, block maxima, running max and decisions (at
+ * p->lambda) as blasst_prefill and writes the same skip map, gap map and
+ * counters, with no exponential, no V load, no P.V product and no output:
+ * p->o is neither read nor written and may be null.  The running max never
+ * depends on the decisions (a skipped block has m~ < m + ln(lambda) <= m), so
+ * the gap map is blasst_prefill's at any lambda and the lambda of a target
+ * sparsity is a quantile of it (blasst_calibrate_search).
+ * Errors: as blasst_prefill, plus INVALID_ARG when gap_map, skip_map and
+ * counters are all null. */
+blasst_status blasst_prefill_gaps(const blasst_prefill_params *p, void *hip_stream);
+
 /* ------------------------------------------------------------------- decode
  * blasst_decode(q, KV cache, seq lens, lambda): one query token per sequence
  * against a KV cache.  A query tile is the group of G = Hq / Hkv query heads
@@ -193,6 +208,15 @@ blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_
  * WORKSPACE for a missing or too small workspace; LAUNCH if HIP fails. */
 blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes,
                             void *hip_stream);
+
+/* The gap pass of blasst_decode, for calibration (see blasst_prefill_gaps):
+ * the same split plan (blasst_decode_plan), scores, decisions at p->lambda,
+ * skip map, gap map and counters, with no V load, no exponential, no P.V
+ * product, no split partials and no output.  Needs no workspace; p->o is
+ * neither read nor written and may be null.
+ * Errors: as blasst_decode (without WORKSPACE), plus INVALID_ARG when gap_map,
+ * skip_map and counters are all null. */
+blasst_status blasst_decode_gaps(const blasst_decode_params *p, void *hip_stream);
 
 /* ------------------------------------------------------------ paged decode
  * blasst_decode over a paged KV cache, the layout of serving engines: the

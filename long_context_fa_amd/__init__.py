@@ -8,7 +8,9 @@ fallback: if the library is missing, importing a call raises.
 
 Entry points (same names as the C ABI):
   blasst_prefill(q, k, v, causal, lam, tile_q, ...)   -> O
+  blasst_prefill_gaps(q, k, v, ...)                    -> gap map (calibration pass, no O)
   blasst_decode(q, k_cache, v_cache, seq_lens, lam, ...) -> O
+  blasst_decode_gaps(q, k_cache, v_cache, seq_lens, ...) -> gap map (calibration pass, no O)
   blasst_decode_plan(...)                              -> (num_splits, workspace bytes)
   blasst_decode_noalloc(q, k_cache, v_cache, seq_lens, lam, ...) -> O (no workspace)
   blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, ...) -> O
@@ -19,12 +21,12 @@ Entry points (same names as the C ABI):
 """
 from ._abi import (BlasstError, blasst_abi_version, blasst_calibrate,  # noqa: F401
                    blasst_calibrate_fit, blasst_calibrate_search, blasst_decode,
-                   blasst_decode_noalloc, blasst_decode_paged, blasst_decode_paged_plan,
-                   blasst_decode_plan, blasst_last_error, blasst_prefill,
+                   blasst_decode_gaps, blasst_decode_noalloc, blasst_decode_paged, blasst_decode_paged_plan,
+                   blasst_decode_plan, blasst_last_error, blasst_prefill, blasst_prefill_gaps,
                    blasst_status_str, library_path, load_library)
 
 __all__ = [
-    "BlasstError", "blasst_prefill", "blasst_decode", "blasst_decode_plan", "blasst_decode_noalloc",
+    "BlasstError", "blasst_prefill", "blasst_prefill_gaps", "blasst_decode", "blasst_decode_gaps", "blasst_decode_plan", "blasst_decode_noalloc",
     "blasst_decode_paged",
     "blasst_decode_paged_plan", "blasst_calibrate",
     "blasst_calibrate_search", "blasst_calibrate_fit", "blasst_status_str", "blasst_last_error",

@@ -99,6 +99,10 @@ def load_library():
     lib.blasst_decode_paged.restype = st
     lib.blasst_decode_paged.argtypes = [ctypes.POINTER(_DecodePagedParams), ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]
+    lib.blasst_prefill_gaps.restype = st
+    lib.blasst_prefill_gaps.argtypes = [ctypes.POINTER(_PrefillParams), ctypes.c_void_p]
+    lib.blasst_decode_gaps.restype = st
+    lib.blasst_decode_gaps.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.c_void_p]
     lib.blasst_decode_noalloc.restype = st
     lib.blasst_decode_noalloc.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.c_void_p]
     lib.blasst_calibrate.restype = st
@@ -218,9 +222,29 @@ def blasst_prefill(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, sca
     return out
 
 
+def blasst_prefill_gaps(q, k, v, *, causal=True, lam=0.0, tile_q=128, block_k=64, scale=None, skip_map=None,
+                        gap_map=None, counters=None, stream=None, window=0):
+    """The gap pass of blasst_prefill (calibration): maps and counters only, no O.
+
+    Returns the gap map float32 [B,Hq,ceil(L/tile_q),ceil(L/block_k)] (``gap_map``
+    if given, else a new one); ``skip_map`` / ``counters`` as in blasst_prefill,
+    for the decisions at ``lam``.
+    """
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k and v must be 4-D [B, H, L, d]")
+    B, Hq, L, _ = q.shape
+    if gap_map is None:
+        gap_map = torch.empty(B, Hq, -(-L // tile_q), -(-L // block_k), dtype=torch.float32, device=q.device)
+    p = _prefill_params(q, k, v, None, causal, lam, tile_q, block_k, scale, skip_map, gap_map, counters, window)
+    if B > 0 and L > 0:
+        _check_devices(q, k=k, v=v, skip_map=skip_map, gap_map=gap_map, counters=counters)
+    _check(load_library().blasst_prefill_gaps(ctypes.byref(p), _stream(stream, q.device)), "blasst_prefill_gaps")
+    return gap_map
+
+
 def _prefill_params(q, k, v, out, causal, lam, tile_q, block_k, scale, skip_map, gap_map, counters, window):
-    """blasst_prefill_params for the tensors, after the host-side shape checks."""
-    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4 and out.dim() == 4,
+    """blasst_prefill_params for the tensors, after the host-side shape checks
+    (``out`` None: no output, for the gap pass)."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4 and (out is None or out.dim() == 4),
           "q, k, v and out must be 4-D [B, H, L, d]")
     B, Hq, L, d = q.shape
     Hkv, dv = k.shape[1], v.shape[3]
@@ -228,7 +252,8 @@ def _prefill_params(q, k, v, out, causal, lam, tile_q, block_k, scale, skip_map,
           f"k must be [B={B}, Hkv, >= L={L}, d={d}] (got {list(k.shape)})")
     _need(v.shape[0] == B and v.shape[1] == Hkv and v.shape[2] >= L,
           f"v must be [B={B}, Hkv={Hkv}, >= L={L}, dv] (got {list(v.shape)})")
-    _need(list(out.shape) == [B, Hq, L, dv], f"out must be [{B}, {Hq}, {L}, {dv}] (got {list(out.shape)})")
+    if out is not None:
+        _need(list(out.shape) == [B, Hq, L, dv], f"out must be [{B}, {Hq}, {L}, {dv}] (got {list(out.shape)})")
     if tile_q > 0 and block_k > 0:
         n = B * Hq * -(-L // tile_q) * -(-L // block_k)
         _check_map(skip_map, "skip_map", torch.uint8, n)
@@ -321,6 +346,27 @@ def blasst_decode(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k
     _check(lib.blasst_decode(ctypes.byref(p), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                              _stream(stream, q.device)), "blasst_decode")
     return out
+
+
+def blasst_decode_gaps(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0, dv=None,
+                       skip_map=None, gap_map=None, counters=None, stream=None, window=0, sink_seed=False):
+    """The gap pass of blasst_decode (calibration): maps and counters only, no
+    O and no workspace; the split plan is blasst_decode's.  Returns the gap map
+    float32 [B,Hkv,ceil(Lmax/block_k)] (``gap_map`` if given, else a new one)."""
+    _need(q.dim() == 3, "q must be 3-D [B, Hq, dqk]")
+    B, Hq, _ = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dv = dv if dv is not None else v_cache.shape[3]
+    if gap_map is None:
+        gap_map = torch.empty(B, Hkv, -(-Lmax // block_k), dtype=torch.float32, device=q.device)
+    p = _decode_params(q, k_cache, v_cache, seq_lens, lam, scale, block_k, num_splits, None,
+                       skip_map, gap_map, counters, window, sink_seed)
+    p.dv = dv
+    if B > 0:
+        _check_devices(q, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, skip_map=skip_map,
+                       gap_map=gap_map, counters=counters)
+    _check(load_library().blasst_decode_gaps(ctypes.byref(p), _stream(stream, q.device)), "blasst_decode_gaps")
+    return gap_map
 
 
 def blasst_decode_noalloc(q, k_cache, v_cache, seq_lens, *, lam=0.0, scale=None, block_k=64, num_splits=0,

@@ -89,10 +89,17 @@ const char *blasst_last_error(void) { return g_last_error; }
 
 int blasst_abi_version(void) { return BLASST_ABI_VERSION; }
 
-blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
+} // extern "C"
+
+namespace {
+
+// gaps: the gap pass (blasst_prefill_gaps): o is neither read nor written.
+blasst_status run_prefill(const blasst_prefill_params *p, void *hip_stream, bool gaps)
 {
     if (p == nullptr)
         return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
+    if (gaps && p->gap_map == nullptr && p->skip_map == nullptr && p->counters == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "the gap pass needs gap_map, skip_map or counters");
     if (p->B < 0 || p->L < 0)
         return fail(BLASST_ERR_INVALID_ARG, "B and L must be >= 0");
     if (p->Hq <= 0 || p->Hkv <= 0 || p->Hq % p->Hkv != 0)
@@ -112,8 +119,9 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
         return s;
     if (blasst_status s = check_tensor(p->v, "v", false, false))
         return s;
-    if (blasst_status s = check_tensor(p->o, "o", false, true))
-        return s;
+    if (!gaps)
+        if (blasst_status s = check_tensor(p->o, "o", false, true))
+            return s;
     if (p->d != p->dv || (p->d != 64 && p->d != 128))
         return fail(BLASST_ERR_UNSUPPORTED, "prefill supports d = dv in {64, 128} (got d=%lld dv=%lld)",
                     (long long)p->d, (long long)p->dv);
@@ -155,12 +163,26 @@ blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
     a.win = window_arg(p->window, p->L);
     const bool skip = p->lambda > 0.0;
     hipError_t e = blasst::launch_prefill(a, (int)p->d, p->tile_q, p->causal != 0, skip,
-                                          p->o.dtype == BLASST_BF16, (hipStream_t)hip_stream);
+                                          p->o.dtype == BLASST_BF16, (hipStream_t)hip_stream, gaps);
     if (e == hipErrorInvalidValue)
         return fail(BLASST_ERR_UNSUPPORTED, "no prefill kernel for this configuration");
     if (e != hipSuccess)
         return fail(BLASST_ERR_LAUNCH, "prefill launch failed: %s", hipGetErrorString(e));
     return BLASST_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+blasst_status blasst_prefill(const blasst_prefill_params *p, void *hip_stream)
+{
+    return run_prefill(p, hip_stream, false);
+}
+
+blasst_status blasst_prefill_gaps(const blasst_prefill_params *p, void *hip_stream)
+{
+    return run_prefill(p, hip_stream, true);
 }
 
 namespace {
@@ -178,7 +200,9 @@ DecodeKind decode_kind(const blasst_decode_params *p)
 }
 
 // pg: the paging fields of blasst_decode_paged, nullptr for a contiguous cache.
-blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode_paged_params *pg = nullptr)
+// gaps: the gap pass (blasst_decode_gaps), which does not touch o.
+blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode_paged_params *pg = nullptr,
+                              bool gaps = false)
 {
     if (p == nullptr)
         return fail(BLASST_ERR_INVALID_ARG, "params: null pointer");
@@ -204,8 +228,9 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
         return s;
     if (blasst_status s = check_tensor(p->v_cache, "v_cache", false, false))
         return s;
-    if (blasst_status s = check_tensor(p->o, "o", true, true))
-        return s;
+    if (!gaps)
+        if (blasst_status s = check_tensor(p->o, "o", true, true))
+            return s;
     if (p->block_k != 64)
         return fail(BLASST_ERR_UNSUPPORTED, "block_k must be 64 (got %d)", p->block_k);
     const DecodeKind kind = decode_kind(p);
@@ -285,12 +310,14 @@ blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_
 namespace {
 
 blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_paged_params *pg, void *workspace,
-                         size_t workspace_bytes, void *hip_stream)
+                         size_t workspace_bytes, void *hip_stream, bool gaps = false)
 {
-    if (blasst_status s = validate_decode(p, pg))
+    if (blasst_status s = validate_decode(p, pg, gaps))
         return s;
+    if (gaps && p->gap_map == nullptr && p->skip_map == nullptr && p->counters == nullptr)
+        return fail(BLASST_ERR_INVALID_ARG, "the gap pass needs gap_map, skip_map or counters");
     const int S = choose_splits(p);
-    const size_t need = workspace_for(p, S);
+    const size_t need = gaps ? 0 : workspace_for(p, S);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(BLASST_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -314,7 +341,7 @@ blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_page
     const double scale = p->scale > 0 ? p->scale : 1.0 / std::sqrt((double)p->dqk);
     a.scale_log2 = (float)(scale * kLog2e);
     a.lnlam2 = log2_lambda(p->lambda);
-    if (S > 1) {
+    if (S > 1 && !gaps) {
         const int64_t units = p->B * p->Hkv * S * a.G;
         a.part_o = (float *)workspace;
         a.part_ml = a.part_o + units * p->dv;
@@ -334,7 +361,7 @@ blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_page
         a.page_shift = shift;
     }
     hipError_t e = blasst::launch_decode(a, (int)p->dqk, (int)p->dv, p->lambda > 0.0, p->o.dtype == BLASST_BF16,
-                                         (hipStream_t)hip_stream);
+                                         (hipStream_t)hip_stream, gaps);
     if (e == hipErrorInvalidValue)
         return fail(BLASST_ERR_UNSUPPORTED, "no decode kernel for this configuration");
     if (e != hipSuccess)
@@ -349,6 +376,11 @@ extern "C" {
 blasst_status blasst_decode(const blasst_decode_params *p, void *workspace, size_t workspace_bytes, void *hip_stream)
 {
     return run_decode(p, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+blasst_status blasst_decode_gaps(const blasst_decode_params *p, void *hip_stream)
+{
+    return run_decode(p, nullptr, nullptr, 0, hip_stream, true);
 }
 
 blasst_status blasst_decode_paged_plan(const blasst_decode_paged_params *p, int *num_splits_used,

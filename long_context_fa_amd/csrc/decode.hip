@@ -27,6 +27,9 @@
 //     A skipped block issues no V load at all.
 // Each wave keeps its own online-softmax state; the 4 states are merged with
 // the log-sum-exp rule at the end, and across splits by the combine kernel.
+// The gap pass (GAPS) keeps steps 1-2 and the maps: no V copy, no
+// exponential, no P.V, no partials (the decisions use the prefix max, which
+// does not depend on them).
 #include "device.h"
 #include "kernels.h"
 
@@ -49,7 +52,7 @@ __device__ __forceinline__ int dswz(int row)
     return DG > 8 ? (row & 7) << 1 : ((row >> 1) & 3) << 1;
 }
 
-template <int D, bool SKIP, bool OUT_BF16, bool PAGED>
+template <int D, bool SKIP, bool OUT_BF16, bool PAGED, bool GAPS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_kernel(const DecodeArgs a)
 {
@@ -62,7 +65,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     constexpr int NS = D / 32;         // 32-wide k-steps of the QK product
     constexpr int NDT = D / 16;        // 16-row d tiles of O^T
     constexpr int KLOADS = 4 * NS;     // K register loads per wave per block
-    __shared__ __attribute__((aligned(1024))) char vsm[NWD * TB];
+    __shared__ __attribute__((aligned(1024))) char vsm[GAPS ? 1024 : NWD * TB];
     __shared__ float mblk[2][NWD][16];
     __shared__ float mw_s[NWD][16], lw_s[NWD][16];
 
@@ -285,7 +288,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
         n_skipped += batch_skipped;
 
-        const bool exec = j < je && !my_skip;
+        const bool exec = !GAPS && j < je && !my_skip;
         if (exec)
             copy_v(j, pc); // V only for an executed block
         const bool more = j0 + NWD < je;
@@ -349,6 +352,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     }
 
     // Merge the 4 wave states (log-sum-exp), then write O or the split partial.
+    if (!GAPS) {
     float l = lsum;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -399,6 +403,7 @@ void decode_gqa_kernel(const DecodeArgs a)
             }
         }
     }
+    } // !GAPS
 
     if (tid == 0) {
         // Blocks that no split visits: before the window (first split writes
@@ -499,13 +504,17 @@ hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_
 namespace {
 
 template <int D, bool SKIP, bool OUT_BF16>
-hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream)
+hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream, bool gaps)
 {
     const dim3 grid(a.num_splits, a.Hkv, a.B);
+    if (gaps) { // decisions through the skip kernel's rule, nothing executed, no partials
+        hipLaunchKernelGGL((decode_gqa_kernel<D, true, false, false, true>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.page_table)
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, true, false>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, false, false>), grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1)
         return e;
@@ -514,26 +523,31 @@ hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream)
 
 } // namespace
 
-hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream);
+hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream, bool gaps);
 
-hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16, hipStream_t stream)
+hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16, hipStream_t stream,
+                         bool gaps)
 {
     if (a.B == 0)
         return hipSuccess;
     if (dqk == dv && a.G <= 16) {
         if (dqk == 128) {
             if (skip)
-                return out_bf16 ? launch_gqa<128, true, true>(a, stream) : launch_gqa<128, true, false>(a, stream);
-            return out_bf16 ? launch_gqa<128, false, true>(a, stream) : launch_gqa<128, false, false>(a, stream);
+                return out_bf16 ? launch_gqa<128, true, true>(a, stream, gaps)
+                                : launch_gqa<128, true, false>(a, stream, gaps);
+            return out_bf16 ? launch_gqa<128, false, true>(a, stream, gaps)
+                            : launch_gqa<128, false, false>(a, stream, gaps);
         }
         if (dqk == 64) {
             if (skip)
-                return out_bf16 ? launch_gqa<64, true, true>(a, stream) : launch_gqa<64, true, false>(a, stream);
-            return out_bf16 ? launch_gqa<64, false, true>(a, stream) : launch_gqa<64, false, false>(a, stream);
+                return out_bf16 ? launch_gqa<64, true, true>(a, stream, gaps)
+                                : launch_gqa<64, true, false>(a, stream, gaps);
+            return out_bf16 ? launch_gqa<64, false, true>(a, stream, gaps)
+                            : launch_gqa<64, false, false>(a, stream, gaps);
         }
     }
     if (dqk == 576 && dv == 512 && a.G == 128)
-        return launch_mla(a, skip, out_bf16, stream);
+        return launch_mla(a, skip, out_bf16, stream, gaps);
     return hipErrorInvalidValue;
 }
 

@@ -20,10 +20,11 @@ struct PrefillArgs {
     int win; // sliding window: query i sees keys > i - win (2^30 when there is none)
 };
 
-// Launches the prefill kernel for (d, tile_q, causal, skip, out dtype).
+// Launches the prefill kernel for (d, tile_q, causal, skip, out dtype); gaps
+// selects the gap pass (maps and counters only, O untouched).
 // Returns hipErrorInvalidValue if no kernel is compiled for the combination.
 hipError_t launch_prefill(const PrefillArgs &a, int d, int tile_q, bool causal, bool skip,
-                          bool out_bf16, hipStream_t stream);
+                          bool out_bf16, hipStream_t stream, bool gaps);
 
 struct DecodeArgs {
     const uint16_t *q, *k, *v;
@@ -51,8 +52,9 @@ struct DecodeArgs {
 
 // GQA/MQA/MHA decode (dqk = dv in {64, 128}, G <= 16) and latent (MLA) decode
 // (dqk 576, dv 512, G 128).  The combine kernel runs when num_splits > 1.
+// gaps selects the gap pass (maps and counters only: no O, no partials).
 hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16,
-                         hipStream_t stream);
+                         hipStream_t stream, bool gaps);
 
 // Log-sum-exp merge of the split partials into O (num_splits > 1).
 hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_t stream);

@@ -27,6 +27,9 @@
 //    (ds_read_b64_tr_b16) from the same K tile;
 //  * split partials (O, max, sum) go to the workspace for the log-sum-exp
 //    combine kernel, or O is written directly for a single split.
+// The gap pass (GAPS) keeps the tile copies, the scores, the votes and the
+// maps, advances the running max over every block (a skip never changes it)
+// and executes nothing.
 #include "acc.h"
 #include "kernels.h"
 
@@ -59,7 +62,7 @@ constexpr int NDT = DV / 32;         // O^T d tiles (16)
 __host__ __device__ constexpr int swzl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __host__ __device__ constexpr int swzr(int r) { return (r >> 1) & 7; }
 
-template <bool SKIP, bool OUT_BF16, bool PAGED>
+template <bool SKIP, bool OUT_BF16, bool PAGED, bool GAPS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mla_kernel(const DecodeArgs a)
 {
@@ -159,7 +162,8 @@ void decode_mla_kernel(const DecodeArgs a)
             voffv[t][x] = ra * LRB + ((4 * x + 2 * vmb + (vq >> 1)) ^ swzl(ra)) * 16 + (vq & 1) * 8;
     }
 
-    acc_zero();
+    if (!GAPS) // the gap pass holds no accumulator
+        acc_zero();
     float m2 = neg_inf(), lsum = 0.f;
     int n_skipped = 0;
 
@@ -239,7 +243,8 @@ void decode_mla_kernel(const DecodeArgs a)
             for (int r = 0; r < 16; ++r)
                 mt = fmaxf(mt, sc[kt][r]);
         mt = max_xor32(mt);
-        const float mt2 = mt * a.scale_log2;
+        float mt2 = mt * a.scale_log2;
+        asm volatile("" : "+v"(mt2)); // a rounded value: the gap mt2 - m2 is the same in every kernel variant
         if (it < 0) {
             m2 = mt2; // the seed: no vote, no P.V for this block
             wait_vmcnt<0>();
@@ -281,7 +286,10 @@ void decode_mla_kernel(const DecodeArgs a)
             if (a.gap_map)
                 a.gap_map[idx] = g * 0.69314718055994531f;
         }
-        if (!skip) {
+        if (GAPS) {
+            m2 = fmaxf(m2, mt2); // the running max, over every block
+            n_skipped += skip ? 1 : 0;
+        } else if (!skip) {
             const float mnew = fmaxf(m2, mt2);
             const float msafe = mnew == neg_inf() ? 0.f : mnew;
             const float alpha = mnew > m2 ? exp2_hw(m2 - msafe) : 1.f;
@@ -346,7 +354,9 @@ void decode_mla_kernel(const DecodeArgs a)
 
     // Output: O^T lane (n, hh) holds head `head`, d = 32dt + 8g + 4hh + i.
     const float l = lsum + __shfl_xor(lsum, 32);
-    if (S == 1) {
+    if (GAPS) {
+        // no output
+    } else if (S == 1) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         char *ob = (char *)a.o;
         const int64_t base = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh;
@@ -415,18 +425,22 @@ template <bool SKIP, bool OUT_BF16>
 void launch_mla_variant(const DecodeArgs &a, dim3 grid, hipStream_t stream)
 {
     if (a.page_table)
-        hipLaunchKernelGGL((decode_mla_kernel<SKIP, OUT_BF16, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_mla_kernel<SKIP, OUT_BF16, true, false>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_mla_kernel<SKIP, OUT_BF16, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_mla_kernel<SKIP, OUT_BF16, false, false>), grid, dim3(256), 0, stream, a);
 }
 
 } // namespace
 
-hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream)
+hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream, bool gaps)
 {
     if (a.G != 128 || a.Hkv != 1)
         return hipErrorInvalidValue;
     const dim3 grid(a.num_splits, 1, a.B);
+    if (gaps) {
+        hipLaunchKernelGGL((decode_mla_kernel<true, false, false, true>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     if (skip) {
         if (out_bf16)
             launch_mla_variant<true, true>(a, grid, stream);

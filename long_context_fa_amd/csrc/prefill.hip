@@ -36,6 +36,13 @@
 //    compares against log2(lambda), exponentials are v_exp_f32.  The
 //    accumulator rescale is skipped when no row of the wave raised its max
 //    (after the first blocks the running max rarely moves).
+//  * Gap pass (GAPS): the same loop with the executed work removed -- no V
+//    copy, no exponential, no P.V, no O -- and the running max advanced over
+//    every block.  A skip never changes the running max (a skipped block has
+//    m~ < m + ln(lambda) <= m), so these are the gaps and decisions of the
+//    full pass; calibration needs only them (BLASST summary, section 2
+//    "Calibracao Automatica": lambda is found by a search over the achieved
+//    sparsity).
 #include "device.h"
 #include "kernels.h"
 
@@ -75,8 +82,9 @@ __device__ __forceinline__ int tile_phase(int t, int nqt)
     return t >= t1 ? 0 : t >= t2 ? 1 : t >= t3 ? 2 : 3;
 }
 
-template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16>
-__global__ __launch_bounds__(2 * BR) __attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, 2)))
+template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16, bool GAPS>
+__global__ __launch_bounds__(2 * BR)
+__attribute__((amdgpu_waves_per_eu((D * 64 / BR) <= 64 ? 2 : 1, GAPS ? 4 : 2))) // no O or P: the gap pass fits more
 void prefill_kernel(const PrefillArgs a)
 {
     constexpr int NW = BR / 32;          // waves
@@ -88,7 +96,7 @@ void prefill_kernel(const PrefillArgs a)
     static_assert(KI >= 1 && KI * NW * 1024 == TB, "tile shape");
 
     // K ring (2 tiles) and V ring (2 tiles).
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
+    __shared__ __attribute__((aligned(1024))) char smem[(GAPS ? 2 : 4) * TB]; // the gap pass has no V ring
     __shared__ int vote[2][NW];
     __shared__ float gapw[2][NW];
 
@@ -149,7 +157,8 @@ void prefill_kernel(const PrefillArgs a)
     const int L = a.L;
     const int qrow = r0 + 32 * w + n;
     const bool row_valid = qrow < L;
-    const bool want_maps = a.skip_map != nullptr || a.gap_map != nullptr;
+    // the gap pass always forms the tile gap (its skip count needs it)
+    const bool want_maps = GAPS || a.skip_map != nullptr || a.gap_map != nullptr;
 
     const uint16_t *qp = a.q + b * a.q_sb + h * a.q_sh;
     const uint16_t *kp = a.k + b * a.k_sb + hk * a.k_sh;
@@ -259,6 +268,11 @@ void prefill_kernel(const PrefillArgs a)
             for (int r = 0; r < 16; ++r)
                 mt = fmaxf(mt, s[kt][r]);
         mt2 = max_xor32(mt) * a.scale_log2;
+        // The scaled block max is a rounded fp32 value in every instantiation:
+        // the gap mt2 - m2 must not fuse the scale into its subtraction in
+        // some kernels and not in others, so that the gap pass, the dense
+        // pass and the skip pass write bit-identical gap maps.
+        asm volatile("" : "+v"(mt2));
     };
 
     float m2 = neg_inf(); // running max of this lane's row (base 2)
@@ -412,18 +426,22 @@ void prefill_kernel(const PrefillArgs a)
         }
         n_skipped += skip ? 1 : 0;
         const bool ecur = !skip;
-        if (ecur)
+        if (!GAPS && ecur)
             copy_tile(vp, a.v_st, voff, j, vbuf(j)); // V_j only for an executed block
 
-        if (eprev)
-            pv(j - 1, pprev); // P_{j-1} is dead afterwards
-        if (ecur)
-            softmax(sc, mtc, pprev); // P_j reuses its registers
+        if (GAPS) {
+            m2 = fmaxf(m2, mtc); // the running max, over every block
+        } else {
+            if (eprev)
+                pv(j - 1, pprev); // P_{j-1} is dead afterwards
+            if (ecur)
+                softmax(sc, mtc, pprev); // P_j reuses its registers
+        }
         if (j + 1 < nvis) {
             scores(j + 1, sn, mtn); // into the other register set
             vote_block(j + 1, mtn);
         }
-        eprev = ecur;
+        eprev = GAPS ? false : ecur;
     };
 
     copy_tile(kp, a.k_st, koff, jlo, kbuf(jlo));
@@ -452,7 +470,7 @@ void prefill_kernel(const PrefillArgs a)
     // Finalize: O = acc / l, l summed over the two lane halves.
     const float l = lsum + __shfl_xor(lsum, 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (row_valid) {
+    if (!GAPS && row_valid) {
         char *ob = (char *)a.o;
         const int64_t base = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)qrow * a.o_st;
 #pragma unroll
@@ -491,20 +509,22 @@ void prefill_kernel(const PrefillArgs a)
     }
 }
 
-template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16>
+template <int D, int BR, bool CAUSAL, bool SKIP, bool OUT_BF16, bool GAPS = false>
 hipError_t launch_one(const PrefillArgs &a, hipStream_t stream)
 {
     const unsigned grid = (unsigned)a.nqt * (unsigned)a.Hq * (unsigned)a.B;
     if (grid == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((prefill_kernel<D, BR, CAUSAL, SKIP, OUT_BF16>), dim3(grid), dim3(2 * BR), 0,
+    hipLaunchKernelGGL((prefill_kernel<D, BR, CAUSAL, SKIP, OUT_BF16, GAPS>), dim3(grid), dim3(2 * BR), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 template <int D, int BR>
-hipError_t launch_tile(const PrefillArgs &a, bool causal, bool skip, bool out_bf16, hipStream_t s)
+hipError_t launch_tile(const PrefillArgs &a, bool causal, bool skip, bool out_bf16, hipStream_t s, bool gaps)
 {
+    if (gaps) // decisions through the skip kernel's vote; O is not written
+        return causal ? launch_one<D, BR, true, true, false, true>(a, s) : launch_one<D, BR, false, true, false, true>(a, s);
     if (causal) {
         if (skip)
             return out_bf16 ? launch_one<D, BR, true, true, true>(a, s) : launch_one<D, BR, true, true, false>(a, s);
@@ -518,16 +538,16 @@ hipError_t launch_tile(const PrefillArgs &a, bool causal, bool skip, bool out_bf
 } // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, int d, int tile_q, bool causal, bool skip, bool out_bf16,
-                          hipStream_t stream)
+                          hipStream_t stream, bool gaps)
 {
     if (d == 128 && tile_q == 128)
-        return launch_tile<128, 128>(a, causal, skip, out_bf16, stream);
+        return launch_tile<128, 128>(a, causal, skip, out_bf16, stream, gaps);
     if (d == 128 && tile_q == 64)
-        return launch_tile<128, 64>(a, causal, skip, out_bf16, stream);
+        return launch_tile<128, 64>(a, causal, skip, out_bf16, stream, gaps);
     if (d == 64 && tile_q == 128)
-        return launch_tile<64, 128>(a, causal, skip, out_bf16, stream);
+        return launch_tile<64, 128>(a, causal, skip, out_bf16, stream, gaps);
     if (d == 64 && tile_q == 64)
-        return launch_tile<64, 64>(a, causal, skip, out_bf16, stream);
+        return launch_tile<64, 64>(a, causal, skip, out_bf16, stream, gaps);
     return hipErrorInvalidValue;
 }
 

@@ -403,3 +403,22 @@ def test_noalloc_decode_refuses_partials_beyond_the_scratch_before_any_launch():
     assert lib.blasst_decode_plan(ctypes.byref(p), None, ctypes.byref(ws)) == 0 and ws.value > cap
     assert lib.blasst_decode_noalloc(ctypes.byref(p), None) == 3
     assert "scratch" in bl.blasst_last_error()
+
+
+def test_gap_passes_need_an_output_and_validate_first():
+    """The gap passes write only maps and counters: with none of them given the
+    call is refused; other arguments are validated as for the full pass (raw
+    ABI calls with host pointers, refused before any launch)."""
+    lib = bl.load_library()
+    q, k, v = _bf16(1, 2, 128, 128), _bf16(1, 1, 128, 128), _bf16(1, 1, 128, 128)
+    p = _abi._prefill_params(q, k, v, None, True, 0.01, 128, 64, None, None, None, None, 0)
+    assert lib.blasst_prefill_gaps(ctypes.byref(p), None) == 1 and "gap pass" in bl.blasst_last_error()
+    gap = torch.zeros(1, 2, 1, 2)
+    p = _abi._prefill_params(q, k, v, None, True, 1.5, 128, 64, None, None, gap, None, 0)
+    assert lib.blasst_prefill_gaps(ctypes.byref(p), None) == 1 and "lambda" in bl.blasst_last_error()
+    qd, kc = _bf16(2, 8, 128), _bf16(2, 2, 256, 128)
+    lens = torch.full((2,), 256, dtype=torch.int32)
+    p = _abi._decode_params(qd, kc, kc, lens, 0.01, None, 64, 0, None, None, None, None)
+    assert lib.blasst_decode_gaps(ctypes.byref(p), None) == 1 and "gap pass" in bl.blasst_last_error()
+    p = _abi._decode_params(qd, kc, kc, lens, 0.01, None, 128, 0, None, None, torch.zeros(2, 2, 4), None)
+    assert lib.blasst_decode_gaps(ctypes.byref(p), None) == 2  # block_k 128 is not compiled

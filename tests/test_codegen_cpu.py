@@ -46,19 +46,33 @@ def _outside_asm(text):
     return keep
 
 
+def _functions(text, kname):
+    """(mangled name, body) of every instantiation of kernel ``kname``."""
+    return re.findall(r"^(_Z\S*" + kname + r"\S*):(.*?)^\.Lfunc_end", text, re.S | re.M)
+
+
+def _gap_pass(mangled):
+    # the last bool template argument is the gap pass, which holds no accumulator
+    return mangled.split("EEEv")[0].endswith("Lb1")
+
+
 def test_compiler_emits_no_agpr_access(kasm):
-    _, text = kasm
+    kname, text = kasm
     agpr = re.compile(r"\ba\[\d|\ba\d+\b|accvgpr")
-    bad = [l for l in _outside_asm(text) if agpr.search(l) and not l.strip().startswith(".")]
-    assert not bad, "compiler-generated AGPR access:\n" + "\n".join(bad[:10])
+    funcs = [(n, body) for n, body in _functions(text, kname) if not _gap_pass(n)]
+    assert len(funcs) >= 4
+    for name, body in funcs:
+        bad = [l for l in _outside_asm(body) if agpr.search(l) and not l.strip().startswith(".")]
+        assert not bad, f"{name}: compiler-generated AGPR access:\n" + "\n".join(bad[:10])
 
 
 def test_no_scratch_and_all_agprs_reserved(kasm):
     kname, text = kasm
     kernels = re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S)
     mine = [(n, body) for n, body in kernels if kname in n]
-    assert len(mine) >= 4
+    assert len(mine) >= 5
     for name, body in mine:
         f = dict(re.findall(r"\.amdhsa_(\w+) (\d+)", body))
         assert int(f["private_segment_fixed_size"]) == 0, f"{name} spills"
-        assert int(f["next_free_vgpr"]) - int(f["accum_offset"]) >= 256, f"{name} reserves too few AGPRs"
+        if not _gap_pass(name):
+            assert int(f["next_free_vgpr"]) - int(f["accum_offset"]) >= 256, f"{name} reserves too few AGPRs"
