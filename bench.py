@@ -556,11 +556,14 @@ def window_prefill(q, k, v, out, W, steps, warmup):
     return res
 
 
-def bench_calibration(lengths=(4096, 8192, 16384, 32768, 65536), targets=(0.5, 0.7)):
-    """The calibration law lambda = a(target) / L on the GQA prefill generator.
+def bench_calibration(lengths=(4096, 8192, 16384, 32768, 65536, 131072), targets=(0.5, 0.7)):
+    """The calibration law lambda = a(target) / L on the GQA prefill generator,
+    over L = 4K .. 128K (one sequence of 32 query / 8 KV heads, d = 128).
 
-    For each L, lambda_L is the exact quantile of the gap map of a calibration
-    input (seed 2000 + L/1024); a is fitted as ln a = mean(ln(lambda_L * L)).
+    For each L, lambda_L is the exact quantile of the gap map (gap pass) of a
+    calibration input (seed 2000 + L/1024); a is fitted as ln a = mean(ln(lambda_L * L))
+    over all the lengths and stored as a table with its tiling (query tile 128,
+    key block 64).
     Fresh evaluation inputs (seed 1000 + L/1024) are then run with
     lambda = a / L from the fitted table, and the achieved block sparsity is
     compared with the target; so is the sparsity that the per-length lambda_L
@@ -576,19 +579,20 @@ def bench_calibration(lengths=(4096, 8192, 16384, 32768, 65536), targets=(0.5, 0
             lam_at[t].append(cal[t][0])
         del q, k, v
     a_fit = [bl.blasst_calibrate_fit(lam_at[t], lengths) for t in targets]
+    table = bl.calib_table(list(targets), a_fit, tile_q=128, block_k=64, num_splits=0)
     rows = []
     for L in lengths:
         q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda",
                                         seed=1000 + L // 1024)
-        def sparsity(lam):
+        def sparsity(lam):  # the gap pass counts the skips at lam (decisions as the full pass)
             cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
-            bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, counters=cnt)
+            bl.blasst_prefill_gaps(q, k, v, causal=True, lam=lam, tile_q=128, counters=cnt)
             torch.cuda.synchronize()
             vis, skp = (int(x) for x in cnt.cpu())
             return skp / vis
 
         for t in targets:
-            lam = bl.blasst_calibrate(list(targets), a_fit, t, L)
+            lam = bl.blasst_calibrate(table, t, L, tile_q=128, block_k=64, num_splits=0)
             lam_l = lam_at[t][list(lengths).index(L)]
             got, got_l = sparsity(lam), sparsity(lam_l)
             rows.append({"L": L, "target": t, "lambda_L_calibrated": lam_l, "lambda_L_times_L": lam_l * L,
@@ -601,6 +605,7 @@ def bench_calibration(lengths=(4096, 8192, 16384, 32768, 65536), targets=(0.5, 0
     return {"workload": "GQA causal prefill B=1 Hq=32 Hkv=8 d=128, tile 128, block 64; calibration seeds "
                         "2000+L/1024, evaluation seeds 1000+L/1024",
             "a_fit": dict(zip([str(t) for t in targets], a_fit)),
+            "table": table,
             "mean_abs_deviation": {str(t): float(np.mean([abs(r["deviation"]) for r in rows if r["target"] == t]))
                                    for t in targets},
             "rows": rows}

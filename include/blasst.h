@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BLASST_ABI_VERSION 2
+#define BLASST_ABI_VERSION 3
 
 typedef enum {
     BLASST_OK = 0,
@@ -296,18 +296,31 @@ blasst_status blasst_decode_noalloc(const blasst_decode_params *p, void *hip_str
  * blasst_calibrate(target_sparsity, L) -> lambda = a(target) / L.  The table
  * holds a fitted per target sparsity (strictly increasing targets, a > 0); ln a
  * is interpolated linearly in the target between rows.  Host only.
+ *
+ * A fitted a is not a universal constant (BLASST reading notes,
+ * papers.lqhl.me/papers/BLASST-MLSys26, "关键观察" observation 2: it is fitted
+ * on calibration data), and the decisions it was fitted on depend on the
+ * tiling: a tile skips a block only when all of its rows meet the test, and a
+ * decode split restarts the running max.  So the table records the tiling it
+ * was fitted with -- query tile (prefill), key block, and decode split count
+ * (0 for prefill) -- and a call states the tiling it will run with; a table
+ * fitted with another tiling is refused.
  * Errors: INVALID_ARG for a null or empty table, non-increasing targets,
- * a <= 0, L <= 0, a target outside [targets[0], targets[n-1]], or a result
- * lambda >= 1.
+ * a <= 0, L <= 0, a target outside [targets[0], targets[n-1]], a result
+ * lambda >= 1, or a tiling (tile_q, block_k, num_splits) other than the
+ * table's.
  */
 typedef struct {
     int n;
     const double *target;
     const double *a;
+    int tile_q;     /* query tile rows the table was fitted with (prefill; 0 for decode) */
+    int block_k;    /* key block (64) */
+    int num_splits; /* decode split count it was fitted with (0 for prefill) */
 } blasst_calib_table;
 
-blasst_status blasst_calibrate(const blasst_calib_table *table, double target_sparsity, int64_t L,
-                               double *lambda_out);
+blasst_status blasst_calibrate(const blasst_calib_table *table, double target_sparsity, int64_t L, int tile_q,
+                               int block_k, int num_splits, double *lambda_out);
 
 /* The calibration search at one length, host only.  gaps: host copy of a gap
  * map (entries of -inf, i.e. unvisited pairs, are ignored).  Because the

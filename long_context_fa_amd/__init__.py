@@ -15,11 +15,13 @@ Entry points (same names as the C ABI):
   blasst_decode_noalloc(q, k_cache, v_cache, seq_lens, lam, ...) -> O (no workspace)
   blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, ...) -> O
   blasst_decode_paged_plan(...)                        -> (num_splits, workspace bytes)
-  blasst_calibrate(targets, a, target, L)              -> lambda = a(target) / L
+  blasst_calibrate(table, target, L, tile_q=, block_k=, num_splits=) -> lambda = a(target) / L
+  calib_table(targets, a, tile_q=, block_k=, num_splits=) -> table (dict); save/load_calib_table (JSON)
   blasst_calibrate_search(gaps, target)                -> (lambda, reached sparsity)
   blasst_calibrate_fit(lambdas, lengths)               -> a
 """
-from ._abi import (BlasstError, blasst_abi_version, blasst_calibrate,  # noqa: F401
+from ._abi import (BlasstError, blasst_abi_version, blasst_calibrate, calib_table,  # noqa: F401
+                   load_calib_table, save_calib_table,
                    blasst_calibrate_fit, blasst_calibrate_search, blasst_decode,
                    blasst_decode_gaps, blasst_decode_noalloc, blasst_decode_paged, blasst_decode_paged_plan,
                    blasst_decode_plan, blasst_last_error, blasst_prefill, blasst_prefill_gaps,
@@ -30,5 +32,5 @@ __all__ = [
     "blasst_decode_paged",
     "blasst_decode_paged_plan", "blasst_calibrate",
     "blasst_calibrate_search", "blasst_calibrate_fit", "blasst_status_str", "blasst_last_error",
-    "blasst_abi_version", "library_path", "load_library",
+    "blasst_abi_version", "library_path", "load_library", "calib_table", "save_calib_table", "load_calib_table",
 ]

@@ -61,13 +61,14 @@ class _DecodePagedParams(ctypes.Structure):
 
 class _CalibTable(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int), ("target", ctypes.POINTER(ctypes.c_double)),
-                ("a", ctypes.POINTER(ctypes.c_double))]
+                ("a", ctypes.POINTER(ctypes.c_double)), ("tile_q", ctypes.c_int), ("block_k", ctypes.c_int),
+                ("num_splits", ctypes.c_int)]
 
 
 _lib = None
 
 # The parameter structs above mirror include/blasst.h at this ABI version.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def library_path():
@@ -106,8 +107,8 @@ def load_library():
     lib.blasst_decode_noalloc.restype = st
     lib.blasst_decode_noalloc.argtypes = [ctypes.POINTER(_DecodeParams), ctypes.c_void_p]
     lib.blasst_calibrate.restype = st
-    lib.blasst_calibrate.argtypes = [ctypes.POINTER(_CalibTable), ctypes.c_double, ctypes.c_int64,
-                                     ctypes.POINTER(ctypes.c_double)]
+    lib.blasst_calibrate.argtypes = [ctypes.POINTER(_CalibTable), ctypes.c_double, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.blasst_calibrate_search.restype = st
     lib.blasst_calibrate_search.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_double,
                                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
@@ -468,15 +469,39 @@ def blasst_decode_paged(q, k_pages, v_pages, page_table, seq_lens, Lmax, *, lam=
     return out
 
 
-def blasst_calibrate(targets, a, target, L):
-    """lambda = a(target) / L from a calibration table (ln a linear in the target)."""
-    n = len(targets)
-    t = (ctypes.c_double * n)(*[float(x) for x in targets])
-    aa = (ctypes.c_double * n)(*[float(x) for x in a])
-    table = _CalibTable(n, t, aa)
+def calib_table(targets, a, *, tile_q=128, block_k=64, num_splits=0):
+    """A calibration table (a plain dict, JSON-serialisable): fitted a per
+    target sparsity and the tiling the fit used (num_splits 0 for prefill;
+    tile_q 0 for decode)."""
+    return {"target": [float(x) for x in targets], "a": [float(x) for x in a], "tile_q": int(tile_q),
+            "block_k": int(block_k), "num_splits": int(num_splits)}
+
+
+def save_calib_table(table, path):
+    """Write a calibration table as JSON (the one state the method keeps between runs)."""
+    import json
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1)
+
+
+def load_calib_table(path):
+    import json
+    with open(path) as f:
+        t = json.load(f)
+    return calib_table(t["target"], t["a"], tile_q=t["tile_q"], block_k=t["block_k"], num_splits=t["num_splits"])
+
+
+def blasst_calibrate(table, target, L, *, tile_q=128, block_k=64, num_splits=0):
+    """lambda = a(target) / L from a calibration table (ln a linear in the
+    target) for a call with the given tiling; a table fitted with another
+    tiling is refused (decisions depend on it)."""
+    n = len(table["target"])
+    t = (ctypes.c_double * n)(*[float(x) for x in table["target"]])
+    aa = (ctypes.c_double * n)(*[float(x) for x in table["a"]])
+    ct = _CalibTable(n, t, aa, int(table["tile_q"]), int(table["block_k"]), int(table["num_splits"]))
     out = ctypes.c_double(0.0)
-    _check(load_library().blasst_calibrate(ctypes.byref(table), float(target), int(L), ctypes.byref(out)),
-           "blasst_calibrate")
+    _check(load_library().blasst_calibrate(ctypes.byref(ct), float(target), int(L), int(tile_q), int(block_k),
+                                           int(num_splits), ctypes.byref(out)), "blasst_calibrate")
     return out.value
 
 

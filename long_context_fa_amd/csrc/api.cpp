@@ -463,10 +463,16 @@ extern "C" blasst_status blasst_decode_noalloc(const blasst_decode_params *p, vo
 extern "C" {
 
 // ------------------------------------------------------------- calibration
-blasst_status blasst_calibrate(const blasst_calib_table *t, double target, int64_t L, double *lambda_out)
+blasst_status blasst_calibrate(const blasst_calib_table *t, double target, int64_t L, int tile_q, int block_k,
+                               int num_splits, double *lambda_out)
 {
     if (t == nullptr || lambda_out == nullptr || t->target == nullptr || t->a == nullptr || t->n < 1)
         return fail(BLASST_ERR_INVALID_ARG, "calibration table or output missing");
+    if (tile_q != t->tile_q || block_k != t->block_k || num_splits != t->num_splits)
+        return fail(BLASST_ERR_INVALID_ARG,
+                    "table fitted with tile_q=%d block_k=%d num_splits=%d; the call uses tile_q=%d block_k=%d "
+                    "num_splits=%d (decisions depend on the tiling)",
+                    t->tile_q, t->block_k, t->num_splits, tile_q, block_k, num_splits);
     for (int i = 0; i < t->n; ++i) {
         if (!(t->a[i] > 0.0) || std::isinf(t->a[i]))
             return fail(BLASST_ERR_INVALID_ARG, "table a[%d] must be positive and finite", i);

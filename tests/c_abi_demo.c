@@ -69,9 +69,10 @@ static int host_checks(void)
 
     /* ln a interpolated linearly in the target */
     const double tg[2] = {0.5, 0.7}, av[2] = {1e-3, 1e-2};
-    const blasst_calib_table table = {2, tg, av};
+    const blasst_calib_table table = {2, tg, av, 128, 64, 0}; /* fitted for tile 128, block 64, prefill */
     double l6 = 0;
-    CHECK(blasst_calibrate(&table, 0.6, 8192, &l6) == BLASST_OK, "calibrate: %s", blasst_last_error());
+    CHECK(blasst_calibrate(&table, 0.6, 8192, 128, 64, 0, &l6) == BLASST_OK, "calibrate: %s", blasst_last_error());
+    CHECK(blasst_calibrate(&table, 0.6, 8192, 64, 64, 0, &l6) == BLASST_ERR_INVALID_ARG, "other tiling accepted");
     CHECK(fabs(l6 / (sqrt(1e-3 * 1e-2) / 8192) - 1) < 1e-9, "calibrate lambda = %g", l6);
 
     /* exact quantile of a gap map: half of the 4 visited gaps below ln(lambda) */

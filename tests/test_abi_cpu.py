@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = bl.load_library()
     for name in declared:
         assert hasattr(lib, name), name
-    assert bl.blasst_abi_version() == 2
+    assert bl.blasst_abi_version() == 3
     for s in range(5):
         assert bl.blasst_status_str(s) != "unknown status"
     assert bl.blasst_status_str(99) == "unknown status"
@@ -271,18 +271,19 @@ def test_calibrate_matches_oracle():
     targets, a = [0.3, 0.5, 0.7, 0.8], [3.0, 40.0, 900.0, 4000.0]
     for target in [0.3, 0.41, 0.5, 0.66, 0.7, 0.79, 0.8]:
         for L in [4096, 8192, 32768, 65536]:
-            lam = bl.blasst_calibrate(targets, a, target, L)
+            lam = bl.blasst_calibrate(bl.calib_table(targets, a), target, L)
             ref = oracle.lambda_from_table(targets, a, target, L)
             assert abs(lam - ref) <= 1e-13 * ref
 
 
 def test_calibrate_rejects():
+    T = bl.calib_table
     with pytest.raises(bl.BlasstError):
-        bl.blasst_calibrate([0.3, 0.5], [3.0, 40.0], 0.9, 4096)   # outside the table
+        bl.blasst_calibrate(T([0.3, 0.5], [3.0, 40.0]), 0.9, 4096)   # outside the table
     with pytest.raises(bl.BlasstError):
-        bl.blasst_calibrate([0.5, 0.3], [3.0, 40.0], 0.4, 4096)   # not increasing
+        bl.blasst_calibrate(T([0.5, 0.3], [3.0, 40.0]), 0.4, 4096)   # not increasing
     with pytest.raises(bl.BlasstError):
-        bl.blasst_calibrate([0.5], [5000.0], 0.5, 4096)           # lambda >= 1
+        bl.blasst_calibrate(T([0.5], [5000.0]), 0.5, 4096)           # lambda >= 1
     with pytest.raises(bl.BlasstError):
         bl.blasst_calibrate_fit([0.0], [100])
     with pytest.raises(bl.BlasstError):
@@ -422,3 +423,25 @@ def test_gap_passes_need_an_output_and_validate_first():
     assert lib.blasst_decode_gaps(ctypes.byref(p), None) == 1 and "gap pass" in bl.blasst_last_error()
     p = _abi._decode_params(qd, kc, kc, lens, 0.01, None, 128, 0, None, None, torch.zeros(2, 2, 4), None)
     assert lib.blasst_decode_gaps(ctypes.byref(p), None) == 2  # block_k 128 is not compiled
+
+
+def test_calibration_table_carries_its_tiling(tmp_path):
+    """A fitted a belongs to the tiling it was fitted with (decisions depend on
+    the query tile and on the decode split count): blasst_calibrate refuses a
+    call with another tiling; a table survives a JSON round trip."""
+    pre = bl.calib_table([0.5, 0.7], [1e-6, 3e-4], tile_q=128, block_k=64, num_splits=0)
+    lam = bl.blasst_calibrate(pre, 0.7, 8192, tile_q=128, block_k=64, num_splits=0)
+    assert abs(lam - 3e-4 / 8192) <= 1e-15
+    for kw in (dict(tile_q=64), dict(block_k=128), dict(num_splits=4)):
+        args = dict(tile_q=128, block_k=64, num_splits=0)
+        args.update(kw)
+        with pytest.raises(bl.BlasstError) as ei:
+            bl.blasst_calibrate(pre, 0.7, 8192, **args)
+        assert ei.value.status == 1 and "tiling" in bl.blasst_last_error()
+    dec = bl.calib_table([0.7], [2e-2], tile_q=0, block_k=64, num_splits=4)
+    assert bl.blasst_calibrate(dec, 0.7, 32768, tile_q=0, num_splits=4) == pytest.approx(2e-2 / 32768, rel=1e-14)
+    with pytest.raises(bl.BlasstError):
+        bl.blasst_calibrate(dec, 0.7, 32768, tile_q=0, num_splits=1)
+    path = tmp_path / "table.json"
+    bl.save_calib_table(pre, str(path))
+    assert bl.load_calib_table(str(path)) == pre
