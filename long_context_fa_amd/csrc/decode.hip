@@ -388,7 +388,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         for (int i = 0; i < NWD; ++i)
             lh += lw_s[i][hd] * exp2_hw(mw_s[i][hd] - Mhs);
         if (S == 1) {
-            const float val = lh > 0.f ? acc / lh : 0.f;
+            const float val = lh != 0.f ? acc / lh : 0.f; // 0 when no key was seen; NaN l gives NaN
             const int64_t off = (int64_t)b * a.o_sb + (int64_t)(g * G + hd) * a.o_sh + d;
             if (OUT_BF16)
                 ((__bf16 *)a.o)[off] = (__bf16)val;
@@ -434,7 +434,8 @@ void decode_gqa_kernel(const DecodeArgs a)
 // columns of one (sequence, query head); a workgroup covers 256 / (dv/4)
 // heads.  Weights are exp2(m_s - M) with M the largest split max among
 // splits that saw keys (kept as a running max, one chunk of splits at a
-// time); splits with l = 0 contribute nothing.
+// time); splits with l = 0 contribute nothing, and a NaN l (a NaN score)
+// takes part, so the NaN reaches O.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a, int dv)
 {
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a,
         float Mc = M;
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            if (s0 + i < S && ml[i].y > 0.f)
+            if (s0 + i < S && ml[i].y != 0.f)
                 Mc = fmaxf(Mc, ml[i].x);
         const float Ms = Mc == neg_inf() ? 0.f : Mc;
         const float r = M == neg_inf() ? 0.f : exp2_hw(M - Ms);
@@ -473,14 +474,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a,
         den *= r;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const float wgt = (s0 + i < S && ml[i].y > 0.f) ? exp2_hw(ml[i].x - Ms) : 0.f;
-            num += wgt * po[i];
-            den += wgt * ml[i].y;
+            if (s0 + i < S && ml[i].y != 0.f) {
+                const float wgt = exp2_hw(ml[i].x - Ms);
+                num += wgt * po[i];
+                den += wgt * ml[i].y;
+            }
         }
         M = Mc;
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    const f32x4 val = num * inv;
+    const f32x4 val = den != 0.f ? num * (1.f / den) : f32x4{};
     const int64_t off = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + d;
     if (OUT_BF16)
         *(bf16x4 *)((__bf16 *)a.o + off) = __builtin_convertvector(val, bf16x4);

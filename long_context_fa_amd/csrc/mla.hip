@@ -357,7 +357,8 @@ void decode_mla_kernel(const DecodeArgs a)
     if (GAPS) {
         // no output
     } else if (S == 1) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = 1.f / l; // exactly 0 below when l = 0 (no key seen); NaN l gives NaN
+        const bool none = l == 0.f;
         char *ob = (char *)a.o;
         const int64_t base = (int64_t)b * a.o_sb + (int64_t)head * a.o_sh;
 #pragma unroll
@@ -366,8 +367,9 @@ void decode_mla_kernel(const DecodeArgs a)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * dt + 8 * g + 4 * hh;
-                const f32x4 v4 = {od[4 * g] * inv, od[4 * g + 1] * inv, od[4 * g + 2] * inv,
-                                  od[4 * g + 3] * inv};
+                f32x4 v4 = {od[4 * g] * inv, od[4 * g + 1] * inv, od[4 * g + 2] * inv, od[4 * g + 3] * inv};
+                if (none)
+                    v4 = f32x4{};
                 if (OUT_BF16)
                     *(bf16x4 *)(ob + 2 * (base + d)) = __builtin_convertvector(v4, bf16x4);
                 else

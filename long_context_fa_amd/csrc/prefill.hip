@@ -182,9 +182,12 @@ void prefill_kernel(const PrefillArgs a)
 
     // Tile copy: wave w fills rows [w*KI*RPI, (w+1)*KI*RPI); lane -> (row, chunk)
     // with the chunk XOR-swizzled by the row (pswz).  Per-lane byte offsets of
-    // a whole tile are computed once: a block that lies entirely below L
-    // costs one scalar add per tile copy.  Rows past L re-read row L-1
-    // (finite data; those keys are masked to -inf).
+    // a whole tile are computed once: a block that lies entirely inside the
+    // tile's key range costs one scalar add per tile copy.  Keys no row of the
+    // tile sees -- past L, or below the window of its first row -- re-read the
+    // nearest key some row sees (kmin or L-1): they are masked to -inf, and
+    // their 0 * V then repeats a value the tile already multiplies, so a
+    // non-finite V outside the tile's keys never reaches it.
     uint32_t koff[KI], voff[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -193,8 +196,9 @@ void prefill_kernel(const PrefillArgs a)
         koff[i] = (uint32_t)((row * a.k_st + c * 8) * 2);
         voff[i] = (uint32_t)((row * a.v_st + c * 8) * 2);
     }
+    const int kmin = CAUSAL && r0 - a.win + 1 > 0 ? r0 - a.win + 1 : 0; // lowest key a row of the tile sees
     auto copy_tile = [&](const uint16_t *base, int64_t st, const uint32_t *off, int j, char *dst) {
-        if ((j + 1) * BC <= L) {
+        if ((j + 1) * BC <= L && j * BC >= kmin) {
             const uint16_t *sb = base + (int64_t)j * BC * st;
 #pragma unroll
             for (int i = 0; i < KI; ++i)
@@ -206,7 +210,7 @@ void prefill_kernel(const PrefillArgs a)
                 const int row = ins * RPI + lane / DG;
                 const int c = (lane % DG) ^ pswz<DG>(row);
                 int key = j * BC + row;
-                key = key < L ? key : L - 1;
+                key = key < L ? (key > kmin ? key : kmin) : L - 1;
                 copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024);
             }
         }
@@ -467,9 +471,11 @@ void prefill_kernel(const PrefillArgs a)
         pv(nvis - 1, pprev);
     }
 
-    // Finalize: O = acc / l, l summed over the two lane halves.
+    // Finalize: O = acc / l, l summed over the two lane halves; exactly 0 for
+    // a row that saw no key (l = 0), NaN when l is NaN.
     const float l = lsum + __shfl_xor(lsum, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = 1.f / l;
+    const bool none = l == 0.f;
     if (!GAPS && row_valid) {
         char *ob = (char *)a.o;
         const int64_t base = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)qrow * a.o_st;
@@ -480,6 +486,8 @@ void prefill_kernel(const PrefillArgs a)
                 const int d = 32 * dt + 8 * g + 4 * hh;
                 f32x4 v4 = {o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
                             o[dt][4 * g + 3] * inv};
+                if (none)
+                    v4 = f32x4{};
                 if (OUT_BF16) {
                     bf16x4 bv = __builtin_convertvector(v4, bf16x4);
                     *(bf16x4 *)(ob + 2 * (base + d)) = bv;

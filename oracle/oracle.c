@@ -62,6 +62,21 @@
  *
  * Arithmetic is IEEE fp64 with libm exp/log, loops in the order written.
  * Inputs are fp64 arrays (the tests pass the exact bf16 values the GPU reads).
+ *
+ * Non-finite inputs (the pages say nothing about them; this is the reading
+ * both sides implement):
+ *  - a block max, the running max and the max over a tile's row gaps ignore
+ *    NaN (a NaN score is not greater than anything); a row gap that is NaN
+ *    (inf - inf) therefore never keeps a block from being skipped;
+ *  - in an executed block every key that some row of the unit sees
+ *    contributes p * V to every row's accumulator and p to its sum, with
+ *    p = 0 for a row that does not see the key; 0 * inf and 0 * NaN are NaN,
+ *    so a non-finite V value reaches every row of a unit that executes its
+ *    block.  Keys that no row of the unit sees contribute nothing;
+ *  - O = acc / l when l != 0 (a NaN l gives NaN), and exactly 0 when l = 0
+ *    (the row saw no key);
+ *  - the split merge takes every split with l != 0 (NaN included) and the
+ *    max of their running maxima.
  */
 #include <math.h>
 #include <stdint.h>
@@ -110,9 +125,11 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
         for (int64_t x = 0; x < dv; ++x)
             acc[r * dv + x] = 0.0;
     }
+    uint8_t seen[bc]; /* key c of the block is seen by some row of the unit */
     for (int64_t j = j_begin; j < j_end; ++j) {
         int64_t c0 = j * bc;
         int any = 0;
+        memset(seen, 0, (size_t)bc);
         /* Scores of the block and the block-local row max m~ (BLASST summary, section 2). */
         for (int64_t r = 0; r < R; ++r) {
             const double *qr = q + r * q_stride;
@@ -131,8 +148,9 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
                     dot += qr[x] * kc[x];
                 double s = scale * dot;
                 S[r * bc + c] = s;
-                if (s > mt[r])
+                if (s > mt[r]) /* a NaN score never raises the max */
                     mt[r] = s;
+                seen[c] = 1;
                 any = 1;
             }
         }
@@ -164,21 +182,22 @@ static void oracle_unit(int64_t R, int64_t d, int64_t dv,
             continue; /* no exp, no V read, no P.V, no change to m, l, acc */
         }
         skip[jj] = 0;
-        /* Textbook online-softmax update of the executed block. */
+        /* Textbook online-softmax update of the executed block.  Every key
+         * that some row of the unit sees enters every row, with p = 0 where the
+         * row does not see it (a row that has seen no key yet keeps m = -inf
+         * and l = 0 and only gathers 0 * V). */
         for (int64_t r = 0; r < R; ++r) {
             double mp = m[r] > mt[r] ? m[r] : mt[r];
-            if (mp == -INFINITY)
-                continue; /* row has seen no valid key yet */
             double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - mp);
             double *ar = acc + r * dv;
             double rowsum = 0.0;
             for (int64_t x = 0; x < dv; ++x)
                 ar[x] *= alpha;
             for (int64_t c = 0; c < bc; ++c) {
+                if (!seen[c])
+                    continue; /* no row of the unit sees this key */
                 double s = S[r * bc + c];
-                if (s == -INFINITY)
-                    continue;
-                double p = exp(s - mp);
+                double p = (s == -INFINITY) ? 0.0 : exp(s - mp);
                 rowsum += p;
                 const double *vc = v + (c0 + c) * dv;
                 for (int64_t x = 0; x < dv; ++x)
@@ -258,7 +277,7 @@ int oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t L, int64_t d, int
                 double *ob = o + ((b * Hq + h) * L + r0) * dv;
                 for (int64_t r = 0; r < R; ++r)
                     for (int64_t x = 0; x < dv; ++x)
-                        ob[r * dv + x] = l[r] > 0.0 ? acc[r * dv + x] / l[r] : 0.0;
+                        ob[r * dv + x] = l[r] != 0.0 ? acc[r * dv + x] / l[r] : 0.0;
                 if (skip_map)
                     memcpy(skip_map + u * nkb, sk, nkb);
                 if (gap_map)
@@ -377,15 +396,15 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                 for (int64_t r = 0; r < G; ++r) {
                     double M = -INFINITY;
                     for (int64_t s = 0; s < num_splits; ++s)
-                        if (ls[s * G + r] > 0.0 && ms[s * G + r] > M)
+                        if (ls[s * G + r] != 0.0 && ms[s * G + r] > M) /* splits that saw keys (NaN l too) */
                             M = ms[s * G + r];
                     double den = 0.0;
                     double *orow = o + (b * Hq + g * G + r) * dv;
                     for (int64_t x = 0; x < dv; ++x)
                         orow[x] = 0.0;
                     for (int64_t s = 0; s < num_splits; ++s) {
-                        if (!(ls[s * G + r] > 0.0))
-                            continue;
+                        if (ls[s * G + r] == 0.0)
+                            continue; /* saw no key, or skipped every block */
                         double w = exp(ms[s * G + r] - M);
                         den += w * ls[s * G + r];
                         const double *ar = accs + (s * G + r) * dv;
@@ -393,7 +412,7 @@ int oracle_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t dqk,
                             orow[x] += w * ar[x];
                     }
                     for (int64_t x = 0; x < dv; ++x)
-                        orow[x] = den > 0.0 ? orow[x] / den : 0.0;
+                        orow[x] = den != 0.0 ? orow[x] / den : 0.0;
                 }
                 if (skip_map)
                     memcpy(skip_map + u * nkb, sk, nkb);

@@ -43,7 +43,8 @@ def check_decisions(gpu_skip, gpu_gap, ref_skip, ref_gap, lam, mask=None):
     assert np.array_equal(gs == 255, rs == 255), "visited pairs differ"
     vis = rs != 255
     band = np.zeros(rg.shape, bool)  # the exemption band, on visited pairs only (their gaps are never -inf)
-    band[vis] = np.abs(rg[vis] - lnlam(lam)) < GAP_BAND
+    with np.errstate(invalid="ignore"):  # -inf gaps of visited pairs (non-finite inputs) at lambda = 0
+        band[vis] = np.abs(rg[vis] - lnlam(lam)) < GAP_BAND
     bad = vis & ~band & (gs != rs)
     assert not bad.any(), f"{int(bad.sum())} decisions differ outside the band"
     # gaps: same infinities, finite values close

@@ -44,6 +44,18 @@ MUTANTS = [
     ("fit uses lambda only", "sum += log(lambda_at_L[i] * (double)L[i]);", "sum += log(lambda_at_L[i]);"),
     ("table interpolation linear in a", "lna = (1.0 - w) * log(a[i]) + w * log(a[i + 1]);",
      "lna = log((1.0 - w) * a[i] + w * a[i + 1]);"),
+    # the reading of non-finite inputs (R24)
+    ("masked keys left out of P.V", "if (!seen[c])\n                    continue; /* no row of the unit sees this key */",
+     "if (!seen[c] || S[r * bc + c] == -INFINITY)\n                    continue;"),
+    ("keys no row sees still enter", "if (!seen[c])\n                    continue; /* no row of the unit sees this key */",
+     "if (c0 + c >= klen)\n                    continue;"),
+    ("rows without a key skip the update", "double mp = m[r] > mt[r] ? m[r] : mt[r];\n            double alpha",
+     "double mp = m[r] > mt[r] ? m[r] : mt[r];\n            if (mp == -INFINITY) continue;\n            double alpha"),
+    ("NaN sum finalised as empty", "ob[r * dv + x] = l[r] != 0.0 ?", "ob[r * dv + x] = l[r] > 0.0 ?"),
+    ("merge drops NaN splits", "if (ls[s * G + r] == 0.0)\n                            continue;",
+     "if (!(ls[s * G + r] > 0.0))\n                            continue;"),
+    ("NaN score raises the block max", "if (s > mt[r]) /* a NaN score never raises the max */",
+     "if (!(s <= mt[r]))"),
 ]
 
 

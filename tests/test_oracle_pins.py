@@ -649,3 +649,175 @@ def test_sink_seed_fully_skipped_split_contributes_nothing():
     ex = np.repeat(sk == 0, bk)
     ref = masked_softmax_attention(S, ex[None], v[0, 0])[0]
     np.testing.assert_allclose(r["o"][0, 0], ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------- non-finite inputs (reading R24)
+# The pages say nothing about NaN or infinite inputs.  The reading both sides
+# implement: block maxima and the tile gap ignore NaN; in an executed block
+# every key that some row of the unit sees enters every row with weight
+# p (0 for a row that does not see it, and 0 * inf = 0 * NaN = NaN); keys no
+# row sees enter nothing; O = acc / l for l != 0, exactly 0 for l = 0; the
+# split merge keeps every split with l != 0.  Each pin below derives the
+# expected outcome from these rules and IEEE arithmetic by hand.
+
+def _finite_case(seed, L, d=8, dv=6, Hkv=1, Hq=1):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((1, Hq, L, d)), rng.standard_normal((1, Hkv, L, d)),
+            rng.standard_normal((1, Hkv, L, dv)))
+
+
+def test_nan_score_makes_exactly_the_rows_that_see_it_nan():
+    """K[5] = NaN: every row that sees key 5 has a NaN weight, hence a NaN sum and
+    a NaN output; rows 0..4 do not see it (causal) and stay plain softmax."""
+    L = 130
+    q, k, v = _finite_case(31, L)
+    k[0, 0, 5, :] = np.nan
+    r = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=64, block_k=64)
+    o = r["o"][0, 0]
+    assert np.isnan(o[5:]).all()
+    S = scores(q[0, 0], k[0, 0], 1 / math.sqrt(8))
+    ref = masked_softmax_attention(S[:5, :5], prefill_mask(5, True), v[0, 0, :5])
+    assert np.abs(o[:5] - ref).max() <= 1e-12
+
+
+def test_nonfinite_v_reaches_every_row_of_a_tile_that_executes_its_block():
+    """V[5, 0] = +inf, V[70, 1] = NaN, lambda = 0 (every visited block executes).
+    Tile 0 (rows 0..63): rows 0..4 do not see key 5 but it is seen by rows
+    5..63, so they add 0 * inf = NaN; rows 5..63 add p * inf = +inf.  Tile 1
+    (rows 64..127): all see key 5 (+inf); key 70 is seen by rows 70..127, so
+    rows 64..69 add 0 * NaN and everyone is NaN at feature 1.  Later tiles see
+    both keys.  Every other feature is plain causal softmax."""
+    L = 200
+    q, k, v = _finite_case(32, L)
+    v[0, 0, 5, 0] = np.inf
+    v[0, 0, 70, 1] = np.nan
+    o = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=64, block_k=64)["o"][0, 0]
+    assert np.isnan(o[:5, 0]).all() and np.isposinf(o[5:, 0]).all()
+    assert np.isfinite(o[:64, 1]).all() and np.isnan(o[64:, 1]).all()
+    S = scores(q[0, 0], k[0, 0], 1 / math.sqrt(8))
+    ref = masked_softmax_attention(S, prefill_mask(L, True), v[0, 0, :, 2:])
+    assert np.abs(o[:, 2:] - ref).max() <= 1e-12
+    fin = np.isfinite(v[0, 0, :, 1])
+    ref1 = masked_softmax_attention(S[:64, :64], prefill_mask(64, True), v[0, 0, :64, 1:2])
+    assert np.abs(o[:64, 1:2] - ref1).max() <= 1e-12 and fin[:64].all()
+
+
+def test_rows_that_have_seen_no_key_gather_zero_weighted_values():
+    """Window W = 1 (row i sees key i only), tile 128: in block 0 rows 64..127
+    see no key yet, but keys 0..63 are seen by rows 0..63, so those rows gather
+    0 * V; with V[3, 0] = NaN all 128 rows of tile 0 end NaN at feature 0
+    (a later rescale by 0 keeps the NaN).  Tile 1 visits blocks 2 and 3 only.
+    Every other value is V itself (W = 1)."""
+    L = 256
+    q, k, v = _finite_case(33, L)
+    v[0, 0, 3, 0] = np.nan
+    o = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=128, block_k=64, window=1)["o"][0, 0]
+    assert np.isnan(o[:128, 0]).all()
+    assert np.array_equal(o[128:, 0], v[0, 0, 128:, 0])
+    assert np.abs(o[:, 1:] - v[0, 0, :, 1:]).max() <= 1e-12
+
+
+def test_keys_no_row_of_the_tile_sees_contribute_nothing():
+    """Window W = 100, tile 128: tile 1 (rows 128..255) visits block 0 for keys
+    29..63, which row 128 sees; keys 0..28 are seen by no row of tile 1, so
+    V[10, 0] = +inf leaves tile 1 finite, while every row of tile 0 sees or
+    shares key 10 and is non-finite at feature 0."""
+    L = 256
+    q, k, v = _finite_case(34, L)
+    v[0, 0, 10, 0] = np.inf
+    o = oracle.prefill(q, k, v, causal=True, lam=0.0, tile_q=128, block_k=64, window=100)["o"][0, 0]
+    assert not np.isfinite(o[:110, 0]).any()     # rows 0..109 see key 10 or share its block with rows that do
+    assert np.isfinite(o[128:, 0]).all()
+    S = scores(q[0, 0], k[0, 0], 1 / math.sqrt(8))
+    # rows 128..255 see keys 29..255 only
+    ref = masked_softmax_attention(S[128:, 29:], prefill_mask(L, True, 100)[128:, 29:], v[0, 0, 29:])
+    assert np.abs(o[128:] - ref).max() <= 1e-12
+
+
+def test_nan_row_sum_propagates_through_the_split_merge():
+    """Decode, 2 splits of 128 keys: K[200] = NaN makes split 1's sum NaN for
+    both heads; the merge keeps splits with l != 0, so O is NaN everywhere.
+    Without the NaN, the two-split merge equals plain softmax."""
+    rng = np.random.default_rng(35)
+    q, k, v = rng.standard_normal((1, 2, 8)), rng.standard_normal((1, 1, 256, 8)), rng.standard_normal((1, 1, 256, 5))
+    lens = np.array([256])
+    base = oracle.decode(q, k, v, lens, lam=0.0, block_k=64, num_splits=2)["o"]
+    S = scores(q[0], k[0, 0], 1 / math.sqrt(8))
+    assert np.abs(base[0] - masked_softmax_attention(S, np.ones_like(S, bool), v[0, 0])).max() <= 1e-12
+    k[0, 0, 200, :] = np.nan
+    o = oracle.decode(q, k, v, lens, lam=0.0, block_k=64, num_splits=2)["o"]
+    assert np.isnan(o).all()
+
+
+def _nan_aware_decisions(S, mask, blocks, lam):
+    """Decisions by the closed form with the R24 rules: per-row block maxima
+    ignore NaN, the running max is their prefix maximum, a NaN row gap never
+    blocks a skip."""
+    lnlam = -math.inf if lam == 0 else math.log(lam)
+    R = S.shape[0]
+    prev = np.full(R, -np.inf)
+    skips = []
+    for c0, c1 in blocks:
+        mb = mask[:, c0:c1]
+        if not mb.any():
+            skips.append(255)
+            continue
+        vals = np.where(mb, S[:, c0:c1], -np.inf)
+        mt = np.array([max([x for x in row if not np.isnan(x)], default=-np.inf) for row in vals])
+        with np.errstate(invalid="ignore"):
+            d = np.where(mt == -np.inf, -np.inf, np.where(prev == -np.inf, np.inf, mt - prev))
+        d = d[~np.isnan(d)]
+        g = d.max() if d.size else -np.inf
+        skips.append(1 if g < lnlam else 0)
+        prev = np.fmax(prev, mt)
+    return skips
+
+
+def test_infinite_query_row_gives_nan_output_and_never_blocks_a_skip():
+    """Q[10] = (+inf, 0, ..., 0): row 10's scores are +inf or -inf by the sign
+    of k[:, 0]; its running max becomes +inf at its first block, after which its
+    gaps are NaN or -inf and never keep the tile from skipping.  Its output is
+    NaN (weight exp(inf - inf)); decisions equal the closed form."""
+    L, tq = 320, 64
+    q, k, v = _prefill_case(36, B=1, Hq=1, Hkv=1, L=L, d=8, dv=6, qstd=2.5, blocky=64)
+    q[0, 0, 10, :] = 0.0
+    q[0, 0, 10, 0] = np.inf
+    r0 = oracle.prefill(q, k, v, causal=False, lam=0.0, tile_q=tq, block_k=64)
+    lam = _lam_at(r0["gap"][np.isfinite(r0["gap"])], 0.5)
+    r = oracle.prefill(q, k, v, causal=False, lam=lam, tile_q=tq, block_k=64)
+    assert r["skipped"] > 0
+    assert np.isnan(r["o"][0, 0, 10]).all()
+    assert np.isfinite(np.delete(r["o"][0, 0], 10, axis=0)).all()
+    with np.errstate(invalid="ignore"):
+        S = 0.0 + np.einsum("id,cd->ic", q[0, 0], k[0, 0]) / math.sqrt(8)
+    mask = np.ones((L, L), bool)
+    for t in range(L // tq):
+        rows = slice(t * tq, (t + 1) * tq)
+        want = _nan_aware_decisions(S[rows], mask[rows], [(c, c + 64) for c in range(0, L, 64)], lam)
+        assert list(r["skip"][0, 0, t]) == want, t
+
+
+def test_nan_scores_are_ignored_by_the_block_max():
+    """A NaN key (K[191] = NaN, the last key of block 2) gives NaN scores in
+    block 2 for every row; the block max and the running max ignore them, so
+    the decisions are those of the closed form over the finite scores
+    (non-causal, lambda at the median gap), and every row of a tile that
+    executes block 2 is NaN."""
+    L, tq = 320, 64
+    q, k, v = _prefill_case(37, B=1, Hq=1, Hkv=1, L=L, d=8, dv=6, qstd=2.5, blocky=64)
+    r0 = oracle.prefill(q, k, v, causal=False, lam=0.0, tile_q=tq, block_k=64)
+    lam = _lam_at(r0["gap"][np.isfinite(r0["gap"])], 0.5)
+    k[0, 0, 191, :] = np.nan
+    r = oracle.prefill(q, k, v, causal=False, lam=lam, tile_q=tq, block_k=64)
+    with np.errstate(invalid="ignore"):
+        S = np.einsum("id,cd->ic", q[0, 0], k[0, 0]) / math.sqrt(8)
+    mask = np.ones((L, L), bool)
+    nskip = 0
+    for t in range(L // tq):
+        rows = slice(t * tq, (t + 1) * tq)
+        want = _nan_aware_decisions(S[rows], mask[rows], [(c, c + 64) for c in range(0, L, 64)], lam)
+        assert list(r["skip"][0, 0, t]) == want, t
+        nskip += sum(x == 1 for x in want)
+        if want[2] == 0:
+            assert np.isnan(r["o"][0, 0, rows]).all()
+    assert nskip > 0
