@@ -75,7 +75,11 @@ extern "C" {
 
 const char *blasst_status_str(blasst_status s)
 {
-    switch (s) {
+    // A C caller may pass any int; reading it as an enum of this C++ file
+    // would be undefined outside the enumerators, so its bytes are read.
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case BLASST_OK: return "ok";
     case BLASST_ERR_INVALID_ARG: return "invalid argument";
     case BLASST_ERR_UNSUPPORTED: return "unsupported configuration";
