@@ -8,7 +8,8 @@ lambda that the library's own calibration search gives for 70% block
 sparsity on that input.  ``value`` is the dense-equivalent throughput
 4*B*Hq*L^2*d/2 / time, in TFLOP/s.  The same run also measures
   * the same prefill at the 50% lambda and with lambda = 0 (the dense kernel),
-    for speedups over the library's own dense path;
+    for speedups over the library's own dense path, and the gap pass that
+    calibration runs (scores, block maxima and decisions only);
   * the GQA decode workload (148 sequences, Hq=32, Hkv=8, 32768 cached tokens,
     d=128, bf16 cache, block 64) at the 70% and 50% lambdas and lambda = 0:
     microseconds per decode step and HBM GB/s on the bytes actually loaded;
@@ -20,11 +21,13 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
     at the 70% lambda and lambda = 0: microseconds per step, GB/s on the
     loaded bytes and MFMA utilisation (the workload sits near the ridge);
   * the long causal prefill (B=2, Hq=32, Hkv=8, L=32768, d=128) over the
-    target sparsities 30/50/70/80% and dense, and with a 4096-key sliding
-    window at 70% and dense;
+    target sparsities 30/50/70/80% and dense (with its own MFMA roofline at
+    70%), and with a 4096-key sliding window at 70% and dense;
   * the calibration law lambda = a/L: a fitted on calibration inputs at
-    L = 4K..32K, then the sparsity lambda = a/L achieves on fresh inputs;
+    L = 4K..128K (a table that records its tiling), then the sparsity
+    lambda = a/L achieves on fresh inputs;
   * the fp64 CPU oracle on a bounded sample of the prefill workload.
+Every timed call passes a counters buffer (each call returns its skip counts).
 Inputs are seeded synthetic segment-center tensors generated on the device.
 Prints ONE JSON line.  ``--only NAME`` runs one measurement (for profilers).
 """
@@ -52,10 +55,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps, warmup, min_warm_ms=100.0):
+MIN_WARM_MS = 100.0  # --min-warm-ms
+
+
+def time_calls(fn, steps, warmup, min_warm_ms=None):
     """ms per call: at least ``warmup`` untimed calls and at least ``min_warm_ms`` of
     untimed work (the clocks settle), then ``steps`` calls enqueued back to back between
     two events on the launch stream, bracketed by device synchronisation."""
+    min_warm_ms = MIN_WARM_MS if min_warm_ms is None else min_warm_ms
     t0 = time.perf_counter()
     n = 0
     while n < warmup or (time.perf_counter() - t0) * 1e3 < min_warm_ms:
@@ -328,24 +335,30 @@ def measured_peaks(reps=20):
 LAM_TINY = 1e-300
 
 
-def bench_prefill(steps, warmup, names=("s70", "s50", "dense", "skip0")):
+def bench_prefill(steps, warmup, names=("s70", "s50", "dense", "skip0", "gaps")):
     (B, Hq, Hkv, L, d), (q, k, v) = prefill_workload()
     cal = calibrate_prefill(q, k, v, [0.5, 0.7])
     lam70, reach70 = cal[0.7]
     lam50, reach50 = cal[0.5]
     log(f"prefill lambda70={lam70:.4g} (gap-map sparsity {reach70:.4f}) lambda50={lam50:.4g} ({reach50:.4f})")
     out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
+    gap = torch.empty(B, Hq, L // 128, L // 64, dtype=torch.float32, device="cuda")
+    run_cnt = torch.zeros(2, dtype=torch.int64, device="cuda")  # every timed call returns its skip counts
 
     def pf(lam, cnt=None):
         return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
 
+    def gp(lam, cnt=None):  # the gap pass (calibration): maps and counters only, no O
+        return lambda: bl.blasst_prefill_gaps(q, k, v, causal=True, lam=lam, tile_q=128, gap_map=gap, counters=cnt)
+
     dense_flops = 4.0 * B * Hq * L * L * d / 2
-    lams = {"s70": lam70, "s50": lam50, "dense": 0.0, "skip0": LAM_TINY}
+    lams = {"s70": lam70, "s50": lam50, "dense": 0.0, "skip0": LAM_TINY, "gaps": lam70}
     res = {}
     for name in names:
         lam = lams[name]
-        mean_ms, _, _ = time_calls(pf(lam), steps, warmup)
-        vis, skp = counts(lambda c: pf(lam, c)())
+        call = gp if name == "gaps" else pf
+        mean_ms, _, _ = time_calls(call(lam, run_cnt), steps, warmup)
+        vis, skp = counts(lambda c: call(lam, c)())
         res[name] = {"lambda": lam, "ms": mean_ms, "visited": vis, "skipped": skp,
                      "sparsity": skp / vis if vis else 0.0,
                      "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12}
@@ -354,28 +367,35 @@ def bench_prefill(steps, warmup, names=("s70", "s50", "dense", "skip0")):
     return (q, k, v, lam70), res, dense_flops
 
 
-def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), window=0, seed=False,
-                 oracle_cpu=False):
+def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0", "gaps"), paged_names=(), window=0,
+                 seed=False, oracle_cpu=False):
     (DB, DHq, DHkv, DL, Dd), (dq, kc, vc, lens) = decode_workload()
     S, ws = bl.blasst_decode_plan(dq, kc, vc, lens, lam=1e-3)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
     dout = torch.empty(DB, DHq, Dd, dtype=torch.bfloat16, device="cuda")
+    dgap = torch.empty(DB, DHkv, DL // 64, dtype=torch.float32, device="cuda")
+    run_cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
     dcal = calibrate_decode(dq, kc, vc, lens, S, [0.5, 0.7])
 
-    def dc(lam, cnt=None):
+    def dc(lam, cnt=None, gaps=False):
+        if gaps:
+            return lambda: bl.blasst_decode_gaps(dq, kc, vc, lens, lam=lam, num_splits=S, gap_map=dgap, counters=cnt)
         return lambda: bl.blasst_decode(dq, kc, vc, lens, lam=lam, num_splits=S, out=dout,
                                         workspace=work, counters=cnt)
 
-    lams = {"s70": dcal[0.7][0], "s50": dcal[0.5][0], "dense": 0.0, "skip0": LAM_TINY}
+    lams = {"s70": dcal[0.7][0], "s50": dcal[0.5][0], "dense": 0.0, "skip0": LAM_TINY, "gaps": dcal[0.7][0]}
     dres = {}
     for name in names:
         lam = lams[name]
-        mean_ms, _, _ = time_calls(dc(lam), steps, warmup)
-        vis, skp = counts(lambda c: dc(lam, c)())
+        mean_ms, _, _ = time_calls(dc(lam, run_cnt, name == "gaps"), steps, warmup)
+        vis, skp = counts(lambda c: dc(lam, c, name == "gaps")())
         blk = 64 * Dd * 2
-        loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
-        if S > 1:
-            loaded += 2 * DB * DHq * S * (Dd + 2) * 4
+        if name == "gaps":  # K of every visited block; no V, no partials, no O
+            loaded = vis * blk + dq.numel() * 2
+        else:
+            loaded = vis * blk + (vis - skp) * blk + dq.numel() * 2 + dout.numel() * 2
+            if S > 1:
+                loaded += 2 * DB * DHq * S * (Dd + 2) * 4
         dres[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "bytes": loaded,
                       "gbps": loaded / (mean_ms * 1e-3) / 1e9}
         log(f"decode {name}: {mean_ms * 1e3:.1f} us, sparsity {skp / vis:.4f}, "
@@ -424,28 +444,35 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_na
     return S, dres
 
 
-def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0"), paged_names=(), seed=False, oracle_cpu=False):
+def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0", "gaps"), paged_names=(), seed=False,
+              oracle_cpu=False):
     (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
     S, ws = bl.blasst_decode_plan(q, kc, kc, lens, lam=1e-3, dv=dv)
     work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty(B, Hq, dv, dtype=torch.bfloat16, device="cuda")
+    mgap = torch.empty(B, 1, L // 64, dtype=torch.float32, device="cuda")
+    run_cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
     cal = calibrate_decode(q, kc, kc, lens, S, [0.5, 0.7], dv=dv)
 
-    def dc(lam, cnt=None):
+    def dc(lam, cnt=None, gaps=False):
+        if gaps:
+            return lambda: bl.blasst_decode_gaps(q, kc, kc, lens, lam=lam, num_splits=S, dv=dv, gap_map=mgap,
+                                                 counters=cnt)
         return lambda: bl.blasst_decode(q, kc, kc, lens, lam=lam, num_splits=S, out=out, dv=dv,
                                         workspace=work, counters=cnt)
 
-    lams = {"s70": cal[0.7][0], "s50": cal[0.5][0], "dense": 0.0, "skip0": LAM_TINY}
+    lams = {"s70": cal[0.7][0], "s50": cal[0.5][0], "dense": 0.0, "skip0": LAM_TINY, "gaps": cal[0.7][0]}
     res = {}
     for name in names:
         lam = lams[name]
-        mean_ms, _, _ = time_calls(dc(lam), steps, warmup)
-        vis, skp = counts(lambda c: dc(lam, c)())
+        gaps = name == "gaps"
+        mean_ms, _, _ = time_calls(dc(lam, run_cnt, gaps), steps, warmup)
+        vis, skp = counts(lambda c: dc(lam, c, gaps)())
         # V aliases the K tile: a visited block loads its 64 x 576 latent rows once
-        loaded = vis * 64 * dqk * 2 + q.numel() * 2 + out.numel() * 2
-        if S > 1:
+        loaded = vis * 64 * dqk * 2 + q.numel() * 2 + (0 if gaps else out.numel() * 2)
+        if S > 1 and not gaps:
             loaded += 2 * B * Hq * S * (dv + 2) * 4
-        flops = vis * 2.0 * Hq * 64 * dqk + (vis - skp) * 2.0 * Hq * 64 * dv
+        flops = vis * 2.0 * Hq * 64 * dqk + (0 if gaps else (vis - skp) * 2.0 * Hq * 64 * dv)
         sec = mean_ms * 1e-3
         res[name] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis, "bytes": loaded,
                      "gbps": loaded / sec / 1e9, "tflops": flops / sec / 1e12}
@@ -482,13 +509,16 @@ def bench_long_prefill(steps, warmup, targets=(0.3, 0.5, 0.7, 0.8), oracle_cpu=F
     def pf(lam, cnt=None):
         return lambda: bl.blasst_prefill(q, k, v, causal=True, lam=lam, tile_q=128, out=out, counters=cnt)
 
+    run_cnt = torch.zeros(2, dtype=torch.int64, device="cuda")
     rows = []
     for t in list(targets) + [None]:
         lam = 0.0 if t is None else cal[t][0]
-        mean_ms, _, _ = time_calls(pf(lam), steps, warmup)
+        mean_ms, _, _ = time_calls(pf(lam, run_cnt), steps, warmup)
         vis, skp = counts(lambda c: pf(lam, c)())
+        mfma = (2 * vis - skp) * 2.0 * 128 * 64 * d  # QK of every visited pair, PV of the executed ones
         rows.append({"target": t, "lambda": lam, "ms": mean_ms, "sparsity": skp / vis,
-                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12})
+                     "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12,
+                     "mfma_flops": mfma, "mfma_util_executed": mfma / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
         log(f"long prefill target {t}: {mean_ms:.3f} ms, sparsity {skp / vis:.4f}")
     dense_ms = rows[-1]["ms"]
     for r in rows:
@@ -619,13 +649,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode and long-prefill sections")
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
-    ap.add_argument("--only", choices=["prefill70", "prefill_dense", "decode70", "decode_dense", "mla70",
-                                       "mla_dense", "decode_paged70", "mla_paged70", "long_prefill70",
-                                       "long_prefill_dense", "prefill_lengths"],
+    ap.add_argument("--only", choices=["prefill70", "prefill_dense", "prefill_gaps", "decode70", "decode_dense",
+                                       "decode_gaps", "mla70", "mla_dense", "mla_gaps", "decode_paged70",
+                                       "mla_paged70", "long_prefill70", "long_prefill_dense", "prefill_lengths"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--min-warm-ms", type=float, default=100.0,
+                    help="least untimed work before each timed run (profiling runs pass 0 so that the trace "
+                         "averages cover mostly timed calls)")
     args = ap.parse_args()
+    global MIN_WARM_MS
+    MIN_WARM_MS = args.min_warm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the method has no multi-GPU path here; run with --gpus 1",
               file=sys.stderr)
@@ -656,7 +691,8 @@ def main():
         print(json.dumps({"only": args.only, "result": r}, default=str), flush=True)
         return
     if args.only:
-        which, name = args.only.split("70")[0].split("_dense")[0], ("dense" if "dense" in args.only else "s70")
+        which = args.only.split("70")[0].split("_dense")[0].split("_gaps")[0]
+        name = "dense" if "dense" in args.only else ("gaps" if "gaps" in args.only else "s70")
         fn = {"prefill": bench_prefill, "decode": bench_decode, "mla": bench_mla}[which]
         r = fn(steps, warmup, names=(name,))
         print(json.dumps({"only": args.only, "result": r[1] if which == "prefill" else r}, default=str), flush=True)
@@ -666,9 +702,11 @@ def main():
     (q, k, v, lam70), res, dense_flops = bench_prefill(steps, warmup)
     B, Hq, L, d = q.shape
     bc, br = 64, 128
+    tile_flops = 2.0 * br * bc * d  # one (query tile, key block) product, QK or PV
     exec70 = res["s70"]["visited"] - res["s70"]["skipped"]
-    mfma_flops70 = res["s70"]["visited"] * 2.0 * br * bc * d + exec70 * 2.0 * br * bc * d
+    mfma_flops70 = res["s70"]["visited"] * tile_flops + exec70 * tile_flops
     achieved = mfma_flops70 / (res["s70"]["ms"] * 1e-3) / 1e12
+    mfma_flops_dense = 2 * res["dense"]["visited"] * tile_flops  # executed work of the dense kernel
     prefill = {
         "lambda70": lam70, "sparsity70": res["s70"]["sparsity"], "ms70": res["s70"]["ms"],
         "lambda50": res["s50"]["lambda"], "sparsity50": res["s50"]["sparsity"], "ms50": res["s50"]["ms"],
@@ -677,9 +715,12 @@ def main():
         "speedup70_vs_dense": res["dense"]["ms"] / res["s70"]["ms"],
         "speedup50_vs_dense": res["dense"]["ms"] / res["s50"]["ms"],
         "mfma_util_executed70": achieved / PEAK_BF16_TFLOPS,
-        "mfma_util_dense": dense_flops / (res["dense"]["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mfma_util_dense": mfma_flops_dense / (res["dense"]["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "ms_skip_logic_nothing_skipped": res["skip0"]["ms"],
         "skip_logic_overhead_vs_dense": res["skip0"]["ms"] / res["dense"]["ms"] - 1.0,
+        "gap_pass": {"ms": res["gaps"]["ms"], "vs_dense": res["gaps"]["ms"] / res["dense"]["ms"],
+                     "note": "calibration pass: scores, block maxima, running max and decisions; no exp, V or P.V"},
+        "timed_calls_return_counts": True,
     }
 
     # ------------------------------------------------------------- decode
@@ -712,6 +753,8 @@ def main():
                        "speedup70_vs_dense": dres["window_dense"]["us"] / dres["window_s70"]["us"],
                        "hbm_gbps70": dres["window_s70"]["gbps"], "hbm_gbps_dense": dres["window_dense"]["gbps"]},
             "sink_seed": dres["sink_seed"],
+            "gap_pass": {"us": dres["gaps"]["us"], "vs_dense": dres["gaps"]["us"] / dres["dense"]["us"],
+                         "hbm_gbps": dres["gaps"]["gbps"]},
             "cpu_oracle": dres.get("cpu_oracle"),
         }
         torch.cuda.empty_cache()
@@ -738,12 +781,20 @@ def main():
                       "overhead70_vs_contiguous": mres["paged_s70"]["us"] / m70["us"] - 1.0,
                       "overhead_dense_vs_contiguous": mres["paged_dense"]["us"] / mres["dense"]["us"] - 1.0},
             "sink_seed": mres["sink_seed"],
+            "gap_pass": {"us": mres["gaps"]["us"], "vs_dense": mres["gaps"]["us"] / mres["dense"]["us"],
+                         "hbm_gbps": mres["gaps"]["gbps"]},
             "cpu_oracle": mres.get("cpu_oracle"),
         }
         torch.cuda.empty_cache()
         sweep, wres, lcpu = bench_long_prefill(max(2, steps // 4), max(1, warmup // 2), oracle_cpu=oc)
+        r70 = next((r for r in sweep if r["target"] == 0.7), None)
         long_prefill = {
             "workload": "GQA causal prefill B=2 Hq=32 Hkv=8 L=32768 d=128 bf16, query tile 128, key block 64",
+            "roofline": None if r70 is None else {
+                "bound": "mfma", "achieved": r70["mfma_flops"] / (r70["ms"] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": r70["mfma_util_executed"], "traffic": measured_traffic("long_prefill70"),
+                "algorithmic_flops": r70["mfma_flops"]},
+            "speedup70_vs_dense": None if r70 is None else r70["speedup_vs_dense"],
             "sweep": sweep,
             "window": wres,
             "cpu_oracle": lcpu,
