@@ -153,7 +153,9 @@ blasst_status blasst_prefill_gaps(const blasst_prefill_params *p, void *hip_stre
  *   seq_lens: device int32 [B], each in 1..Lmax (the kernel clamps other
  *             values into 0..Lmax; a length of 0 yields O = 0).
  *   Supported: (dqk = dv in {64, 128}, G in 1..16) and the latent form
- *   (dqk = 576, dv = 512, Hkv = 1, G = 128, v aliasing k).  block_k = 64.
+ *   (dqk = 576, dv = 512, Hkv = 1, G in 1..128 -- all heads of a model, or
+ *   a shard of them when heads are split across GPUs -- v aliasing k).
+ *   block_k = 64.
  *   num_splits: 0 lets the library choose; otherwise 1..nKB.
  *   skip_map / gap_map: optional device [B, Hkv, nKB], nKB = ceil(Lmax/64).
  *   B = 0 is a valid no-op: only the scalar arguments are checked, the

@@ -548,7 +548,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool o
                             : launch_gqa<64, false, false>(a, stream, gaps);
         }
     }
-    if (dqk == 576 && dv == 512 && a.G == 128)
+    if (dqk == 576 && dv == 512 && a.G >= 1 && a.G <= 128)
         return launch_mla(a, skip, out_bf16, stream, gaps);
     return hipErrorInvalidValue;
 }

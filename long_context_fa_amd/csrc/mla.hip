@@ -1,18 +1,24 @@
 // mla.hip -- latent (MLA, absorbed form) decode with BLASST block skipping,
-// gfx950: 128 query heads share one latent KV head of width 576 (512 latent
-// + 64 rotary); the value of a token is the first 512 columns of its latent
-// row, so V costs no bytes of its own.
+// gfx950: up to 128 query heads share one latent KV head of width 576 (512
+// latent + 64 rotary); the value of a token is the first 512 columns of its
+// latent row, so V costs no bytes of its own.
 //
 // Method: "BLASST: Dynamic BLocked Attention Sparsity via Softmax
 // Thresholding" (gist.science/pt/paper/2512.12087, section 2; section 3 lists
 // MHA/GQA/MQA/MLA support).  A query tile is the group of heads sharing the KV
-// head -- here all 128 -- and a key block is skipped when every head meets
-// m~ - m < ln(lambda).  With V aliasing the latent K, a skipped block saves the
+// head -- here all G <= 128 -- and a key block is skipped when every head
+// meets m~ - m < ln(lambda).  With V aliasing the latent K, a skipped block saves the
 // exponentials and the P.V product (about half the matrix work), not bytes.
 //
 // One workgroup (4 waves x 32 heads, one wave per SIMD so that each wave can
 // hold the 576-wide Q^T operand in VGPRs and its 512x32 O^T accumulator in
-// AGPRs) walks the key blocks of one (sequence, split):
+// AGPRs) walks the key blocks of one (sequence, split).  With G < 128 heads
+// (e.g. 16 or 32 per GPU when the heads are sharded across GPUs) lane slot
+// 32 w + n >= G computes head (32 w + n) mod G again: a repeated head leaves
+// every vote (an AND over heads), block maximum and gap (maxima over heads)
+// unchanged, so the loop needs no per-lane head test; only the writes of O or
+// of the partials are limited to slots < G.  A wave on its own SIMD costs the
+// others nothing:
 //  * the 64 x 576 bf16 K tile (72 KB) is copied global -> LDS with
 //    global_load_lds_dwordx4 into a double buffer, issued between the score
 //    MFMAs of the previous block, with the non-temporal hint (a step reads
@@ -62,6 +68,21 @@ constexpr int NDT = DV / 32;         // O^T d tiles (16)
 __host__ __device__ constexpr int swzl(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __host__ __device__ constexpr int swzr(int r) { return (r >> 1) & 7; }
 
+// Sum of the 8 bf16 values of a P operand, in fp32.  The row sum adds the
+// probabilities as the P.V product sees them (rounded to bf16), so that O is
+// a weighted mean of V rows with one set of weights: with the latent rows'
+// large values, an fp32 sum beside bf16 products leaves an error of up to
+// 2^-9 of |V| when one key dominates.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 x)
+{
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s += __builtin_bit_cast(float, u[i] << 16) + __builtin_bit_cast(float, u[i] & 0xffff0000u);
+    return s;
+}
+
 template <bool SKIP, bool OUT_BF16, bool PAGED, bool GAPS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mla_kernel(const DecodeArgs a)
@@ -110,7 +131,8 @@ void decode_mla_kernel(const DecodeArgs a)
     // Q^T as the B operand: lane (n, hh) holds q[head][16kk + 8hh .. +7].
     bf16x8 qf[NKK];
     {
-        const uint16_t *qp = a.q + b * a.q_sb + (int64_t)head * a.q_sh;
+        // heads past G repeat head (32 w + n) mod G
+        const uint16_t *qp = a.q + b * a.q_sb + (int64_t)(head % a.G) * a.q_sh;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
             qf[kk] = as_bf16x8(*(const u32x4 *)(qp + 16 * kk + 8 * hh));
@@ -304,12 +326,12 @@ void decode_mla_kernel(const DecodeArgs a)
             auto pexp = [&](int u, int r) {
                 const float p = exp2_hw(__builtin_fmaf(sc[u >> 1][8 * (u & 1) + r], a.scale_log2, -msafe));
                 pv8[r] = p;
-                rs += p;
             };
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 pexp(0, r);
             bf16x8 pf = cvt_bf16x8(pv8);
+            rs += sum_bf16x8(pf);
             // O^T += V^T P^T, V = first 512 columns of the K tile.
             auto vread = [&](int m) {
                 const int u = m / NDT, dt = m % NDT;
@@ -337,8 +359,10 @@ void decode_mla_kernel(const DecodeArgs a)
                 if (u + 1 < 4) {
                     if (dt < 8)
                         pexp(u + 1, dt);
-                    else if (dt == 8)
+                    else if (dt == 8) {
                         pnext = cvt_bf16x8(pv8);
+                        rs += sum_bf16x8(pnext);
+                    }
                 }
             }
             mfma_drain();
@@ -356,7 +380,10 @@ void decode_mla_kernel(const DecodeArgs a)
     const float l = lsum + __shfl_xor(lsum, 32);
     if (GAPS) {
         // no output
+    } else if (32 * w >= a.G) {
+        // no heads, no output
     } else if (S == 1) {
+        const bool head_ok = head < a.G;
         const float inv = 1.f / l; // exactly 0 below when l = 0 (no key seen); NaN l gives NaN
         const bool none = l == 0.f;
         char *ob = (char *)a.o;
@@ -370,6 +397,8 @@ void decode_mla_kernel(const DecodeArgs a)
                 f32x4 v4 = {od[4 * g] * inv, od[4 * g + 1] * inv, od[4 * g + 2] * inv, od[4 * g + 3] * inv};
                 if (none)
                     v4 = f32x4{};
+                if (!head_ok)
+                    continue;
                 if (OUT_BF16)
                     *(bf16x4 *)(ob + 2 * (base + d)) = __builtin_convertvector(v4, bf16x4);
                 else
@@ -377,17 +406,20 @@ void decode_mla_kernel(const DecodeArgs a)
             }
         }
     } else {
-        const int64_t pu = ((int64_t)b * S + s) * 128 + head; // Hkv = 1, G = 128
+        const bool head_ok = head < a.G;
+        const int64_t pu = ((int64_t)b * S + s) * a.G + head; // Hkv = 1
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const f32x16 od = acc_read(16 * dt);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = 32 * dt + 8 * g + 4 * hh;
-                *(f32x4 *)(a.part_o + pu * DV + d) = f32x4{od[4 * g], od[4 * g + 1], od[4 * g + 2], od[4 * g + 3]};
+                if (head_ok)
+                    *(f32x4 *)(a.part_o + pu * DV + d) =
+                        f32x4{od[4 * g], od[4 * g + 1], od[4 * g + 2], od[4 * g + 3]};
             }
         }
-        if (hh == 0) {
+        if (hh == 0 && head_ok) {
             a.part_ml[2 * pu] = m2;
             a.part_ml[2 * pu + 1] = l;
         }
@@ -436,7 +468,7 @@ void launch_mla_variant(const DecodeArgs &a, dim3 grid, hipStream_t stream)
 
 hipError_t launch_mla(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream, bool gaps)
 {
-    if (a.G != 128 || a.Hkv != 1)
+    if (a.G < 1 || a.G > 128 || a.Hkv != 1)
         return hipErrorInvalidValue;
     const dim3 grid(a.num_splits, 1, a.B);
     if (gaps) {

@@ -164,6 +164,17 @@ def test_decode_rejects():
                        seq_lens=torch.full((1,), 256, dtype=torch.int32)) == 2
     # more splits than one: workspace too small
     assert _decode_err(num_splits=4, workspace=torch.zeros(16, dtype=torch.uint8)) == 3
+    # the latent form takes 1..128 heads sharing the latent head
+    q = _bf16(1, 129, 576)
+    assert _decode_err(q=q, k_cache=kc, v_cache=kc, dv=512, seq_lens=torch.full((1,), 256, dtype=torch.int32)) == 2
+
+
+def test_latent_plan_accepts_head_shards():
+    kc = _bf16(1, 1, 4096, 576).expand(16, 1, 4096, 576)  # plan reads no memory; shapes only
+    lens = torch.full((16,), 4096, dtype=torch.int32)
+    for hq in (1, 16, 40, 64, 128):
+        S, ws = bl.blasst_decode_plan(_bf16(16, hq, 576), kc, kc, lens, lam=0.01, dv=512)
+        assert S >= 1 and ws == (16 * hq * S * (512 + 2) * 4 + 256 if S > 1 else 0)
 
 
 def test_decode_plan_host_only():

@@ -171,6 +171,22 @@ def test_mla_bf16_output_and_determinism():
     assert o4.dtype == torch.bfloat16 and torch.isfinite(o4.float()).all()
 
 
+@pytest.mark.parametrize("G,splits", [(16, 1), (16, 4), (40, 3), (64, 2), (127, 1)])
+def test_parity_mla_head_shards(G, splits):
+    """The latent form with fewer than 128 heads (a shard of a model's heads):
+    waves or lanes past G hold no query and must neither vote nor write."""
+    q, kc, _, lens = inputs.decode_inputs(3, G, 1, 2000, 576, 512, n_random=16, mla=True, device=DEV,
+                                          seed=140 + G + splits, seq_lens=[2000, 1, 777])
+    _, _, gap0, _ = gpu_decode(q, kc, kc, lens, lam=0.0, num_splits=splits, dv=512)
+    lam, _ = lambda_for(gap0, 0.6)
+    _run(q, kc, kc, lens, lam=lam, splits=splits, dv=512, mla=True, what=f"mla G={G}")
+    # paged: the same call over a shuffled 64-row pool is bit-equal
+    (kp,), table = inputs.paged_pool([kc], lens, 64, seed=5)
+    got = gpu_decode_paged(q, kp, kp, table, lens, kc.shape[2], lam=lam, num_splits=splits, dv=512)
+    ref = gpu_decode(q, kc, kc, lens, lam=lam, num_splits=splits, dv=512)
+    _equal_calls(got, ref)
+
+
 def test_parity_mla_decode_full_size_sampled():
     """The 16-sequence, 64K-token latent decode step at ~70% sparsity, in the
     split configuration the planner picks; the oracle checks two whole
