@@ -444,6 +444,64 @@ def bench_decode(steps, warmup, names=("s70", "s50", "dense", "skip0", "gaps"), 
     return S, dres
 
 
+def bench_paged_layouts(steps, warmup, rounds=4):
+    """Where the paged GQA decode's extra time goes, at the 70% lambda: the
+    contiguous cache against three page pools holding the same rows, timed in
+    alternating rounds (median per layout):
+      shuffled  64-row pages [pages, Hkv, 64, d] in seeded random order (the bench's paged leg);
+      in_order  the same pool layout with the pages in sequence order;
+      whole     the contiguous cache itself passed as one page per sequence (page = Lmax rows):
+                the addresses of the contiguous call, through the paged kernel's code.
+    whole - contiguous is the cost of the paged code path; in_order - whole that of the pool's
+    address pattern (16 KB per head and block, 128 KB apart); shuffled - in_order that of the
+    random page order."""
+    (B, Hq, Hkv, L, d), (q, kc, vc, lens) = decode_workload()
+    S, ws = bl.blasst_decode_plan(q, kc, vc, lens, lam=1e-3)
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lam = calibrate_decode(q, kc, vc, lens, S, [0.7])[0.7][0]
+    (kp, vp), table = inputs.paged_pool([kc, vc], lens, 64, seed=9)
+    npb = L // 64
+
+    def in_order(c):  # page b * npb + i holds rows 64 i .. 64 i + 63 of sequence b
+        return c.view(B, Hkv, npb, 64, d).permute(0, 2, 1, 3, 4).reshape(B * npb, Hkv, 64, d)
+
+    ko, vo = in_order(kc), in_order(vc)
+    t_in = (torch.arange(B, device="cuda", dtype=torch.int32)[:, None] * npb
+            + torch.arange(npb, device="cuda", dtype=torch.int32)[None, :]).contiguous()
+    t_whole = torch.arange(B, device="cuda", dtype=torch.int32)[:, None].contiguous()
+    calls = {
+        "contiguous": lambda: bl.blasst_decode(q, kc, vc, lens, lam=lam, num_splits=S, out=out, workspace=work),
+        "whole": lambda: bl.blasst_decode_paged(q, kc, vc, t_whole, lens, L, lam=lam, num_splits=S, out=out,
+                                                workspace=work),
+        "in_order": lambda: bl.blasst_decode_paged(q, ko, vo, t_in, lens, L, lam=lam, num_splits=S, out=out,
+                                                   workspace=work),
+        "shuffled": lambda: bl.blasst_decode_paged(q, kp, vp, table, lens, L, lam=lam, num_splits=S, out=out,
+                                                   workspace=work),
+    }
+    ref = None
+    for name, fn in calls.items():  # every layout gives the contiguous call's O, bit for bit
+        fn()
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = out.clone()
+        elif not torch.equal(out, ref):
+            raise RuntimeError(f"paged layout {name} differs from the contiguous call")
+    times = {name: [] for name in calls}
+    for _ in range(rounds):
+        for name, fn in calls.items():
+            times[name].append(time_calls(fn, steps, warmup, min_warm_ms=20.0)[0] * 1e3)
+    med = {name: float(np.median(v)) for name, v in times.items()}
+    c = med["contiguous"]
+    res = {"num_splits": S, "lambda70": lam, "us": med, "rounds": rounds,
+           "overhead_vs_contiguous": {k: v / c - 1.0 for k, v in med.items() if k != "contiguous"},
+           "split": {"paged_code": med["whole"] / c - 1.0, "pool_address_pattern": (med["in_order"] - med["whole"]) / c,
+                     "random_page_order": (med["shuffled"] - med["in_order"]) / c}}
+    for name in calls:
+        log(f"decode 70% {name}: {med[name]:.1f} us ({med[name] / c - 1.0:+.2%})")
+    return res
+
+
 def bench_mla(steps, warmup, names=("s70", "s50", "dense", "skip0", "gaps"), paged_names=(), seed=False,
               oracle_cpu=False):
     (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
@@ -651,6 +709,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "prefill_gaps", "decode70", "decode_dense",
                                        "decode_gaps", "mla70", "mla_dense", "mla_gaps", "decode_paged70",
+                                       "decode_paged_layouts",
                                        "mla_paged70", "long_prefill70", "long_prefill_dense", "prefill_lengths"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -684,6 +743,9 @@ def main():
         t = (0.7,) if args.only == "long_prefill70" else ()
         rows, _, _ = bench_long_prefill(steps, warmup, targets=t, window_leg=False)
         print(json.dumps({"only": args.only, "result": rows}, default=str), flush=True)
+        return
+    if args.only == "decode_paged_layouts":
+        print(json.dumps({"only": args.only, "result": bench_paged_layouts(steps, warmup)}, default=str), flush=True)
         return
     if args.only in ("decode_paged70", "mla_paged70"):
         fn = bench_decode if args.only == "decode_paged70" else bench_mla
