@@ -131,9 +131,9 @@ def long_prefill_workload(seed=1004):
     return (B, Hq, Hkv, L, d), (q, k, v)
 
 
-def calibrate_prefill(q, k, v, targets, window=0):
+def calibrate_prefill(q, k, v, targets, window=0, causal=True, tile_q=128):
     """lambda for each target sparsity: the gap pass (no O), then the exact quantile."""
-    gap = bl.blasst_prefill_gaps(q, k, v, causal=True, lam=0.0, tile_q=128, window=window)
+    gap = bl.blasst_prefill_gaps(q, k, v, causal=causal, lam=0.0, tile_q=tile_q, window=window)
     g = gap.cpu().numpy().ravel()
     return {t: bl.blasst_calibrate_search(g, t) for t in targets}
 
@@ -618,6 +618,42 @@ def bench_prefill_lengths(steps, warmup, lengths=(2048, 4096, 8192, 16384, 32768
     return rows
 
 
+def bench_prefill_variants(steps, warmup):
+    """The prefill kernels off the headline shape, on the 8K workload's input
+    recipe (B = 1, 32 query / 8 KV heads, L = 8192): non-causal, d = 64, and a
+    64-row query tile, each at its own 70% lambda and at lambda = 0.  Executed
+    MFMA work counts QK of every visited (tile, block) pair and P.V of every
+    executed one."""
+    cases = [("causal_d128_tile128", True, 128, 128), ("noncausal_d128_tile128", False, 128, 128),
+             ("causal_d64_tile128", True, 64, 128), ("causal_d128_tile64", True, 128, 64),
+             ("causal_d64_tile64", True, 64, 64)]
+    B, Hq, Hkv, L = 1, 32, 8, 8192
+    rows = []
+    for name, causal, d, tile in cases:
+        q, k, v = inputs.prefill_inputs(B, Hq, Hkv, L, d, n_random=6, local_window=1, device="cuda", seed=1001)
+        lam70, _ = calibrate_prefill(q, k, v, [0.7], causal=causal, tile_q=tile)[0.7]
+        out = torch.empty(B, Hq, L, d, dtype=torch.bfloat16, device="cuda")
+        dense_flops = 4.0 * B * Hq * L * L * d / (2 if causal else 1)
+        row = {"case": name, "causal": causal, "d": d, "tile_q": tile, "lambda70": lam70}
+        for leg, lam in (("s70", lam70), ("dense", 0.0)):
+            def pf(cnt=None, lam=lam):
+                return bl.blasst_prefill(q, k, v, causal=causal, lam=lam, tile_q=tile, out=out, counters=cnt)
+            mean_ms, _, _ = time_calls(pf, steps, warmup)
+            vis, skp = counts(lambda c: pf(c))
+            mfma = (vis + (vis - skp)) * 2.0 * tile * 64 * d
+            row[leg] = {"ms": mean_ms, "sparsity": skp / vis,
+                        "dense_equiv_tflops": dense_flops / (mean_ms * 1e-3) / 1e12,
+                        "mfma_util_executed": mfma / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        row["speedup70_vs_dense"] = row["dense"]["ms"] / row["s70"]["ms"]
+        log(f"prefill {name}: dense {row['dense']['ms']:.3f} ms ({row['dense']['mfma_util_executed']:.3f} MFMA), "
+            f"70% {row['s70']['ms']:.3f} ms ({row['s70']['mfma_util_executed']:.3f}), "
+            f"speedup {row['speedup70_vs_dense']:.3f}")
+        rows.append(row)
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def window_prefill(q, k, v, out, W, steps, warmup):
     """The same prefill with a sliding window of W keys, at the 70% lambda of
     the windowed gaps and at lambda = 0."""
@@ -709,7 +745,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "prefill_gaps", "decode70", "decode_dense",
                                        "decode_gaps", "mla70", "mla_dense", "mla_gaps", "decode_paged70",
-                                       "decode_paged_layouts",
+                                       "decode_paged_layouts", "prefill_variants",
                                        "mla_paged70", "long_prefill70", "long_prefill_dense", "prefill_lengths"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -743,6 +779,10 @@ def main():
         t = (0.7,) if args.only == "long_prefill70" else ()
         rows, _, _ = bench_long_prefill(steps, warmup, targets=t, window_leg=False)
         print(json.dumps({"only": args.only, "result": rows}, default=str), flush=True)
+        return
+    if args.only == "prefill_variants":
+        print(json.dumps({"only": args.only, "result": bench_prefill_variants(steps, warmup)}, default=str),
+              flush=True)
         return
     if args.only == "decode_paged_layouts":
         print(json.dumps({"only": args.only, "result": bench_paged_layouts(steps, warmup)}, default=str), flush=True)
