@@ -51,8 +51,10 @@ def _decode_cfg(i, mla):
     B = int(r.integers(1, 3 if mla else 5))
     lens = [int(x) for x in r.integers(1, Lmax + 1, size=B)]
     lens[0] = Lmax
+    # the latent head count (all 128 heads, or a shard of them) from a stream of its own
+    g_mla = int(np.random.default_rng(7500 + i).choice([16, 32, 64, 100, 128]))
     return dict(B=B, Lmax=Lmax, lens=lens, d=int(r.choice([64, 128])),
-                Hkv=1 if mla else int(r.choice([1, 2])), G=128 if mla else int(r.choice([1, 2, 4, 8, 16])),
+                Hkv=1 if mla else int(r.choice([1, 2])), G=g_mla if mla else int(r.choice([1, 2, 4, 8, 16])),
                 splits=min(int(r.choice([0, 1, 2, 3, 7])), -(-Lmax // 64)),  # at most one split per block
                 window=int(r.integers(1, Lmax + 1)) if r.random() < 0.3 else 0,
                 sink_seed=bool(r.random() < 0.3), page=int(r.choice([0, 0, 16, 32, 64])),
@@ -63,7 +65,7 @@ def _decode_case(i, mla):
     c = _decode_cfg(i, mla)
     say(f"[random {'latent' if mla else 'gqa'} decode {i}] {c}")
     if mla:
-        q, kc, _, lens = inputs.decode_inputs(c["B"], 128, 1, c["Lmax"], 576, 512, n_random=8, mla=True,
+        q, kc, _, lens = inputs.decode_inputs(c["B"], c["G"], 1, c["Lmax"], 576, 512, n_random=8, mla=True,
                                               device=DEV, seed=8000 + i, seq_lens=c["lens"])
         vc, dv = kc, 512
     else:
@@ -104,6 +106,6 @@ def test_random_gqa_decode(i):
     _decode_case(i, mla=False)
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(8))
 def test_random_latent_decode(i):
     _decode_case(i, mla=True)
