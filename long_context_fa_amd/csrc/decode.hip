@@ -11,19 +11,23 @@
 //
 // Here a workgroup (4 waves) owns one (split, KV head, sequence) unit and walks
 // its key blocks in batches of 4, one block per wave:
-//  1. every wave loads its block's K straight into MFMA operand registers and
-//     computes S^T = K q^T (16x16x32 bf16 MFMA; the G <= 16 query heads that
-//     share the KV head are the 16 columns, padded with zeros);
+//  1. every wave copies its block's K global -> LDS into its own K slot
+//     (global_load_lds, whole 256-byte rows per instruction: the loads go to
+//     memory as full 128-byte lines, where MFMA-layout register loads would
+//     take 64 bytes of 16 rows each and run the compute unit out of
+//     outstanding-miss entries at ~5.7 TB/s), reads it back into MFMA operand
+//     registers and computes S^T = K q^T (16x16x32 bf16 MFMA; the G <= 16
+//     query heads that share the KV head are the 16 columns, padded with
+//     zeros); the next batch's K copy goes out as soon as the slot is read;
 //  2. the 4 block maxima are exchanged through LDS and every wave evaluates
 //     the 4 decisions in order.  The running max never depends on earlier
 //     decisions (a skipped block has m~ < m + ln(lambda) <= m), so the
 //     decision of block i uses the exclusive prefix max of the block maxima;
-//  3. a wave whose block is executed copies V global -> LDS into its own slice
-//     (global_load_lds, no registers; K and V loads carry the non-temporal
-//     hint, since a step reads each cache row once), then issues the next
-//     batch's K loads,
-//     computes the exponentials while both are in flight, and accumulates
-//     O^T += V^T P^T with the V^T operand taken by the gfx950 transpose read.
+//  3. a wave whose block is executed copies V global -> LDS into its own V
+//     slot (K and V copies carry the non-temporal hint, since a step reads
+//     each cache row once), computes the exponentials while it is in flight,
+//     and accumulates O^T += V^T P^T with the V^T operand taken by the gfx950
+//     transpose read.
 //     A skipped block issues no V load at all.
 // Each wave keeps its own online-softmax state; the 4 states are merged with
 // the log-sum-exp rule at the end, and across splits by the combine kernel.
@@ -52,8 +56,17 @@ __device__ __forceinline__ int dswz(int row)
     return DG > 8 ? (row & 7) << 1 : ((row >> 1) & 3) << 1;
 }
 
+// K slot chunk swizzle.  The operand read (ds_read_b128) serves 8 lanes per
+// LDS cycle: rows 16 kt + 0..7 (or + 8..15) at one logical chunk.  A row is
+// one (d = 64) or two (d = 128) full bank lines, so the 8 rows' physical
+// chunks must differ in bits 0-2.  The XOR stays inside a 128-byte line, so
+// each aligned group of 8 lanes of a copy still reads one whole line.
+__device__ __forceinline__ int kswz(int row) { return row & 7; }
+
 template <int D, bool SKIP, bool OUT_BF16, bool PAGED, bool GAPS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// With d = 128 the K and V slots hold one workgroup per compute unit (one
+// wave per SIMD), so the wave may use the whole register file; otherwise two.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 64 && !GAPS ? 1 : 2, D > 64 && !GAPS ? 1 : 2)))
 void decode_gqa_kernel(const DecodeArgs a)
 {
     constexpr int RB = D * 2;          // bytes per V row
@@ -64,7 +77,11 @@ void decode_gqa_kernel(const DecodeArgs a)
     static_assert(16 % RPI == 0, "a V copy must stay inside one 16-row group");
     constexpr int NS = D / 32;         // 32-wide k-steps of the QK product
     constexpr int NDT = D / 16;        // 16-row d tiles of O^T
-    constexpr int KLOADS = 4 * NS;     // K register loads per wave per block
+    // K slots (one 64-row tile per wave) and V slots; the V slots are reused
+    // as fp32 staging by the final merge.  With d = 128 the 128 KB hold one
+    // workgroup (4 waves) per compute unit, which keeps enough whole-line
+    // copies in flight.
+    __shared__ __attribute__((aligned(1024))) char ksm[NWD * TB];
     __shared__ __attribute__((aligned(1024))) char vsm[GAPS ? 1024 : NWD * TB];
     __shared__ float mblk[2][NWD][16];
     __shared__ float mw_s[NWD][16], lw_s[NWD][16];
@@ -140,38 +157,73 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
     }
 
-    // K operand of S^T = K q^T for one 64-key block, straight from HBM into
-    // registers: tile kt = 16 keys, lane (m = key, grp) holds
-    // K[key][32 st + 8 grp .. +7].  Every lane always issues all KLOADS loads:
-    // keys outside the split read row len-1 (finite; their scores are masked
-    // to -inf below), because the V wait counts on exactly KLOADS younger
-    // vector-memory operations (plus the id load of a paged cache).
-    u32x4 kr[4][NS];
-    auto load_k = [&](int j, const int (&ids)[4]) {
+    // K of block j -> this wave's K slot, row-major with the 16-byte chunks
+    // XOR-swizzled by row (kswz).  Keys outside the split or past len re-read
+    // row len-1 (finite; their scores are masked to -inf below).
+    char *const kt_slot = ksm + w * TB;
+    // Tile copy (K or V): copy i moves RPI rows (1 KB).  When every row of
+    // block j is a visible key (the common case), the 16 rows of a group lie
+    // in one page (or one sequence) from a wave-uniform base, walked with one
+    // scalar add per copy, and a lane's byte offset from the copy's first
+    // row depends only on the parity of i (the swizzles depend on the row
+    // mod 8).  Otherwise each lane clamps its own row.
+    const int rin = lane / DG, pch = lane % DG;
+    const bool offs32 = (int64_t)RPI * (a.k_st > a.v_st ? a.k_st : a.v_st) * 2 < ((int64_t)1 << 30);
+    auto lane_off = [&](int i, int64_t st, bool isk) -> uint32_t {
+        const int row = i * RPI + rin;
+        const int c = pch ^ (isk ? kswz(row) : dswz<DG>(row));
+        return (uint32_t)((int64_t)rin * st * 2 + c * 16);
+    };
+    const uint32_t koff[2] = {lane_off(0, a.k_st, true), lane_off(1, a.k_st, true)};
+    const uint32_t voff[2] = {lane_off(0, a.v_st, false), lane_off(1, a.v_st, false)};
+    auto copy_rows = [&](const uint16_t *base, int64_t st, int64_t sb, const int (&ids)[4], int j, char *dst,
+                         const uint32_t (&off)[2], bool isk) __attribute__((always_inline)) {
+        if (offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
+            constexpr int CPG = 16 / RPI; // copies per 16-row group
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int key = j * BC + 16 * kt + n;
-            const int kc = (j < je && key < len) ? (key > klo ? key : klo) : len - 1;
-            const uint16_t *rp = kp + page_off(ids, kt, a.k_sb) + (int64_t)(kc & pmask) * a.k_st;
+            for (int g = 0; g < 4; ++g) {
+                const uint16_t *gb = base + page_off(ids, g, sb) + (int64_t)((j * BC + 16 * g) & pmask) * st;
+                uint64_t addr = (uint64_t)(uintptr_t)gb;
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
-                kr[kt][st] = __builtin_nontemporal_load((const u32x4 *)(rp + 32 * st + 8 * grp));
+                for (int q = 0; q < CPG; ++q) {
+                    const int i = g * CPG + q;
+                    copy16_to_lds_s<true>((const void *)(uintptr_t)addr, off[i & 1], dst + i * 1024);
+                    addr += (uint64_t)(RPI * 2) * (uint64_t)st;
+                    asm volatile("" : "+s"(addr)); // one running base, not one register pair per copy
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < VI; ++i) {
+                const int row = i * RPI + rin;
+                const int c = pch ^ (isk ? kswz(row) : dswz<DG>(row));
+                const int key = j * BC + row;
+                const int kc = (j < je && key < len) ? (key > klo ? key : klo) : len - 1;
+                copy16_to_lds<true>(base + page_off(ids, (i * RPI) >> 4, sb) + (int64_t)(kc & pmask) * st + c * 8,
+                                    dst + i * 1024);
+            }
         }
     };
+    auto copy_k = [&](int j, const int (&ids)[4]) { copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_slot, koff, true); };
+    // K operand of S^T = K q^T from the slot: tile kt = 16 keys, lane
+    // (m = key, grp) holds K[key][32 st + 8 grp .. +7] (logical chunk
+    // 4 st + grp).  The caller waits for the copy first.
+    u32x4 kr[4][NS];
+    auto read_k = [&]() {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int row = 16 * kt + n;
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+                kr[kt][st] = *(const u32x4 *)(kt_slot + row * RB + (((4 * st + grp) ^ kswz(row)) * 16));
+        }
+    };
+    // The slot is refilled only once every read of it has returned.
+    auto reads_done = [&]() { __builtin_amdgcn_s_waitcnt(0xC07F); }; // lgkmcnt(0)
     // V tile of block j -> this wave's slice, row-major with the 16-byte
     // chunks XOR-swizzled by row (rows past len re-read row len-1: finite
     // values whose probabilities are exactly 0).
-    auto copy_v = [&](int j, const int (&ids)[4]) {
-#pragma unroll
-        for (int i = 0; i < VI; ++i) {
-            const int row = i * RPI + lane / DG;
-            const int c = (lane % DG) ^ dswz<DG>(row);
-            int key = j * BC + row;
-            key = key < len ? (key > klo ? key : klo) : len - 1;
-            copy16_to_lds<true>(vp + page_off(ids, (i * RPI) >> 4, a.v_sb) + (int64_t)(key & pmask) * a.v_st + c * 8,
-                          vt + i * 1024);
-        }
-    };
+    auto copy_v = [&](int j, const int (&ids)[4]) { copy_rows(vp, a.v_st, a.v_sb, ids, j, vt, voff, false); };
 
     f32x4 o[NDT];
 #pragma unroll
@@ -186,7 +238,9 @@ void decode_gqa_kernel(const DecodeArgs a)
     const int vj = (lane & 15) >> 2, vq = lane & 3, vgrp = lane >> 4;
 
     // Page ids (paged cache): pc for this batch's block (its V copy), pn for
-    // the next batch's (its K loads); idv is the vector load in flight.
+    // the next batch's (its K copy, issued first thing in a batch); idv is
+    // the vector load of the next batch's ids, issued a batch ahead beside
+    // the K copy so that the wait for one covers the other.
     int pc[4] = {0, 0, 0, 0}, pn[4] = {0, 0, 0, 0}, idv = 0;
 
     // Sink seed (splits after the first): the decisions' prefix max starts
@@ -194,7 +248,10 @@ void decode_gqa_kernel(const DecodeArgs a)
     // the block itself (the rows of its K land in L2 once).
     if (a.sink_seed && s > 0 && jb < je) {
         ids_take(ids_load(j0), pc);
-        load_k(j0, pc);
+        copy_k(j0, pc);
+        wait_vmcnt<0>();
+        compiler_fence();
+        read_k();
         f32x4 sc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -217,13 +274,31 @@ void decode_gqa_kernel(const DecodeArgs a)
     }
     if (jb < je) {
         ids_take(ids_load(jb + w), pc);
-        load_k(jb + w, pc);
+        reads_done(); // (the sink block's reads, if any)
+        compiler_fence();
+        copy_k(jb + w, pc);
         idv = ids_load(jb + NWD + w);
     }
     int it = 0;
     for (int j0 = jb; j0 < je; j0 += NWD, ++it) {
         const int j = j0 + w; // this wave's block
         const int par = it & 1;
+        const bool more = j0 + NWD < je;
+        // K of this block landed (and every older copy: V of the last
+        // batch was waited for before its P.V); read it, then refill the
+        // slot with the next batch's block right away.
+        wait_vmcnt<0>();
+        compiler_fence();
+        read_k();
+        if (PAGED)
+            ids_take(idv, pn); // the next batch's page ids (landed with this block's K)
+        reads_done();
+        compiler_fence();
+        if (more) {
+            copy_k(j0 + NWD + w, pn);
+            if (PAGED)
+                idv = ids_load(j0 + 2 * NWD + w);
+        }
         f32x4 sc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -232,8 +307,6 @@ void decode_gqa_kernel(const DecodeArgs a)
             for (int st = 0; st < NS; ++st)
                 sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
         }
-        if (PAGED)
-            ids_take(idv, pn); // issued behind the K loads just consumed
         // Mask keys outside klo .. len-1 (and the whole block if j >= je).
         const int k0 = j * BC;
         if (j >= je || k0 + BC > len || k0 < klo) {
@@ -291,16 +364,6 @@ void decode_gqa_kernel(const DecodeArgs a)
         const bool exec = !GAPS && j < je && !my_skip;
         if (exec)
             copy_v(j, pc); // V only for an executed block
-        const bool more = j0 + NWD < je;
-        if (more) {
-            load_k(j0 + NWD + w, pn); // next batch's K in flight
-            if (PAGED) {
-                idv = ids_load(j0 + 2 * NWD + w);
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-                    pc[kt] = pn[kt];
-            }
-        }
 
         if (exec) {
             // Online-softmax update with this wave's running max.
@@ -327,12 +390,9 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
                 o[dt] *= alpha;
-            // The V copy is older than the next K loads (and, paged, the id
-            // load behind them): wait for it only.
-            if (more)
-                wait_vmcnt<KLOADS + (PAGED ? 1 : 0)>();
-            else
-                wait_vmcnt<0>();
+            // The V copy is the youngest vector-memory operation (the next
+            // K copy and, paged, the id load went out before it).
+            wait_vmcnt<0>();
             compiler_fence();
             // O^T += V^T P^T: two k-steps of 32 keys.  A operand lane (m = d,
             // grp) slot i <-> key 32 u2 + 16 (i / 4) + 4 grp + i % 4.
@@ -348,6 +408,11 @@ void decode_gqa_kernel(const DecodeArgs a)
                     const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
                     o[dt] = mfma16(as_bf16x8(va), pf[u2], o[dt]);
                 }
+        }
+        if (PAGED && more) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                pc[kt] = pn[kt]; // the next batch's block (its V copy)
         }
     }
 
