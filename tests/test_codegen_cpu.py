@@ -28,7 +28,8 @@ KERNELS = {"mla.hip": "decode_mla_kernel"}
 @pytest.fixture(scope="module", params=sorted(KERNELS))
 def kasm(request, tmp_path_factory):
     out = tmp_path_factory.mktemp("asm") / (request.param + ".s")
-    cmd = [B.HIPCC] + B.FLAGS + ["-S", "--cuda-device-only", os.path.join(B.CSRC, request.param), "-o", str(out)]
+    cmd = ([B.HIPCC] + B.FLAGS + B.EXTRA.get(request.param, [])
+           + ["-S", "--cuda-device-only", os.path.join(B.CSRC, request.param), "-o", str(out)])
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return KERNELS[request.param], out.read_text()
