@@ -193,7 +193,9 @@ typedef struct {
 
 /* Host-only: the split count a call with *p will use and the device workspace
  * (bytes) it needs; either output pointer may be NULL.  Same validation as
- * blasst_decode. */
+ * blasst_decode.  With more than one split the workspace holds each split's
+ * fp32 partial output, max and sum per query head, and each split's block
+ * counts (merged into counters by the combine step); with one split it is 0. */
 blasst_status blasst_decode_plan(const blasst_decode_params *p, int *num_splits_used,
                                  size_t *workspace_bytes);
 

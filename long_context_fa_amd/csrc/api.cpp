@@ -292,7 +292,8 @@ size_t workspace_for(const blasst_decode_params *p, int S)
         return 0;
     const int64_t G = p->Hq / p->Hkv;
     const int64_t units = p->B * p->Hkv * S * G;
-    return (size_t)units * (size_t)(p->dv + 2) * sizeof(float) + 256;
+    const int64_t wgs = p->B * p->Hkv * S; // (visited, skipped) per split workgroup
+    return (size_t)units * (size_t)(p->dv + 2) * sizeof(float) + (size_t)wgs * 2 * sizeof(int32_t) + 256;
 }
 
 } // namespace
@@ -349,6 +350,8 @@ blasst_status run_decode(const blasst_decode_params *p, const blasst_decode_page
         const int64_t units = p->B * p->Hkv * S * a.G;
         a.part_o = (float *)workspace;
         a.part_ml = a.part_o + units * p->dv;
+        if (p->counters)
+            a.part_cnt = (int32_t *)(a.part_ml + 2 * units);
     }
     a.skip_map = p->skip_map;
     a.gap_map = p->gap_map;

@@ -488,7 +488,11 @@ void decode_gqa_kernel(const DecodeArgs a)
                 for (int j = nkb_b; j < a.nkb; ++j)
                     unvisited(j);
         }
-        if (a.counters && je > jb) {
+        if (a.part_cnt) {
+            const int64_t w = ((int64_t)(b * a.Hkv + g) * S + s) * 2;
+            a.part_cnt[w] = je > jb ? je - jb : 0;
+            a.part_cnt[w + 1] = je > jb ? n_skipped : 0;
+        } else if (a.counters && je > jb) {
             atomicAdd(a.counters, (unsigned long long)(je - jb));
             atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
         }
@@ -500,10 +504,28 @@ void decode_gqa_kernel(const DecodeArgs a)
 // heads.  Weights are exp2(m_s - M) with M the largest split max among
 // splits that saw keys (kept as a running max, one chunk of splits at a
 // time); splits with l = 0 contribute nothing, and a NaN l (a NaN score)
-// takes part, so the NaN reaches O.
+// takes part, so the NaN reaches O.  The first workgroup of each sequence
+// also sums the split workgroups' block counts into the counters.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeArgs a, int dv)
 {
+    if (a.part_cnt && blockIdx.x == 0 && threadIdx.x < 64) {
+        const int n = a.Hkv * a.num_splits;
+        const int32_t *pc = a.part_cnt + (int64_t)blockIdx.y * n * 2;
+        unsigned long long vis = 0, skp = 0;
+        for (int i = (int)threadIdx.x; i < n; i += 64) {
+            vis += (unsigned)pc[2 * i];
+            skp += (unsigned)pc[2 * i + 1];
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            vis += __shfl_down(vis, off);
+            skp += __shfl_down(skp, off);
+        }
+        if (threadIdx.x == 0 && vis != 0) {
+            atomicAdd(a.counters, vis);
+            atomicAdd(a.counters + 1, skp);
+        }
+    }
     const int tph = dv / 4, hpw = 256 / tph;
     const int hq = blockIdx.x * hpw + (int)threadIdx.x / tph;
     const int b = blockIdx.y;

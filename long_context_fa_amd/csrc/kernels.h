@@ -41,6 +41,11 @@ struct DecodeArgs {
     uint8_t *skip_map;
     float *gap_map;
     unsigned long long *counters;
+    // Split workgroups' (visited, skipped) block counts, [B][Hkv][S][2]
+    // int32, summed into counters by the combine kernel: set when counters
+    // are asked for with num_splits > 1, so that thousands of workgroups do
+    // not each add into the same two words.  Null: workgroups add directly.
+    int32_t *part_cnt;
     // Paged cache (page_table != nullptr): k/v point at page pools whose
     // batch stride is the page stride; row r of sequence b lives in pool page
     // page_table[b * pt_stride + (r >> page_shift)] (ids clamped into

@@ -442,7 +442,11 @@ void decode_mla_kernel(const DecodeArgs a)
                 for (int j = nkb_b; j < a.nkb; ++j)
                     unvisited(j);
         }
-        if (a.counters && je > jb) {
+        if (a.part_cnt) {
+            const int64_t w = ((int64_t)b * S + s) * 2; // Hkv = 1
+            a.part_cnt[w] = je > jb ? je - jb : 0;
+            a.part_cnt[w + 1] = je > jb ? n_skipped : 0;
+        } else if (a.counters && je > jb) {
             atomicAdd(a.counters, (unsigned long long)(je - jb));
             atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
         }

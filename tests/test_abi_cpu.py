@@ -174,7 +174,7 @@ def test_latent_plan_accepts_head_shards():
     lens = torch.full((16,), 4096, dtype=torch.int32)
     for hq in (1, 16, 40, 64, 128):
         S, ws = bl.blasst_decode_plan(_bf16(16, hq, 576), kc, kc, lens, lam=0.01, dv=512)
-        assert S >= 1 and ws == (16 * hq * S * (512 + 2) * 4 + 256 if S > 1 else 0)
+        assert S >= 1 and ws == (16 * hq * S * (512 + 2) * 4 + 16 * S * 2 * 4 + 256 if S > 1 else 0)
 
 
 def test_decode_plan_host_only():
