@@ -130,7 +130,16 @@ void decode_gqa_kernel(const DecodeArgs a)
         g0 = (j < je && g0 < len) ? (g0 > klo ? g0 : klo) : len - 1;
         return a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
     };
+    // Pages of 64 rows or more hold a whole (aligned) block: one id per block.
+    const bool one_page = PAGED && a.page_shift >= 6;
     auto ids_take = [&](int v, int (&ids)[4]) {
+        if (one_page) {
+            int id = __builtin_amdgcn_readlane(v, 0);
+            id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
+            asm volatile("" : "+s"(id));
+            ids[0] = id;
+            return;
+        }
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             int id = __builtin_amdgcn_readlane(v, kt);
@@ -140,7 +149,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
     };
     auto page_off = [&](const int (&ids)[4], int grp16, int64_t sb) -> int64_t {
-        return PAGED ? (int64_t)ids[grp16] * sb : 0;
+        return PAGED ? (int64_t)ids[one_page ? 0 : grp16] * sb : 0;
     };
     char *const vt = vsm + w * TB; // this wave's V slice
 
@@ -178,7 +187,16 @@ void decode_gqa_kernel(const DecodeArgs a)
     const uint32_t voff[2] = {lane_off(0, a.v_st, false), lane_off(1, a.v_st, false)};
     auto copy_rows = [&](const uint16_t *base, int64_t st, int64_t sb, const int (&ids)[4], int j, char *dst,
                          const uint32_t (&off)[2], bool isk) __attribute__((always_inline)) {
-        if (offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
+        if (one_page && offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
+            // the block's 64 rows are consecutive rows of one page
+            uint64_t addr = (uint64_t)(uintptr_t)(base + (int64_t)ids[0] * sb + (int64_t)((j * BC) & pmask) * st);
+#pragma unroll
+            for (int i = 0; i < VI; ++i) {
+                copy16_to_lds_s<true>((const void *)(uintptr_t)addr, off[i & 1], dst + i * 1024);
+                addr += (uint64_t)(RPI * 2) * (uint64_t)st;
+                asm volatile("" : "+s"(addr));
+            }
+        } else if (offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
             constexpr int CPG = 16 / RPI; // copies per 16-row group
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
