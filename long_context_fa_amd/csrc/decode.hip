@@ -185,14 +185,14 @@ void decode_gqa_kernel(const DecodeArgs a)
     };
     const uint32_t koff[2] = {lane_off(0, a.k_st, true), lane_off(1, a.k_st, true)};
     const uint32_t voff[2] = {lane_off(0, a.v_st, false), lane_off(1, a.v_st, false)};
-    auto copy_rows = [&](const uint16_t *base, int64_t st, int64_t sb, const int (&ids)[4], int j, char *dst,
+    auto copy_rows = [&](const uint16_t *base, int64_t st, int64_t sb, const int (&ids)[4], int j, uint32_t dst,
                          const uint32_t (&off)[2], bool isk) __attribute__((always_inline)) {
         if (one_page && offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
             // the block's 64 rows are consecutive rows of one page
             uint64_t addr = (uint64_t)(uintptr_t)(base + (int64_t)ids[0] * sb + (int64_t)((j * BC) & pmask) * st);
 #pragma unroll
             for (int i = 0; i < VI; ++i) {
-                copy16_to_lds_s<true>((const void *)(uintptr_t)addr, off[i & 1], dst + i * 1024);
+                copy16_to_lds_s<true>((const void *)(uintptr_t)addr, off[i & 1], dst + i * 1024u);
                 addr += (uint64_t)(RPI * 2) * (uint64_t)st;
                 asm volatile("" : "+s"(addr));
             }
@@ -205,7 +205,7 @@ void decode_gqa_kernel(const DecodeArgs a)
 #pragma unroll
                 for (int q = 0; q < CPG; ++q) {
                     const int i = g * CPG + q;
-                    copy16_to_lds_s<true>((const void *)(uintptr_t)addr, off[i & 1], dst + i * 1024);
+                    copy16_to_lds_s<true>((const void *)(uintptr_t)addr, off[i & 1], dst + i * 1024u);
                     addr += (uint64_t)(RPI * 2) * (uint64_t)st;
                     asm volatile("" : "+s"(addr)); // one running base, not one register pair per copy
                 }
@@ -218,11 +218,12 @@ void decode_gqa_kernel(const DecodeArgs a)
                 const int key = j * BC + row;
                 const int kc = (j < je && key < len) ? (key > klo ? key : klo) : len - 1;
                 copy16_to_lds<true>(base + page_off(ids, (i * RPI) >> 4, sb) + (int64_t)(kc & pmask) * st + c * 8,
-                                    dst + i * 1024);
+                                    dst + i * 1024u);
             }
         }
     };
-    auto copy_k = [&](int j, const int (&ids)[4]) { copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_slot, koff, true); };
+    const uint32_t kt_lds = lds_addr(kt_slot), vt_lds = lds_addr(vt);
+    auto copy_k = [&](int j, const int (&ids)[4]) { copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_lds, koff, true); };
     // K operand of S^T = K q^T from the slot: tile kt = 16 keys, lane
     // (m = key, grp) holds K[key][32 st + 8 grp .. +7] (logical chunk
     // 4 st + grp).  The caller waits for the copy first.
@@ -241,7 +242,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     // V tile of block j -> this wave's slice, row-major with the 16-byte
     // chunks XOR-swizzled by row (rows past len re-read row len-1: finite
     // values whose probabilities are exactly 0).
-    auto copy_v = [&](int j, const int (&ids)[4]) { copy_rows(vp, a.v_st, a.v_sb, ids, j, vt, voff, false); };
+    auto copy_v = [&](int j, const int (&ids)[4]) { copy_rows(vp, a.v_st, a.v_sb, ids, j, vt_lds, voff, false); };
 
     f32x4 o[NDT];
 #pragma unroll

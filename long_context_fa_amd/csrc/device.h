@@ -84,8 +84,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// LDS byte address of a pointer into __shared__ memory: the value the copies
+// below put in m0.  Taken once per buffer, outside the loops: converting a
+// generic pointer costs a null test, and per copy those tests and the 64-bit
+// pointers they need crowd the scalar registers.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_void *)p; }
+
 // 16-byte global -> LDS copy (global_load_lds_dwordx4); the wave's 64 lanes
-// fill 1024 consecutive LDS bytes starting at lds_base (wave-uniform).  It is
+// fill 1024 consecutive LDS bytes starting at LDS byte address lds
+// (wave-uniform).  It is
 // issued from inline asm so that the compiler does not add its own
 // conservative vmcnt(0) waits before every later LDS read: the kernels wait
 // for these copies explicitly (wait_vmcnt) before the barrier that publishes
@@ -97,9 +104,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // NT = true adds the non-temporal hint, for data that is streamed once (a
 // decode step reads each cache row once).
 template <bool NT = false>
-__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     if (NT)
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(src) : "memory", "m0");
     else
@@ -109,9 +116,9 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
 // Same copy with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
 // byte offset: the per-block address arithmetic becomes one scalar add.
 template <bool NT = false>
-__device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff, void *lds_base)
+__device__ __forceinline__ void copy16_to_lds_s(const void *sbase, uint32_t voff, uint32_t lds)
 {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     const uint64_t b = (uint64_t)(uintptr_t)sbase;
     // readfirstlane returns int: zero-extend each half (a sign-extended low
     // half would turn the base into an invalid address).

@@ -146,13 +146,15 @@ void decode_mla_kernel(const DecodeArgs a)
     // row inside (finite data, masked later).  Offsets are 32-bit from the sequence (or page)
     // base gb = group_base(j) (the host checks rows * row stride).
     auto tile = [&](int it) { return smem + (it & 1) * TB; };
+    const uint32_t smem_lds = lds_addr(smem); // the tiles as LDS byte addresses, for the copies
+    auto tile_l = [&](int it) { return smem_lds + (uint32_t)((it & 1) * TB); };
     const uint32_t rowb = (uint32_t)a.k_st * 2;
-    auto copy_one = [&](const uint16_t *gb, int j, char *t, int i) {
+    auto copy_one = [&](const uint16_t *gb, int j, uint32_t t, int i) {
         if (i < 16) {
             int key = j * BC + 16 * w + i;
             key = key < len ? (key > klo ? key : klo) : len - 1;
             copy16_to_lds_s<true>(gb + (int64_t)(key & pmask) * a.k_st, (uint32_t)(16 * (lane ^ swzl(i))),
-                            t + (16 * w + i) * LRB);
+                            t + (uint32_t)((16 * w + i) * LRB));
         } else {
             const int e = i - 16;
             int lr = lane >> 3;
@@ -160,7 +162,7 @@ void decode_mla_kernel(const DecodeArgs a)
             int key = j * BC + 16 * w + 8 * e + lr;
             key = key < len ? (key > klo ? key : klo) : len - 1;
             const uint32_t off = LRB + 16 * ((lane & 7) ^ ((4 * e + (lane >> 4)) & 7)); // swzr of the row
-            copy16_to_lds_s<true>(gb, (uint32_t)(key & pmask) * rowb + off, t + ROPE + (16 * w + 8 * e) * RRB);
+            copy16_to_lds_s<true>(gb, (uint32_t)(key & pmask) * rowb + off, t + (uint32_t)(ROPE + (16 * w + 8 * e) * RRB));
         }
     };
 
@@ -198,7 +200,7 @@ void decode_mla_kernel(const DecodeArgs a)
         const uint16_t *gb = group_base(jf);
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            copy_one(gb, jf, tile(it0), i);
+            copy_one(gb, jf, tile_l(it0), i);
         wait_vmcnt<0>();
         lds_barrier();
     }
@@ -213,7 +215,7 @@ void decode_mla_kernel(const DecodeArgs a)
         // it, so a burst would stall the MFMA stream).
         const bool dma = jn < je;
         const uint16_t *gbn = group_base(jn);
-        char *const tn = tile(it + 1);
+        const uint32_t tn = tile_l(it + 1);
         f32x16 sc[2];
         // rope offsets are recomputed here (4 per block) to spare registers
         int nl = n;

@@ -197,12 +197,12 @@ void prefill_kernel(const PrefillArgs a)
         voff[i] = (uint32_t)((row * a.v_st + c * 8) * 2);
     }
     const int kmin = CAUSAL && r0 - a.win + 1 > 0 ? r0 - a.win + 1 : 0; // lowest key a row of the tile sees
-    auto copy_tile = [&](const uint16_t *base, int64_t st, const uint32_t *off, int j, char *dst) {
+    auto copy_tile = [&](const uint16_t *base, int64_t st, const uint32_t *off, int j, uint32_t dst) {
         if ((j + 1) * BC <= L && j * BC >= kmin) {
             const uint16_t *sb = base + (int64_t)j * BC * st;
 #pragma unroll
             for (int i = 0; i < KI; ++i)
-                copy16_to_lds_s(sb, off[i], dst + (w * KI + i) * 1024);
+                copy16_to_lds_s(sb, off[i], dst + (w * KI + i) * 1024u);
         } else {
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
@@ -211,12 +211,16 @@ void prefill_kernel(const PrefillArgs a)
                 const int c = (lane % DG) ^ pswz<DG>(row);
                 int key = j * BC + row;
                 key = key < L ? (key > kmin ? key : kmin) : L - 1;
-                copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024);
+                copy16_to_lds(base + (int64_t)key * st + c * 8, dst + ins * 1024u);
             }
         }
     };
     auto kbuf = [&](int j) { return smem + (j & 1) * TB; };
     auto vbuf = [&](int j) { return smem + (2 + (j & 1)) * TB; };
+    // the same slots as LDS byte addresses, for the copies
+    const uint32_t smem_lds = lds_addr(smem);
+    auto kbuf_l = [&](int j) { return smem_lds + (uint32_t)((j & 1) * TB); };
+    auto vbuf_l = [&](int j) { return smem_lds + (uint32_t)((2 + (j & 1)) * TB); };
 
     // S^T = K_j Q^T (two 32-key tiles) with the causal / ragged mask, and the
     // block-local row max (base 2).
@@ -413,7 +417,7 @@ void prefill_kernel(const PrefillArgs a)
                 all &= vote[par][i];
         }
         if (j + 2 < nvis)
-            copy_tile(kp, a.k_st, koff, j + 2, kbuf(j)); // K ring refill
+            copy_tile(kp, a.k_st, koff, j + 2, kbuf_l(j)); // K ring refill
         bool skip = false;
         if (SKIP)
             skip = __builtin_amdgcn_readfirstlane(all) != 0; // uniform across the workgroup
@@ -431,7 +435,7 @@ void prefill_kernel(const PrefillArgs a)
         n_skipped += skip ? 1 : 0;
         const bool ecur = !skip;
         if (!GAPS && ecur)
-            copy_tile(vp, a.v_st, voff, j, vbuf(j)); // V_j only for an executed block
+            copy_tile(vp, a.v_st, voff, j, vbuf_l(j)); // V_j only for an executed block
 
         if (GAPS) {
             m2 = fmaxf(m2, mtc); // the running max, over every block
@@ -448,9 +452,9 @@ void prefill_kernel(const PrefillArgs a)
         eprev = GAPS ? false : ecur;
     };
 
-    copy_tile(kp, a.k_st, koff, jlo, kbuf(jlo));
+    copy_tile(kp, a.k_st, koff, jlo, kbuf_l(jlo));
     if (jlo + 1 < nvis) {
-        copy_tile(kp, a.k_st, koff, jlo + 1, kbuf(jlo + 1));
+        copy_tile(kp, a.k_st, koff, jlo + 1, kbuf_l(jlo + 1));
         wait_vmcnt<KI>();
     } else {
         wait_vmcnt<0>();
