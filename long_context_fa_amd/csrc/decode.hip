@@ -63,12 +63,17 @@ __device__ __forceinline__ int dswz(int row)
 // each aligned group of 8 lanes of a copy still reads one whole line.
 __device__ __forceinline__ int kswz(int row) { return row & 7; }
 
-template <int D, bool SKIP, bool OUT_BF16, bool PAGED, bool GAPS>
+// PG: 0 contiguous cache; 1 paged, pages of 16 or 32 rows (a block spans
+// several pages: one id per 16-row group); 2 paged, pages of 64 rows or more
+// (a block lies in one page: one id).
+template <int D, bool SKIP, bool OUT_BF16, int PG, bool GAPS>
 // With d = 128 the K and V slots hold one workgroup per compute unit (one
 // wave per SIMD), so the wave may use the whole register file; otherwise two.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 64 && !GAPS ? 1 : 2, D > 64 && !GAPS ? 1 : 2)))
 void decode_gqa_kernel(const DecodeArgs a)
 {
+    constexpr bool PAGED = PG != 0;
+    constexpr int NID = PG == 2 ? 1 : 4; // page ids per block
     constexpr int RB = D * 2;          // bytes per V row
     constexpr int DG = D / 8;          // 16-byte chunks per row
     constexpr int TB = BC * RB;        // bytes per V tile
@@ -130,10 +135,8 @@ void decode_gqa_kernel(const DecodeArgs a)
         g0 = (j < je && g0 < len) ? (g0 > klo ? g0 : klo) : len - 1;
         return a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
     };
-    // Pages of 64 rows or more hold a whole (aligned) block: one id per block.
-    const bool one_page = PAGED && a.page_shift >= 6;
-    auto ids_take = [&](int v, int (&ids)[4]) {
-        if (one_page) {
+    auto ids_take = [&](int v, int (&ids)[NID]) {
+        if (NID == 1) {
             int id = __builtin_amdgcn_readlane(v, 0);
             id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
             asm volatile("" : "+s"(id));
@@ -141,15 +144,15 @@ void decode_gqa_kernel(const DecodeArgs a)
             return;
         }
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < NID; ++kt) {
             int id = __builtin_amdgcn_readlane(v, kt);
             id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
             asm volatile("" : "+s"(id)); // in SGPRs here, before any later copy
             ids[kt] = id;
         }
     };
-    auto page_off = [&](const int (&ids)[4], int grp16, int64_t sb) -> int64_t {
-        return PAGED ? (int64_t)ids[one_page ? 0 : grp16] * sb : 0;
+    auto page_off = [&](const int (&ids)[NID], int grp16, int64_t sb) -> int64_t {
+        return PAGED ? (int64_t)ids[grp16 & (NID - 1)] * sb : 0;
     };
     char *const vt = vsm + w * TB; // this wave's V slice
 
@@ -185,9 +188,9 @@ void decode_gqa_kernel(const DecodeArgs a)
     };
     const uint32_t koff[2] = {lane_off(0, a.k_st, true), lane_off(1, a.k_st, true)};
     const uint32_t voff[2] = {lane_off(0, a.v_st, false), lane_off(1, a.v_st, false)};
-    auto copy_rows = [&](const uint16_t *base, int64_t st, int64_t sb, const int (&ids)[4], int j, uint32_t dst,
+    auto copy_rows = [&](const uint16_t *base, int64_t st, int64_t sb, const int (&ids)[NID], int j, uint32_t dst,
                          const uint32_t (&off)[2], bool isk) __attribute__((always_inline)) {
-        if (one_page && offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
+        if (PG == 2 && offs32 && j < je && j * BC >= klo && (j + 1) * BC <= len) {
             // the block's 64 rows are consecutive rows of one page
             uint64_t addr = (uint64_t)(uintptr_t)(base + (int64_t)ids[0] * sb + (int64_t)((j * BC) & pmask) * st);
 #pragma unroll
@@ -223,7 +226,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
     };
     const uint32_t kt_lds = lds_addr(kt_slot), vt_lds = lds_addr(vt);
-    auto copy_k = [&](int j, const int (&ids)[4]) { copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_lds, koff, true); };
+    auto copy_k = [&](int j, const int (&ids)[NID]) { copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_lds, koff, true); };
     // K operand of S^T = K q^T from the slot: tile kt = 16 keys, lane
     // (m = key, grp) holds K[key][32 st + 8 grp .. +7] (logical chunk
     // 4 st + grp).  The caller waits for the copy first.
@@ -242,7 +245,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     // V tile of block j -> this wave's slice, row-major with the 16-byte
     // chunks XOR-swizzled by row (rows past len re-read row len-1: finite
     // values whose probabilities are exactly 0).
-    auto copy_v = [&](int j, const int (&ids)[4]) { copy_rows(vp, a.v_st, a.v_sb, ids, j, vt_lds, voff, false); };
+    auto copy_v = [&](int j, const int (&ids)[NID]) { copy_rows(vp, a.v_st, a.v_sb, ids, j, vt_lds, voff, false); };
 
     f32x4 o[NDT];
 #pragma unroll
@@ -260,7 +263,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     // the next batch's (its K copy, issued first thing in a batch); idv is
     // the vector load of the next batch's ids, issued a batch ahead beside
     // the K copy so that the wait for one covers the other.
-    int pc[4] = {0, 0, 0, 0}, pn[4] = {0, 0, 0, 0}, idv = 0;
+    int pc[NID] = {}, pn[NID] = {}, idv = 0;
 
     // Sink seed (splits after the first): the decisions' prefix max starts
     // from the row maxima of block j0 instead of -inf.  Every wave scores
@@ -430,7 +433,7 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
         if (PAGED && more) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < NID; ++kt)
                 pc[kt] = pn[kt]; // the next batch's block (its V copy)
         }
     }
@@ -616,13 +619,15 @@ hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream, bool gaps)
 {
     const dim3 grid(a.num_splits, a.Hkv, a.B);
     if (gaps) { // decisions through the skip kernel's rule, nothing executed, no partials
-        hipLaunchKernelGGL((decode_gqa_kernel<D, true, false, false, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, true, false, 0, true>), grid, dim3(256), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.page_table)
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, true, false>), grid, dim3(256), 0, stream, a);
+    if (a.page_table && a.page_shift >= 6)
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 2, false>), grid, dim3(256), 0, stream, a);
+    else if (a.page_table)
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 1, false>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, false, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 0, false>), grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1)
         return e;
