@@ -122,7 +122,9 @@ def test_parity_gqa_decode_148_sequences_sampled():
     S, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=0.01)
     _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=S)
     lam, reached = lambda_for(gap0, 0.7)
-    units = [(0, 0), (17, 3), (63, 7), (100, 5), (147, 2), (147, 7)]
+    # every KV head of 16 sequences spread over the batch (first and last included): 128 of 1184 units
+    seqs = [0, 9, 17, 28, 37, 46, 55, 63, 74, 83, 92, 100, 111, 120, 133, 147]
+    units = [(b, g) for b in seqs for g in range(8)]
     cnt, _ = _run(q, kc, vc, lens, lam=lam, splits=S, what="148x32/8x32768x128", unit_mask=units)
     assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
 
@@ -357,7 +359,7 @@ def test_sink_seed_gqa_decode_148_sequences_sampled():
     S, _ = bl.blasst_decode_plan(q, kc, vc, lens, lam=0.01)
     _, _, gap0, _ = gpu_decode(q, kc, vc, lens, lam=0.0, num_splits=S, sink_seed=True)
     lam, reached = lambda_for(gap0, 0.7)
-    units = [(0, 0), (63, 7), (147, 2)]
+    units = [(b, g) for b in (0, 37, 63, 100, 147) for g in range(8)]  # 40 of 1184 units
     cnt, _ = _run(q, kc, vc, lens, lam=lam, splits=S, what="148x32/8x32768x128 sink seed", unit_mask=units,
                   sink_seed=True)
     assert abs(cnt[1] / cnt[0] - reached) <= SPARSITY_ABS
