@@ -152,7 +152,7 @@ blasst_status blasst_prefill_gaps(const blasst_prefill_params *p, void *hip_stre
  *   k_cache [B, Hkv, Lmax, dqk] bf16         v_cache [B, Hkv, Lmax, dv] bf16
  *   seq_lens: device int32 [B], each in 1..Lmax (the kernel clamps other
  *             values into 0..Lmax; a length of 0 yields O = 0).
- *   Supported: (dqk = dv in {64, 128}, G in 1..16) and the latent form
+ *   Supported: (dqk = dv in {64, 128}, G in 1..64: MHA, GQA and MQA) and the latent form
  *   (dqk = 576, dv = 512, Hkv = 1, G in 1..128 -- all heads of a model, or
  *   a shard of them when heads are split across GPUs -- v aliasing k).
  *   block_k = 64.

@@ -196,7 +196,7 @@ enum DecodeKind { KIND_NONE, KIND_GQA, KIND_MLA };
 DecodeKind decode_kind(const blasst_decode_params *p)
 {
     const int64_t G = p->Hq / p->Hkv;
-    if (p->dqk == p->dv && (p->dqk == 64 || p->dqk == 128) && G <= 16)
+    if (p->dqk == p->dv && (p->dqk == 64 || p->dqk == 128) && G >= 1 && G <= 64)
         return KIND_GQA;
     if (p->dqk == 576 && p->dv == 512 && p->Hkv == 1 && G >= 1 && G <= 128)
         return KIND_MLA;
@@ -240,7 +240,7 @@ blasst_status validate_decode(const blasst_decode_params *p, const blasst_decode
     const DecodeKind kind = decode_kind(p);
     if (kind == KIND_NONE)
         return fail(BLASST_ERR_UNSUPPORTED,
-                    "decode supports dqk = dv in {64,128} with Hq/Hkv <= 16, or dqk=576, dv=512, Hkv=1, Hq <= 128");
+                    "decode supports dqk = dv in {64,128} with Hq/Hkv <= 64, or dqk=576, dv=512, Hkv=1, Hq <= 128");
     if (kind == KIND_MLA && p->v_cache.ptr != p->k_cache.ptr)
         return fail(BLASST_ERR_UNSUPPORTED, "latent decode needs v_cache to alias k_cache");
     if (p->Lmax > (int64_t)1 << 30 || p->B > 65535 || p->Hkv > 65535)

@@ -16,9 +16,10 @@
 //     memory as full 128-byte lines, where MFMA-layout register loads would
 //     take 64 bytes of 16 rows each and run the compute unit out of
 //     outstanding-miss entries at ~5.7 TB/s), reads it back into MFMA operand
-//     registers and computes S^T = K q^T (16x16x32 bf16 MFMA; the G <= 16
-//     query heads that share the KV head are the 16 columns, padded with
-//     zeros); the next batch's K copy goes out as soon as the slot is read;
+//     registers and computes S^T = K q^T (16x16x32 bf16 MFMA; the G <= 64
+//     query heads that share the KV head are the columns, in groups of 16
+//     padded with zeros, all groups on the same K operands); the next
+//     batch's K copy goes out as soon as the slot is read;
 //  2. the 4 block maxima are exchanged through LDS and every wave evaluates
 //     the 4 decisions in order.  The running max never depends on earlier
 //     decisions (a skipped block has m~ < m + ln(lambda) <= m), so the
@@ -66,10 +67,14 @@ __device__ __forceinline__ int kswz(int row) { return row & 7; }
 // PG: 0 contiguous cache; 1 paged, pages of 16 or 32 rows (a block spans
 // several pages: one id per 16-row group); 2 paged, pages of 64 rows or more
 // (a block lies in one page: one id).
-template <int D, bool SKIP, bool OUT_BF16, int PG, bool GAPS>
+// NG: 16-head column groups per wave (G <= 16 NG): every group's scores and
+// P.V reuse the same K and V operand registers.
+template <int D, bool SKIP, bool OUT_BF16, int PG, bool GAPS, int NG>
 // With d = 128 the K and V slots hold one workgroup per compute unit (one
-// wave per SIMD), so the wave may use the whole register file; otherwise two.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 64 && !GAPS ? 1 : 2, D > 64 && !GAPS ? 1 : 2)))
+// wave per SIMD), so the wave may use the whole register file; otherwise two,
+// unless several head groups need the registers.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D > 64 || NG > 1) && !GAPS ? 1 : 2,
+                                                                     (D > 64 || NG > 1) && !GAPS ? 1 : 2)))
 void decode_gqa_kernel(const DecodeArgs a)
 {
     constexpr bool PAGED = PG != 0;
@@ -88,8 +93,9 @@ void decode_gqa_kernel(const DecodeArgs a)
     // copies in flight.
     __shared__ __attribute__((aligned(1024))) char ksm[NWD * TB];
     __shared__ __attribute__((aligned(1024))) char vsm[GAPS ? 1024 : NWD * TB];
-    __shared__ float mblk[2][NWD][16];
-    __shared__ float mw_s[NWD][16], lw_s[NWD][16];
+    constexpr int NH = 16 * NG; // head slots per wave
+    __shared__ float mblk[2][NWD][NH];
+    __shared__ float mw_s[NWD][NH], lw_s[NWD][NH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -156,16 +162,18 @@ void decode_gqa_kernel(const DecodeArgs a)
     };
     char *const vt = vsm + w * TB; // this wave's V slice
 
-    // q^T as the B operand: lane (n, grp) holds q[head n][32 st + 8 grp .. +7].
-    bf16x8 qf[NS];
-    {
-        const uint16_t *qp = a.q + b * a.q_sb + (int64_t)(g * G + n) * a.q_sh;
+    // q^T as the B operand: lane (n, grp) holds q[head 16 h + n][32 st + 8 grp .. +7]
+    // for head group h (zeros for slots past G).
+    bf16x8 qf[NG][NS];
+#pragma unroll
+    for (int h = 0; h < NG; ++h) {
+        const uint16_t *qp = a.q + b * a.q_sb + (int64_t)(g * G + 16 * h + n) * a.q_sh;
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             u32x4 u = {0, 0, 0, 0};
-            if (n < G)
+            if (16 * h + n < G)
                 u = *(const u32x4 *)(qp + 32 * st + 8 * grp);
-            qf[st] = as_bf16x8(u);
+            qf[h][st] = as_bf16x8(u);
         }
     }
 
@@ -247,13 +255,17 @@ void decode_gqa_kernel(const DecodeArgs a)
     // values whose probabilities are exactly 0).
     auto copy_v = [&](int j, const int (&ids)[NID]) { copy_rows(vp, a.v_st, a.v_sb, ids, j, vt_lds, voff, false); };
 
-    f32x4 o[NDT];
+    f32x4 o[NG][NDT];
+    float m2[NG], lsum[NG], pmax[NG];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-        o[dt] = f32x4{};
-    float m2 = neg_inf();   // this wave's running max for head n (base 2)
-    float lsum = 0.f;       // this lane's partial running sum for head n
-    float pmax = neg_inf(); // exclusive prefix max of block maxima (decisions)
+    for (int h = 0; h < NG; ++h) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            o[h][dt] = f32x4{};
+        m2[h] = neg_inf();   // this wave's running max for head 16 h + n (base 2)
+        lsum[h] = 0.f;       // this lane's partial running sum for that head
+        pmax[h] = neg_inf(); // exclusive prefix max of block maxima (decisions)
+    }
     int n_skipped = 0;
 
     // Transpose-read addressing of the V^T operand (16x16x32 A layout).
@@ -274,25 +286,28 @@ void decode_gqa_kernel(const DecodeArgs a)
         wait_vmcnt<0>();
         compiler_fence();
         read_k();
-        f32x4 sc[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sc[kt] = f32x4{};
+        for (int h = 0; h < NG; ++h) {
+            f32x4 sc[4];
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
-                sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
-        }
-        float mt = neg_inf();
+            for (int kt = 0; kt < 4; ++kt) {
+                sc[kt] = f32x4{};
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = j0 * BC + 16 * kt + 4 * grp + r;
-                if (key < len && key >= klo)
-                    mt = fmaxf(mt, sc[kt][r]);
+                for (int st = 0; st < NS; ++st)
+                    sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[h][st], sc[kt]);
             }
-        mt = max_xor32(max_xor16(mt));
-        pmax = mt * a.scale_log2;
+            float mt = neg_inf();
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = j0 * BC + 16 * kt + 4 * grp + r;
+                    if (key < len && key >= klo)
+                        mt = fmaxf(mt, sc[kt][r]);
+                }
+            mt = max_xor32(max_xor16(mt));
+            pmax[h] = mt * a.scale_log2;
+        }
     }
     if (jb < je) {
         ids_take(ids_load(jb + w), pc);
@@ -321,36 +336,44 @@ void decode_gqa_kernel(const DecodeArgs a)
             if (PAGED)
                 idv = ids_load(j0 + 2 * NWD + w);
         }
-        f32x4 sc[4];
+        f32x4 sc[NG][4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sc[kt] = f32x4{};
+        for (int h = 0; h < NG; ++h)
 #pragma unroll
-            for (int st = 0; st < NS; ++st)
-                sc[kt] = mfma16(as_bf16x8(kr[kt][st]), qf[st], sc[kt]);
-        }
+            for (int kt = 0; kt < 4; ++kt) {
+                sc[h][kt] = f32x4{};
+#pragma unroll
+                for (int st = 0; st < NS; ++st)
+                    sc[h][kt] = mfma16(as_bf16x8(kr[kt][st]), qf[h][st], sc[h][kt]);
+            }
         // Mask keys outside klo .. len-1 (and the whole block if j >= je).
         const int k0 = j * BC;
         if (j >= je || k0 + BC > len || k0 < klo) {
 #pragma unroll
+            for (int h = 0; h < NG; ++h)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = k0 + 16 * kt + 4 * grp + r;
+                        if (j >= je || key >= len || key < klo)
+                            sc[h][kt][r] = neg_inf();
+                    }
+        }
+        float mt2[NG];
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+            float mt = neg_inf();
+#pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = k0 + 16 * kt + 4 * grp + r;
-                    if (j >= je || key >= len || key < klo)
-                        sc[kt][r] = neg_inf();
-                }
+                for (int r = 0; r < 4; ++r)
+                    mt = fmaxf(mt, sc[h][kt][r]);
+            mt = max_xor32(max_xor16(mt));
+            mt2[h] = mt * a.scale_log2;
+            if (grp == 0)
+                mblk[par][w][16 * h + n] = mt2[h];
         }
-        float mt = neg_inf();
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                mt = fmaxf(mt, sc[kt][r]);
-        mt = max_xor32(max_xor16(mt));
-        const float mt2 = mt * a.scale_log2;
-        if (grp == 0)
-            mblk[par][w][n] = mt2;
         lds_barrier();
 
         // Decisions of the batch, in block order, identical in every wave.
@@ -360,14 +383,22 @@ void decode_gqa_kernel(const DecodeArgs a)
         for (int i = 0; i < NWD; ++i) {
             if (j0 + i >= je)
                 break;
-            const float mb = mblk[par][i][n];
-            const bool valid_head = n < G;
-            const float dgap = (!valid_head || mb == neg_inf()) ? neg_inf() : mb - pmax;
+            bool meets = true;     // every head slot of this lane meets the test
+            float dmax = neg_inf(); // largest gap over this lane's head slots
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                const float mb = mblk[par][i][16 * h + n];
+                const bool valid_head = 16 * h + n < G;
+                const float dgap = (!valid_head || mb == neg_inf()) ? neg_inf() : mb - pmax[h];
+                meets = meets && !(dgap >= a.lnlam2);
+                dmax = fmaxf(dmax, dgap);
+                pmax[h] = fmaxf(pmax[h], mb);
+            }
             bool skip_i = false;
             if (SKIP)
-                skip_i = __all(!(dgap >= a.lnlam2)) != 0;
+                skip_i = __all(meets) != 0;
             if (want_maps) {
-                const float gg = wave_max(dgap);
+                const float gg = wave_max(dmax);
                 if (w == 0 && lane == 0) {
                     const int64_t idx = (int64_t)(b * a.Hkv + g) * a.nkb + j0 + i;
                     if (a.skip_map)
@@ -376,7 +407,6 @@ void decode_gqa_kernel(const DecodeArgs a)
                         a.gap_map[idx] = gg * 0.69314718055994531f;
                 }
             }
-            pmax = fmaxf(pmax, mb);
             if (i == w)
                 my_skip = skip_i;
             batch_skipped += skip_i ? 1 : 0;
@@ -388,30 +418,33 @@ void decode_gqa_kernel(const DecodeArgs a)
             copy_v(j, pc); // V only for an executed block
 
         if (exec) {
-            // Online-softmax update with this wave's running max.
-            const float mnew = fmaxf(m2, mt2);
-            const float msafe = mnew == neg_inf() ? 0.f : mnew;
-            const float alpha = exp2_hw(m2 - msafe);
-            float rs = 0.f;
-            bf16x8 pf[2];
+            // Online-softmax update with this wave's running max, per head group.
+            bf16x8 pf[NG][2];
 #pragma unroll
-            for (int u2 = 0; u2 < 2; ++u2) {
-                f32x8 pv;
+            for (int h = 0; h < NG; ++h) {
+                const float mnew = fmaxf(m2[h], mt2[h]);
+                const float msafe = mnew == neg_inf() ? 0.f : mnew;
+                const float alpha = exp2_hw(m2[h] - msafe);
+                float rs = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p0 = exp2_hw(__builtin_fmaf(sc[2 * u2][r], a.scale_log2, -msafe));
-                    const float p1 = exp2_hw(__builtin_fmaf(sc[2 * u2 + 1][r], a.scale_log2, -msafe));
-                    pv[r] = p0;
-                    pv[r + 4] = p1;
-                    rs += p0 + p1;
+                for (int u2 = 0; u2 < 2; ++u2) {
+                    f32x8 pv;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p0 = exp2_hw(__builtin_fmaf(sc[h][2 * u2][r], a.scale_log2, -msafe));
+                        const float p1 = exp2_hw(__builtin_fmaf(sc[h][2 * u2 + 1][r], a.scale_log2, -msafe));
+                        pv[r] = p0;
+                        pv[r + 4] = p1;
+                        rs += p0 + p1;
+                    }
+                    pf[h][u2] = cvt_bf16x8(pv);
                 }
-                pf[u2] = cvt_bf16x8(pv);
-            }
-            lsum = alpha * lsum + rs;
-            m2 = mnew;
+                lsum[h] = alpha * lsum[h] + rs;
+                m2[h] = mnew;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-                o[dt] *= alpha;
+                for (int dt = 0; dt < NDT; ++dt)
+                    o[h][dt] *= alpha;
+            }
             // The V copy is the youngest vector-memory operation (the next
             // K copy and, paged, the id load went out before it).
             wait_vmcnt<0>();
@@ -428,7 +461,9 @@ void decode_gqa_kernel(const DecodeArgs a)
                     const i16x4 x1 = lds_read_tr16(vt + rb * RB + ((c ^ dswz<DG>(rb)) * 16) + (vq & 1) * 8);
                     const u32x2 y0 = __builtin_bit_cast(u32x2, x0), y1 = __builtin_bit_cast(u32x2, x1);
                     const u32x4 va = {y0[0], y0[1], y1[0], y1[1]};
-                    o[dt] = mfma16(as_bf16x8(va), pf[u2], o[dt]);
+#pragma unroll
+                    for (int h = 0; h < NG; ++h)
+                        o[h][dt] = mfma16(as_bf16x8(va), pf[h][u2], o[h][dt]);
                 }
         }
         if (PAGED && more) {
@@ -440,32 +475,39 @@ void decode_gqa_kernel(const DecodeArgs a)
 
     // Merge the 4 wave states (log-sum-exp), then write O or the split partial.
     if (!GAPS) {
-    float l = lsum;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (grp == 0) {
-        mw_s[w][n] = m2;
-        lw_s[w][n] = l;
+#pragma unroll
+    for (int h = 0; h < NG; ++h) {
+        float l = lsum[h];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (grp == 0) {
+            mw_s[w][16 * h + n] = m2[h];
+            lw_s[w][16 * h + n] = l;
+        }
     }
-    lds_barrier();
+    // One head group at a time: stage its scaled wave accumulators as fp32
+    // [wave][head][D] (reusing the V slices), then merge them.
+    float *stage = (float *)vsm;
+#pragma unroll
+    for (int h = 0; h < NG; ++h) {
+    lds_barrier(); // the group's statistics are in; the last group's staging is consumed
     float M = neg_inf();
 #pragma unroll
     for (int i = 0; i < NWD; ++i)
-        M = fmaxf(M, mw_s[i][n]);
+        M = fmaxf(M, mw_s[i][16 * h + n]);
     const float Msafe = M == neg_inf() ? 0.f : M;
-    const float cw = exp2_hw(m2 - Msafe);
-    // Stage the scaled wave accumulators as fp32 [wave][head][D] (reuses the V slices).
-    float *stage = (float *)vsm;
+    const float cw = exp2_hw(m2[h] - Msafe);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-        *(f32x4 *)(stage + (w * 16 + n) * D + 16 * dt + 4 * grp) = o[dt] * cw;
+        *(f32x4 *)(stage + (w * 16 + n) * D + 16 * dt + 4 * grp) = o[h][dt] * cw;
     lds_barrier();
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int hd = idx / D, d = idx % D;
+    const int gh = G - 16 * h < 16 ? G - 16 * h : 16; // heads of this group
+    for (int idx = tid; idx < gh * D; idx += 256) {
+        const int hl = idx / D, d = idx % D, hd = 16 * h + hl;
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < NWD; ++i)
-            acc += stage[(i * 16 + hd) * D + d];
+            acc += stage[(i * 16 + hl) * D + d];
         float Mh = neg_inf(), lh = 0.f;
 #pragma unroll
         for (int i = 0; i < NWD; ++i)
@@ -490,6 +532,7 @@ void decode_gqa_kernel(const DecodeArgs a)
             }
         }
     }
+    } // head groups
     } // !GAPS
 
     if (tid == 0) {
@@ -614,24 +657,42 @@ hipError_t launch_combine(const DecodeArgs &a, int dv, bool out_bf16, hipStream_
 
 namespace {
 
-template <int D, bool SKIP, bool OUT_BF16>
+template <int D, int NG, bool SKIP, bool OUT_BF16>
 hipError_t launch_gqa(const DecodeArgs &a, hipStream_t stream, bool gaps)
 {
     const dim3 grid(a.num_splits, a.Hkv, a.B);
     if (gaps) { // decisions through the skip kernel's rule, nothing executed, no partials
-        hipLaunchKernelGGL((decode_gqa_kernel<D, true, false, 0, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, true, false, 0, true, NG>), grid, dim3(256), 0, stream, a);
         return hipGetLastError();
     }
     if (a.page_table && a.page_shift >= 6)
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 2, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 2, false, NG>), grid, dim3(256), 0, stream, a);
     else if (a.page_table)
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 1, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 1, false, NG>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 0, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<D, SKIP, OUT_BF16, 0, false, NG>), grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1)
         return e;
     return launch_combine(a, D, OUT_BF16, stream);
+}
+
+template <int D, int NG>
+hipError_t launch_gqa_g(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream, bool gaps)
+{
+    if (skip)
+        return out_bf16 ? launch_gqa<D, NG, true, true>(a, stream, gaps) : launch_gqa<D, NG, true, false>(a, stream, gaps);
+    return out_bf16 ? launch_gqa<D, NG, false, true>(a, stream, gaps) : launch_gqa<D, NG, false, false>(a, stream, gaps);
+}
+
+template <int D>
+hipError_t launch_gqa_d(const DecodeArgs &a, bool skip, bool out_bf16, hipStream_t stream, bool gaps)
+{
+    if (a.G <= 16)
+        return launch_gqa_g<D, 1>(a, skip, out_bf16, stream, gaps);
+    if (a.G <= 32)
+        return launch_gqa_g<D, 2>(a, skip, out_bf16, stream, gaps);
+    return launch_gqa_g<D, 4>(a, skip, out_bf16, stream, gaps);
 }
 
 } // namespace
@@ -643,21 +704,11 @@ hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool o
 {
     if (a.B == 0)
         return hipSuccess;
-    if (dqk == dv && a.G <= 16) {
-        if (dqk == 128) {
-            if (skip)
-                return out_bf16 ? launch_gqa<128, true, true>(a, stream, gaps)
-                                : launch_gqa<128, true, false>(a, stream, gaps);
-            return out_bf16 ? launch_gqa<128, false, true>(a, stream, gaps)
-                            : launch_gqa<128, false, false>(a, stream, gaps);
-        }
-        if (dqk == 64) {
-            if (skip)
-                return out_bf16 ? launch_gqa<64, true, true>(a, stream, gaps)
-                                : launch_gqa<64, true, false>(a, stream, gaps);
-            return out_bf16 ? launch_gqa<64, false, true>(a, stream, gaps)
-                            : launch_gqa<64, false, false>(a, stream, gaps);
-        }
+    if (dqk == dv && a.G >= 1 && a.G <= 64) {
+        if (dqk == 128)
+            return launch_gqa_d<128>(a, skip, out_bf16, stream, gaps);
+        if (dqk == 64)
+            return launch_gqa_d<64>(a, skip, out_bf16, stream, gaps);
     }
     if (dqk == 576 && dv == 512 && a.G >= 1 && a.G <= 128)
         return launch_mla(a, skip, out_bf16, stream, gaps);

@@ -55,7 +55,7 @@ struct DecodeArgs {
     int num_pages, page_shift;
 };
 
-// GQA/MQA/MHA decode (dqk = dv in {64, 128}, G <= 16) and latent (MLA) decode
+// GQA/MQA/MHA decode (dqk = dv in {64, 128}, G <= 64) and latent (MLA) decode
 // (dqk 576, dv 512, G 128).  The combine kernel runs when num_splits > 1.
 // gaps selects the gap pass (maps and counters only: no O, no partials).
 hipError_t launch_decode(const DecodeArgs &a, int dqk, int dv, bool skip, bool out_bf16,

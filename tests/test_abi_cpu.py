@@ -169,6 +169,17 @@ def test_decode_rejects():
     assert _decode_err(q=q, k_cache=kc, v_cache=kc, dv=512, seq_lens=torch.full((1,), 256, dtype=torch.int32)) == 2
 
 
+def test_gqa_plan_accepts_wide_groups():
+    """dqk = dv decode takes up to 64 query heads per KV head (MQA included); 65 is refused."""
+    kc = _bf16(1, 1, 4096, 128).expand(4, 1, 4096, 128)  # plan reads no memory; shapes only
+    lens = torch.full((4,), 4096, dtype=torch.int32)
+    for hq in (1, 16, 17, 32, 33, 64):
+        S, ws = bl.blasst_decode_plan(_bf16(4, hq, 128), kc, kc, lens, lam=0.01)
+        assert S >= 1 and ws == (4 * hq * S * (128 + 2) * 4 + 4 * S * 2 * 4 + 256 if S > 1 else 0)
+    assert _decode_err(q=_bf16(1, 65, 128), k_cache=_bf16(1, 1, 256, 128), v_cache=_bf16(1, 1, 256, 128),
+                       seq_lens=torch.full((1,), 256, dtype=torch.int32)) == 2
+
+
 def test_latent_plan_accepts_head_shards():
     kc = _bf16(1, 1, 4096, 576).expand(16, 1, 4096, 576)  # plan reads no memory; shapes only
     lens = torch.full((16,), 4096, dtype=torch.int32)

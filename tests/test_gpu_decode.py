@@ -74,7 +74,8 @@ def _run(q, kc, vc, lens, *, lam, splits, what, unit_mask=None, dv=None, mla=Fal
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 16])
-@pytest.mark.parametrize("d,G", [(128, 4), (64, 4), (128, 1), (128, 16), (64, 8)])
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 4), (128, 1), (128, 16), (64, 8),
+                                 (128, 32), (64, 24), (128, 40), (128, 64), (64, 64)])
 def test_parity_ragged(d, G, splits):
     B, Hkv, Lmax = 3, 2, 1000
     q, kc, vc, _ = inputs.decode_inputs(B, G * Hkv, Hkv, Lmax, d, device=DEV, seed=11 + d + G + splits)
@@ -219,7 +220,7 @@ def _gathered(pool, table, lens, Lmax):
 
 
 @pytest.mark.parametrize("P,row_major", [(16, False), (64, True), (256, False)])
-@pytest.mark.parametrize("d,G,splits", [(128, 4, 3), (64, 8, 1), (128, 16, 16)])
+@pytest.mark.parametrize("d,G,splits", [(128, 4, 3), (64, 8, 1), (128, 16, 16), (128, 40, 2), (64, 64, 3)])
 def test_paged_gqa_matches_contiguous_and_oracle(P, row_major, d, G, splits):
     B, Hkv, Lmax = 3, 2, 1000
     q, kc, vc, _ = inputs.decode_inputs(B, G * Hkv, Hkv, Lmax, d, device=DEV, seed=61 + d + G + P)

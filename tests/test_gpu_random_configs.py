@@ -53,12 +53,17 @@ def _decode_cfg(i, mla):
     lens[0] = Lmax
     # the latent head count (all 128 heads, or a shard of them) from a stream of its own
     g_mla = int(np.random.default_rng(7500 + i).choice([16, 32, 64, 100, 128]))
-    return dict(B=B, Lmax=Lmax, lens=lens, d=int(r.choice([64, 128])),
-                Hkv=1 if mla else int(r.choice([1, 2])), G=g_mla if mla else int(r.choice([1, 2, 4, 8, 16])),
-                splits=min(int(r.choice([0, 1, 2, 3, 7])), -(-Lmax // 64)),  # at most one split per block
-                window=int(r.integers(1, Lmax + 1)) if r.random() < 0.3 else 0,
-                sink_seed=bool(r.random() < 0.3), page=int(r.choice([0, 0, 16, 32, 64])),
-                target=float(r.choice([0.0, 0.4, 0.7])))
+    c = dict(B=B, Lmax=Lmax, lens=lens, d=int(r.choice([64, 128])),
+             Hkv=1 if mla else int(r.choice([1, 2])), G=g_mla if mla else int(r.choice([1, 2, 4, 8, 16])),
+             splits=min(int(r.choice([0, 1, 2, 3, 7])), -(-Lmax // 64)),  # at most one split per block
+             window=int(r.integers(1, Lmax + 1)) if r.random() < 0.3 else 0,
+             sink_seed=bool(r.random() < 0.3), page=int(r.choice([0, 0, 16, 32, 64])),
+             target=float(r.choice([0.0, 0.4, 0.7])))
+    # wide GQA/MQA groups (17..64 heads per KV head) from a stream of their own
+    wide = np.random.default_rng(7600 + i)
+    if not mla and wide.random() < 0.35:
+        c["G"] = int(wide.choice([24, 32, 40, 48, 64]))
+    return c
 
 
 def _decode_case(i, mla):
