@@ -654,6 +654,39 @@ def bench_prefill_variants(steps, warmup):
     return rows
 
 
+def bench_decode_wide(steps, warmup):
+    """GQA/MQA decode with 17..64 query heads per KV head (the kernel's 2- and
+    4-group forms) on the decode workload's input recipe, at the planner's
+    split count, at the 70% lambda and at lambda = 0.  Loaded bytes: K of
+    every visited block and V of every executed one."""
+    cases = [(64, 64, 1, 32768, 128), (64, 32, 1, 32768, 128), (32, 64, 2, 32768, 128),
+             (16, 48, 1, 65536, 128), (64, 64, 1, 32768, 64)]
+    rows = []
+    for B, Hq, Hkv, L, d in cases:
+        q, kc, vc, lens = inputs.decode_inputs(B, Hq, Hkv, L, d, n_random=8, device="cuda", seed=1002)
+        S, ws = bl.blasst_decode_plan(q, kc, vc, lens, lam=1e-3)
+        work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+        lam70 = calibrate_decode(q, kc, vc, lens, S, [0.7])[0.7][0]
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        row = {"B": B, "Hq": Hq, "Hkv": Hkv, "L": L, "d": d, "num_splits": S}
+        for leg, lam in (("s70", lam70), ("dense", 0.0)):
+            def dc(cnt=None, lam=lam):
+                return bl.blasst_decode(q, kc, vc, lens, lam=lam, num_splits=S, out=out, workspace=work,
+                                        counters=cnt)
+            tc = torch.zeros(2, dtype=torch.int64, device="cuda")  # timed calls return their counts too
+            mean_ms, _, _ = time_calls(lambda: dc(tc), steps, warmup)
+            vis, skp = counts(lambda c: dc(c))
+            loaded = (vis + (vis - skp)) * 64 * d * 2
+            row[leg] = {"us": mean_ms * 1e3, "sparsity": skp / vis, "hbm_gbps": loaded / (mean_ms * 1e-3) / 1e9}
+        log(f"decode wide {B}x{Hq}/{Hkv}x{L}x{d} S={S}: 70% {row['s70']['us']:.1f} us "
+            f"({row['s70']['hbm_gbps']:.0f} GB/s), dense {row['dense']['us']:.1f} us "
+            f"({row['dense']['hbm_gbps']:.0f} GB/s)")
+        rows.append(row)
+        del q, kc, vc, work, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def window_prefill(q, k, v, out, W, steps, warmup):
     """The same prefill with a sliding window of W keys, at the 70% lambda of
     the windowed gaps and at lambda = 0."""
@@ -745,7 +778,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "prefill_gaps", "decode70", "decode_dense",
                                        "decode_gaps", "mla70", "mla_dense", "mla_gaps", "decode_paged70",
-                                       "decode_paged_layouts", "prefill_variants",
+                                       "decode_paged_layouts", "prefill_variants", "decode_wide",
                                        "mla_paged70", "long_prefill70", "long_prefill_dense", "prefill_lengths"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -783,6 +816,9 @@ def main():
     if args.only == "prefill_variants":
         print(json.dumps({"only": args.only, "result": bench_prefill_variants(steps, warmup)}, default=str),
               flush=True)
+        return
+    if args.only == "decode_wide":
+        print(json.dumps({"only": args.only, "result": bench_decode_wide(steps, warmup)}, default=str), flush=True)
         return
     if args.only == "decode_paged_layouts":
         print(json.dumps({"only": args.only, "result": bench_paged_layouts(steps, warmup)}, default=str), flush=True)

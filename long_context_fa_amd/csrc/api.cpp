@@ -273,13 +273,14 @@ int choose_splits(const blasst_decode_params *p)
     if (p->num_splits > 0)
         return p->num_splits;
     const int64_t units = p->B * p->Hkv;
-    // GQA: two workgroups are resident per compute unit (512 on the chip);
-    // aim for >= 4096 workgroups, about eight rounds, so that the last,
-    // partly filled round is a small share of the step.  Latent decode holds
-    // one workgroup per compute unit (its K ring fills the LDS): one round of
-    // 256; more splits only add partial-result traffic.  Either way keep
-    // >= 16 blocks a split.
-    const int64_t want = decode_kind(p) == KIND_MLA ? 256 : 4096;
+    // GQA with up to 16 heads per KV head: aim for >= 4096 workgroups, about
+    // sixteen rounds of the 256 resident at d = 128, so that the last, partly
+    // filled round is a small share of the step.  Wider groups (17..64 heads)
+    // and latent decode: one round of 256.  Their workgroups carry more fixed
+    // work (the query load, one merge per 16 heads, larger partials), so more
+    // splits cost more than the balance they buy (64 x 32K MQA at 70%: 4
+    // splits 184 us, 32 splits 264 us).  Either way keep >= 16 blocks a split.
+    const int64_t want = (decode_kind(p) == KIND_MLA || p->Hq / p->Hkv > 16) ? 256 : 4096;
     int s = 1;
     while (units * s < want && nkb / (2 * s) >= 16)
         s *= 2;
