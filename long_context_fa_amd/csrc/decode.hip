@@ -476,64 +476,64 @@ void decode_gqa_kernel(const DecodeArgs a)
     // Merge the 4 wave states (log-sum-exp), then write O or the split partial.
     if (!GAPS) {
 #pragma unroll
-    for (int h = 0; h < NG; ++h) {
-        float l = lsum[h];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        if (grp == 0) {
-            mw_s[w][16 * h + n] = m2[h];
-            lw_s[w][16 * h + n] = l;
+        for (int h = 0; h < NG; ++h) {
+            float l = lsum[h];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            if (grp == 0) {
+                mw_s[w][16 * h + n] = m2[h];
+                lw_s[w][16 * h + n] = l;
+            }
         }
-    }
-    // One head group at a time: stage its scaled wave accumulators as fp32
-    // [wave][head][D] (reusing the V slices), then merge them.
-    float *stage = (float *)vsm;
+        // One head group at a time: stage its scaled wave accumulators as fp32
+        // [wave][head][D] (reusing the V slices), then merge them.
+        float *stage = (float *)vsm;
 #pragma unroll
-    for (int h = 0; h < NG; ++h) {
-    lds_barrier(); // the group's statistics are in; the last group's staging is consumed
-    float M = neg_inf();
+        for (int h = 0; h < NG; ++h) {
+            lds_barrier(); // the group's statistics are in; the last group's staging is consumed
+            float M = neg_inf();
 #pragma unroll
-    for (int i = 0; i < NWD; ++i)
-        M = fmaxf(M, mw_s[i][16 * h + n]);
-    const float Msafe = M == neg_inf() ? 0.f : M;
-    const float cw = exp2_hw(m2[h] - Msafe);
+            for (int i = 0; i < NWD; ++i)
+                M = fmaxf(M, mw_s[i][16 * h + n]);
+            const float Msafe = M == neg_inf() ? 0.f : M;
+            const float cw = exp2_hw(m2[h] - Msafe);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-        *(f32x4 *)(stage + (w * 16 + n) * D + 16 * dt + 4 * grp) = o[h][dt] * cw;
-    lds_barrier();
-    const int gh = G - 16 * h < 16 ? G - 16 * h : 16; // heads of this group
-    for (int idx = tid; idx < gh * D; idx += 256) {
-        const int hl = idx / D, d = idx % D, hd = 16 * h + hl;
-        float acc = 0.f;
+            for (int dt = 0; dt < NDT; ++dt)
+                *(f32x4 *)(stage + (w * 16 + n) * D + 16 * dt + 4 * grp) = o[h][dt] * cw;
+            lds_barrier();
+            const int gh = G - 16 * h < 16 ? G - 16 * h : 16; // heads of this group
+            for (int idx = tid; idx < gh * D; idx += 256) {
+                const int hl = idx / D, d = idx % D, hd = 16 * h + hl;
+                float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < NWD; ++i)
-            acc += stage[(i * 16 + hl) * D + d];
-        float Mh = neg_inf(), lh = 0.f;
+                for (int i = 0; i < NWD; ++i)
+                    acc += stage[(i * 16 + hl) * D + d];
+                float Mh = neg_inf(), lh = 0.f;
 #pragma unroll
-        for (int i = 0; i < NWD; ++i)
-            Mh = fmaxf(Mh, mw_s[i][hd]);
-        const float Mhs = Mh == neg_inf() ? 0.f : Mh;
+                for (int i = 0; i < NWD; ++i)
+                    Mh = fmaxf(Mh, mw_s[i][hd]);
+                const float Mhs = Mh == neg_inf() ? 0.f : Mh;
 #pragma unroll
-        for (int i = 0; i < NWD; ++i)
-            lh += lw_s[i][hd] * exp2_hw(mw_s[i][hd] - Mhs);
-        if (S == 1) {
-            const float val = lh != 0.f ? acc / lh : 0.f; // 0 when no key was seen; NaN l gives NaN
-            const int64_t off = (int64_t)b * a.o_sb + (int64_t)(g * G + hd) * a.o_sh + d;
-            if (OUT_BF16)
-                ((__bf16 *)a.o)[off] = (__bf16)val;
-            else
-                ((float *)a.o)[off] = val;
-        } else {
-            const int64_t pu = ((int64_t)(b * a.Hkv + g) * S + s) * G + hd;
-            a.part_o[pu * D + d] = acc;
-            if (d == 0) {
-                a.part_ml[2 * pu] = Mh;
-                a.part_ml[2 * pu + 1] = lh;
+                for (int i = 0; i < NWD; ++i)
+                    lh += lw_s[i][hd] * exp2_hw(mw_s[i][hd] - Mhs);
+                if (S == 1) {
+                    const float val = lh != 0.f ? acc / lh : 0.f; // 0 when no key was seen; NaN l gives NaN
+                    const int64_t off = (int64_t)b * a.o_sb + (int64_t)(g * G + hd) * a.o_sh + d;
+                    if (OUT_BF16)
+                        ((__bf16 *)a.o)[off] = (__bf16)val;
+                    else
+                        ((float *)a.o)[off] = val;
+                } else {
+                    const int64_t pu = ((int64_t)(b * a.Hkv + g) * S + s) * G + hd;
+                    a.part_o[pu * D + d] = acc;
+                    if (d == 0) {
+                        a.part_ml[2 * pu] = Mh;
+                        a.part_ml[2 * pu + 1] = lh;
+                    }
+                }
             }
         }
     }
-    } // head groups
-    } // !GAPS
 
     if (tid == 0) {
         // Blocks that no split visits: before the window (first split writes
