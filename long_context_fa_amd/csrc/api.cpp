@@ -165,6 +165,20 @@ blasst_status run_prefill(const blasst_prefill_params *p, void *hip_stream, bool
     a.gap_map = p->gap_map;
     a.counters = p->counters;
     a.win = window_arg(p->window, p->L);
+    if (p->counters) {
+        // visited blocks of each query tile, as the kernel walks them: the
+        // causal range ends at the block of the tile's last row and a window
+        // starts it at the block of its first row's lowest key
+        int64_t per_head = 0;
+        for (int64_t t = 0; t < nqt; ++t) {
+            const int64_t r0 = t * p->tile_q;
+            const int64_t last_row = std::min<int64_t>(r0 + p->tile_q, p->L) - 1;
+            const int64_t nvis = p->causal ? std::min<int64_t>(last_row / 64 + 1, nkb) : nkb;
+            const int64_t jlo = (p->causal && r0 - a.win + 1 > 0) ? (r0 - a.win + 1) / 64 : 0;
+            per_head += nvis - jlo;
+        }
+        a.visited_total = (unsigned long long)(per_head * p->B * p->Hq);
+    }
     const bool skip = p->lambda > 0.0;
     hipError_t e = blasst::launch_prefill(a, (int)p->d, p->tile_q, p->causal != 0, skip,
                                           p->o.dtype == BLASST_BF16, (hipStream_t)hip_stream, gaps);

@@ -18,6 +18,11 @@ struct PrefillArgs {
     float *gap_map;
     unsigned long long *counters;
     int win; // sliding window: query i sees keys > i - win (2^30 when there is none)
+    // (tile, block) pairs the launch visits, computed on the host: workgroup 0
+    // adds it to counters[0] once, and a workgroup adds its skipped count to
+    // counters[1] only when it skipped a block, so that a launch does not end
+    // with thousands of workgroups adding into the same two words.
+    unsigned long long visited_total;
 };
 
 // Launches the prefill kernel for (d, tile_q, causal, skip, out dtype); gaps

@@ -515,8 +515,10 @@ void prefill_kernel(const PrefillArgs a)
                 unvisited(j);
         }
         if (a.counters) {
-            atomicAdd(a.counters, (unsigned long long)(nvis - jlo));
-            atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
+            if (blockIdx.x == 0)
+                atomicAdd(a.counters, a.visited_total);
+            if (n_skipped > 0)
+                atomicAdd(a.counters + 1, (unsigned long long)n_skipped);
         }
     }
 }
