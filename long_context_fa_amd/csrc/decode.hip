@@ -142,13 +142,6 @@ void decode_gqa_kernel(const DecodeArgs a)
         return a.page_table[b * a.pt_stride + (g0 >> a.page_shift)];
     };
     auto ids_take = [&](int v, int (&ids)[NID]) {
-        if (NID == 1) {
-            int id = __builtin_amdgcn_readlane(v, 0);
-            id = id < 0 ? 0 : (id < a.num_pages ? id : a.num_pages - 1);
-            asm volatile("" : "+s"(id));
-            ids[0] = id;
-            return;
-        }
 #pragma unroll
         for (int kt = 0; kt < NID; ++kt) {
             int id = __builtin_amdgcn_readlane(v, kt);
