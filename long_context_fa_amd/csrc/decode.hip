@@ -91,7 +91,10 @@ void decode_gqa_kernel(const DecodeArgs a)
     // as fp32 staging by the final merge.  With d = 128 the 128 KB hold one
     // workgroup (4 waves) per compute unit, which keeps enough whole-line
     // copies in flight.
-    __shared__ __attribute__((aligned(1024))) char ksm[NWD * TB];
+    // The gap pass has no V slices: each wave keeps two K slots instead and
+    // copies its block two batches ahead.
+    constexpr int KS = GAPS ? 2 : 1; // K slots per wave
+    __shared__ __attribute__((aligned(1024))) char ksm[NWD * TB * KS];
     __shared__ __attribute__((aligned(1024))) char vsm[GAPS ? 1024 : NWD * TB];
     constexpr int NH = 16 * NG; // head slots per wave
     __shared__ float mblk[2][NWD][NH];
@@ -173,7 +176,7 @@ void decode_gqa_kernel(const DecodeArgs a)
     // K of block j -> this wave's K slot, row-major with the 16-byte chunks
     // XOR-swizzled by row (kswz).  Keys outside the split or past len re-read
     // row len-1 (finite; their scores are masked to -inf below).
-    char *const kt_slot = ksm + w * TB;
+    char *const kt_slot = ksm + w * KS * TB; // slot 0 (slot 1 follows it in the gap pass)
     // Tile copy (K or V): copy i moves RPI rows (1 KB).  When every row of
     // block j is a visible key (the common case), the 16 rows of a group lie
     // in one page (or one sequence) from a wave-uniform base, walked with one
@@ -227,18 +230,22 @@ void decode_gqa_kernel(const DecodeArgs a)
         }
     };
     const uint32_t kt_lds = lds_addr(kt_slot), vt_lds = lds_addr(vt);
-    auto copy_k = [&](int j, const int (&ids)[NID]) { copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_lds, koff, true); };
+    // K of block j into K slot p (p = batch parity in the gap pass, else 0)
+    auto copy_k = [&](int j, const int (&ids)[NID], int p = 0) {
+        copy_rows(kp, a.k_st, a.k_sb, ids, j, kt_lds + (uint32_t)((KS == 2 ? (p & 1) : 0) * TB), koff, true);
+    };
     // K operand of S^T = K q^T from the slot: tile kt = 16 keys, lane
     // (m = key, grp) holds K[key][32 st + 8 grp .. +7] (logical chunk
     // 4 st + grp).  The caller waits for the copy first.
     u32x4 kr[4][NS];
-    auto read_k = [&]() {
+    auto read_k = [&](int p = 0) {
+        const char *slot = kt_slot + (KS == 2 ? (p & 1) : 0) * TB;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int row = 16 * kt + n;
 #pragma unroll
             for (int st = 0; st < NS; ++st)
-                kr[kt][st] = *(const u32x4 *)(kt_slot + row * RB + (((4 * st + grp) ^ kswz(row)) * 16));
+                kr[kt][st] = *(const u32x4 *)(slot + row * RB + (((4 * st + grp) ^ kswz(row)) * 16));
         }
     };
     // The slot is refilled only once every read of it has returned.
@@ -307,6 +314,8 @@ void decode_gqa_kernel(const DecodeArgs a)
         reads_done(); // (the sink block's reads, if any)
         compiler_fence();
         copy_k(jb + w, pc);
+        if (GAPS && jb + NWD < je)
+            copy_k(jb + NWD + w, pc, 1); // the gap pass reads no page table
         idv = ids_load(jb + NWD + w);
     }
     int it = 0;
@@ -316,15 +325,23 @@ void decode_gqa_kernel(const DecodeArgs a)
         const bool more = j0 + NWD < je;
         // K of this block landed (and every older copy: V of the last
         // batch was waited for before its P.V); read it, then refill the
-        // slot with the next batch's block right away.
-        wait_vmcnt<0>();
+        // slot with the next batch's block right away.  The gap pass lets the
+        // next batch's copy (the youngest VI copies, from the last batch)
+        // stay in flight and refills the slot with the block after it.
+        if (GAPS && more)
+            wait_vmcnt<VI>();
+        else
+            wait_vmcnt<0>();
         compiler_fence();
-        read_k();
+        read_k(it);
         if (PAGED)
             ids_take(idv, pn); // the next batch's page ids (landed with this block's K)
         reads_done();
         compiler_fence();
-        if (more) {
+        if (GAPS) {
+            if (j0 + 2 * NWD < je)
+                copy_k(j0 + 2 * NWD + w, pn, it);
+        } else if (more) {
             copy_k(j0 + NWD + w, pn);
             if (PAGED)
                 idv = ids_load(j0 + 2 * NWD + w);
