@@ -74,12 +74,16 @@ def _gap_pass_decode(q, kc, vc, lens, *, lam, splits, dv=None, window=0, sink_se
 
 @pytest.mark.parametrize("layout,splits,window,sink_seed", [
     ("gqa", 1, 0, False), ("gqa", 3, 0, False), ("gqa", 3, 0, True), ("gqa", 2, 1000, False),
+    ("gqa_d64", 2, 0, False), ("gqa_g40", 3, 0, True), ("gqa_g64_d64", 1, 700, False),
     ("latent", 1, 0, False), ("latent", 4, 0, True),
 ])
 def test_decode_gap_pass(layout, splits, window, sink_seed):
     say(f"[gaps] decode {layout} splits={splits} window={window} sink_seed={sink_seed}")
-    if layout == "gqa":
-        q, kc, vc, lens = inputs.decode_inputs(3, 32, 8, 3000, 128, device=DEV, seed=950 + splits,
+    if layout.startswith("gqa"):
+        # (query heads, KV heads, d): 4 heads per KV head, or the 2- and 4-group forms
+        Hq, Hkv, d = {"gqa": (32, 8, 128), "gqa_d64": (32, 8, 64), "gqa_g40": (80, 2, 128),
+                      "gqa_g64_d64": (64, 1, 64)}[layout]
+        q, kc, vc, lens = inputs.decode_inputs(3, Hq, Hkv, 3000, d, device=DEV, seed=950 + splits,
                                                seq_lens=[3000, 1234, 1])
         dv, vv = None, None
     else:
