@@ -29,9 +29,9 @@
 //    softmax of block j, so a skipped block costs its Q.K product, its row
 //    max and its vote, and a V copy has a whole iteration to land.
 //  * Skip vote: a lane meets the test when its row does; the tile skips when
-//    every valid row of every wave does (one LDS word per wave, exchanged at
-//    the barrier that also publishes the next K tile), so the branch is
-//    uniform across the workgroup.
+//    every valid row of every wave does (one LDS byte per wave, the bytes
+//    read back as one word after the barrier that also publishes the next
+//    K tile), so the branch is uniform across the workgroup.
 //  * Base-2 arithmetic: scores are scaled by scale*log2(e) in fp32, the test
 //    compares against log2(lambda), exponentials are v_exp_f32.  The
 //    accumulator rescale is skipped when no row of the wave raised its max
@@ -97,7 +97,10 @@ void prefill_kernel(const PrefillArgs a)
 
     // K ring (2 tiles) and V ring (2 tiles).
     __shared__ __attribute__((aligned(1024))) char smem[(GAPS ? 2 : 4) * TB]; // the gap pass has no V ring
-    __shared__ int vote[2][NW];
+    // Tile votes, one byte per wave (1: every row of the wave meets the
+    // test); bytes past NW stay 1, so the tile skips when the word reads
+    // 0x01010101 -- one LDS read and one scalar compare per block.
+    __shared__ __attribute__((aligned(4))) uint8_t vote[2][4];
     __shared__ float gapw[2][NW];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -298,7 +301,7 @@ void prefill_kernel(const PrefillArgs a)
             if (SKIP) {
                 const int wall = __all(!(dgap >= a.lnlam2)); // -inf rows always meet it
                 if (lane == 0)
-                    vote[j & 1][w] = wall;
+                    vote[j & 1][w] = (uint8_t)wall;
             }
             if (want_maps) {
                 const float wg = wave_max(dgap);
@@ -403,24 +406,27 @@ void prefill_kernel(const PrefillArgs a)
     // consecutive blocks (the loop is unrolled by two), so the loop carries no
     // register copies.
     bf16x8 pprev[4];
-    bool eprev = false;
+    int eprev = 0; // block j-1 executed (a scalar 0/1, like the flags below)
     auto iter = [&](int j, f32x16(&sc)[2], float mtc, f32x16(&sn)[2], float &mtn) {
         wait_vmcnt<0>();
         lds_barrier(); // votes_j, K_{j+1}, V_{j-1} visible; iteration j-1 done everywhere
         const int par = j & 1;
         // The votes are read before the K refill is issued, so that their LDS
         // latency passes while the copies are accepted.
-        int all = 1;
-        if (SKIP) {
-#pragma unroll
-            for (int i = 0; i < NW; ++i)
-                all &= vote[par][i];
-        }
+        uint32_t votes = 0;
+        if (SKIP)
+            votes = *(const uint32_t *)&vote[par][0];
         if (j + 2 < nvis)
             copy_tile(kp, a.k_st, koff, j + 2, kbuf_l(j)); // K ring refill
-        bool skip = false;
-        if (SKIP)
-            skip = __builtin_amdgcn_readfirstlane(all) != 0; // uniform across the workgroup
+        // The decision is taken from lane 0 as a 0/1 int pinned to an SGPR,
+        // so that the skip count and the branches on it stay scalar (as a
+        // bool, the compiler kept it as a lane mask and converted it with
+        // vector instructions on every block).
+        int skip = 0;
+        if (SKIP) {
+            skip = __builtin_amdgcn_readfirstlane(votes == 0x01010101u ? 1 : 0); // uniform across the workgroup
+            asm volatile("" : "+s"(skip));
+        }
         if (want_maps && tid == 0) {
             float g = neg_inf();
 #pragma unroll
@@ -428,12 +434,12 @@ void prefill_kernel(const PrefillArgs a)
                 g = fmaxf(g, gapw[par][i]);
             const int64_t idx = ((int64_t)(b * a.Hq + h) * a.nqt + t) * a.nkb + j;
             if (a.skip_map)
-                a.skip_map[idx] = skip ? 1 : 0;
+                a.skip_map[idx] = (uint8_t)skip;
             if (a.gap_map)
                 a.gap_map[idx] = g * 0.69314718055994531f; // back to natural log
         }
-        n_skipped += skip ? 1 : 0;
-        const bool ecur = !skip;
+        n_skipped += skip;
+        const int ecur = skip ^ 1;
         if (!GAPS && ecur)
             copy_tile(vp, a.v_st, voff, j, vbuf_l(j)); // V_j only for an executed block
 
@@ -449,9 +455,11 @@ void prefill_kernel(const PrefillArgs a)
             scores(j + 1, sn, mtn); // into the other register set
             vote_block(j + 1, mtn);
         }
-        eprev = GAPS ? false : ecur;
+        eprev = GAPS ? 0 : ecur;
     };
 
+    if (NW < 4 && tid < 8 && (tid & 3) >= NW)
+        vote[tid >> 2][tid & 3] = 1; // bytes no wave writes (published by the barrier below)
     copy_tile(kp, a.k_st, koff, jlo, kbuf_l(jlo));
     if (jlo + 1 < nvis) {
         copy_tile(kp, a.k_st, koff, jlo + 1, kbuf_l(jlo + 1));
