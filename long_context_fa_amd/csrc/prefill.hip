@@ -27,7 +27,7 @@
 //  * Software pipeline with one barrier per key block: iteration j finishes
 //    the P.V product of block j-1, forms the scores of block j+1 and the
 //    softmax of block j, so a skipped block costs its Q.K product, its row
-//    max and its vote, and a V copy has a whole iteration to land.
+//    max and its vote, and a V copy has most of an iteration to land.
 //  * Skip vote: a lane meets the test when its row does; the tile skips when
 //    every valid row of every wave does (one LDS byte per wave, the bytes
 //    read back as one word after the barrier that also publishes the next
@@ -397,12 +397,12 @@ void prefill_kernel(const PrefillArgs a)
     //   K_{j+1} and (if block j-1 executed) V_{j-1} are in flight;
     //   P_{j-1} is in registers if block j-1 executed.
     // Iteration j: barrier; read the votes on block j and request K_{j+2}
-    // (no decision needed); request V_j if it executes; then O += V_{j-1}
-    // P_{j-1} (MFMA), the softmax of block j (VALU) and the scores of block
-    // j+1 (MFMA); finally vote on block j+1.  The other workgroup on the
-    // compute unit fills the matrix / vector gaps.  By the barrier of
-    // iteration j+1 the V_j and K_{j+2} copies have had a whole iteration to
-    // land.  S_j and S_{j+1} live in two register sets that alternate between
+    // (no decision needed); O += V_{j-1} P_{j-1} (MFMA) while the votes
+    // arrive; request V_j if block j executes, then its softmax (VALU) and
+    // the scores of block j+1 (MFMA); finally vote on block j+1.  The other
+    // workgroup on the compute unit fills the matrix / vector gaps.  By the
+    // barrier of iteration j+1 the V_j and K_{j+2} copies have had most of an
+    // iteration to land.  S_j and S_{j+1} live in two register sets that alternate between
     // consecutive blocks (the loop is unrolled by two), so the loop carries no
     // register copies.
     bf16x8 pprev[4];
@@ -418,10 +418,13 @@ void prefill_kernel(const PrefillArgs a)
             votes = *(const uint32_t *)&vote[par][0];
         if (j + 2 < nvis)
             copy_tile(kp, a.k_st, koff, j + 2, kbuf_l(j)); // K ring refill
-        // The decision is taken from lane 0 as a 0/1 int pinned to an SGPR,
-        // so that the skip count and the branches on it stay scalar (as a
-        // bool, the compiler kept it as a lane mask and converted it with
-        // vector instructions on every block).
+        // P.V of block j-1 first: its MFMAs cover the LDS latency of the
+        // votes.  The decision is then taken from lane 0 as a 0/1 int pinned
+        // to an SGPR, so that the skip count and the branches on it stay
+        // scalar (as a bool, the compiler kept it as a lane mask and
+        // converted it with vector instructions on every block).
+        if (!GAPS && eprev)
+            pv(j - 1, pprev); // P_{j-1} is dead afterwards
         int skip = 0;
         if (SKIP) {
             skip = __builtin_amdgcn_readfirstlane(votes == 0x01010101u ? 1 : 0); // uniform across the workgroup
@@ -446,8 +449,6 @@ void prefill_kernel(const PrefillArgs a)
         if (GAPS) {
             m2 = fmaxf(m2, mtc); // the running max, over every block
         } else {
-            if (eprev)
-                pv(j - 1, pprev); // P_{j-1} is dead afterwards
             if (ecur)
                 softmax(sc, mtc, pprev); // P_j reuses its registers
         }
