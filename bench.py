@@ -20,6 +20,9 @@ sparsity on that input.  ``value`` is the dense-equivalent throughput
     576-wide latent KV head, V = its first 512 columns, 65536 cached tokens)
     at the 70% lambda and lambda = 0: microseconds per step, GB/s on the
     loaded bytes and MFMA utilisation (the workload sits near the ridge);
+  * one GPU's share of each decode step sharded over 8 GPUs, at its real
+    shape: a 4096-token context slice of the GQA step, 16 of the latent
+    step's 128 heads;
   * the long causal prefill (B=2, Hq=32, Hkv=8, L=32768, d=128) over the
     target sparsities 30/50/70/80% and dense (with its own MFMA roofline at
     70%), and with a 4096-key sliding window at 70% and dense;
@@ -687,6 +690,72 @@ def bench_decode_wide(steps, warmup):
     return rows
 
 
+def bench_shards(steps, warmup, n_gpus=8):
+    """One GPU's share of a decode step sharded over n_gpus, at its real shape
+    (nothing runs on a second GPU):
+      * context-parallel GQA decode: the 148 x 32/8 x 32K x 128 step's cache cut
+        into n_gpus contiguous slices of 32768/n_gpus tokens; one GPU holds the
+        third slice (a strided view of the full cache, no copy) and runs the
+        split kernel and combine on it, its slice being one split of the whole
+        step (lambda calibrated to 70% on that slice).  The partials that GPU
+        would all-gather are B * Hq * (d + 2) fp32 values;
+      * head-parallel latent decode: the 16 x 128/1 x 64K step's 128 query
+        heads split n_gpus ways, each GPU taking 128/n_gpus heads with the
+        whole latent cache.
+    Microseconds per step at the 70% lambda and at lambda = 0, and GB/s on
+    the loaded bytes (K of every visited block, V of every executed one)."""
+    res = {}
+    (B, Hq, Hkv, L, d), (q, kc, vc, lens) = decode_workload()
+    Ls = L // n_gpus
+    ks, vs = kc[:, :, 2 * Ls:3 * Ls], vc[:, :, 2 * Ls:3 * Ls]
+    ls = torch.full_like(lens, Ls)
+    S, ws = bl.blasst_decode_plan(q, ks, vs, ls, lam=1e-3)
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lam70 = calibrate_decode(q, ks, vs, ls, S, [0.7])[0.7][0]
+    row = {"shape": f"{B}x{Hq}/{Hkv}x{Ls}x{d}: tokens {2 * Ls}..{3 * Ls - 1} of the {L}-token cache",
+           "num_splits": S, "allgather_bytes_per_gpu": B * Hq * (d + 2) * 4}
+    for leg, lam in (("s70", lam70), ("dense", 0.0)):
+        def dc(cnt=None, lam=lam):
+            return bl.blasst_decode(q, ks, vs, ls, lam=lam, num_splits=S, out=out, workspace=work, counters=cnt)
+        tc = torch.zeros(2, dtype=torch.int64, device="cuda")
+        mean_ms, _, _ = time_calls(lambda: dc(tc), steps, warmup)
+        vis, skp = counts(lambda c: dc(c))
+        loaded = (vis + (vis - skp)) * 64 * d * 2
+        row[leg] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis,
+                    "hbm_gbps": loaded / (mean_ms * 1e-3) / 1e9}
+    log(f"decode context shard 1/{n_gpus} ({row['shape']}, S={S}): 70% {row['s70']['us']:.1f} us "
+        f"({row['s70']['hbm_gbps']:.0f} GB/s), dense {row['dense']['us']:.1f} us ({row['dense']['hbm_gbps']:.0f} GB/s)")
+    res["gqa_context_shard"] = row
+    del q, kc, vc, ks, vs, work, out
+    torch.cuda.empty_cache()
+
+    (B, Hq, L, dqk, dv), (q, kc, lens) = mla_workload()
+    Hs = Hq // n_gpus
+    qs = q[:, :Hs]
+    S, ws = bl.blasst_decode_plan(qs, kc, kc, lens, lam=1e-3, dv=dv)
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hs, dv, dtype=torch.bfloat16, device="cuda")
+    lam70 = calibrate_decode(qs, kc, kc, lens, S, [0.7], dv=dv)[0.7][0]
+    row = {"shape": f"{B}x{Hs}/1x{L}, dqk={dqk} dv={dv}: heads 0..{Hs - 1} of {Hq}", "num_splits": S}
+    for leg, lam in (("s70", lam70), ("dense", 0.0)):
+        def mc(cnt=None, lam=lam):
+            return bl.blasst_decode(qs, kc, kc, lens, lam=lam, num_splits=S, out=out, dv=dv, workspace=work,
+                                    counters=cnt)
+        tc = torch.zeros(2, dtype=torch.int64, device="cuda")
+        mean_ms, _, _ = time_calls(lambda: mc(tc), steps, warmup)
+        vis, skp = counts(lambda c: mc(c))
+        loaded = vis * 64 * dqk * 2
+        row[leg] = {"lambda": lam, "us": mean_ms * 1e3, "sparsity": skp / vis,
+                    "hbm_gbps": loaded / (mean_ms * 1e-3) / 1e9}
+    log(f"latent decode head shard 1/{n_gpus} ({row['shape']}, S={S}): 70% {row['s70']['us']:.1f} us "
+        f"({row['s70']['hbm_gbps']:.0f} GB/s), dense {row['dense']['us']:.1f} us")
+    res["latent_head_shard"] = row
+    del q, kc, work, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def window_prefill(q, k, v, out, W, steps, warmup):
     """The same prefill with a sliding window of W keys, at the 70% lambda of
     the windowed gaps and at lambda = 0."""
@@ -778,7 +847,7 @@ def main():
     ap.add_argument("--no-calibration", action="store_true", help="skip the calibration-law study")
     ap.add_argument("--only", choices=["prefill70", "prefill_dense", "prefill_gaps", "decode70", "decode_dense",
                                        "decode_gaps", "mla70", "mla_dense", "mla_gaps", "decode_paged70",
-                                       "decode_paged_layouts", "prefill_variants", "decode_wide",
+                                       "decode_paged_layouts", "prefill_variants", "decode_wide", "decode_shards",
                                        "mla_paged70", "long_prefill70", "long_prefill_dense", "prefill_lengths"],
                     help="run one measurement only and print its numbers (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -816,6 +885,9 @@ def main():
     if args.only == "prefill_variants":
         print(json.dumps({"only": args.only, "result": bench_prefill_variants(steps, warmup)}, default=str),
               flush=True)
+        return
+    if args.only == "decode_shards":
+        print(json.dumps({"only": args.only, "result": bench_shards(steps, warmup)}, default=str), flush=True)
         return
     if args.only == "decode_wide":
         print(json.dumps({"only": args.only, "result": bench_decode_wide(steps, warmup)}, default=str), flush=True)
@@ -862,7 +934,7 @@ def main():
     }
 
     # ------------------------------------------------------------- decode
-    decode = mla = long_prefill = None
+    decode = mla = long_prefill = shards = None
     if not args.no_decode:
         oc = not args.no_cpu_baseline
         S, dres = bench_decode(steps, warmup, paged_names=("paged_s70", "paged_dense"), window=4096, seed=True,
@@ -924,6 +996,7 @@ def main():
             "cpu_oracle": mres.get("cpu_oracle"),
         }
         torch.cuda.empty_cache()
+        shards = bench_shards(steps, warmup)
         sweep, wres, lcpu = bench_long_prefill(max(2, steps // 4), max(1, warmup // 2), oracle_cpu=oc)
         r70 = next((r for r in sweep if r["target"] == 0.7), None)
         long_prefill = {
@@ -964,6 +1037,7 @@ def main():
         "prefill": prefill,
         "decode": decode,
         "mla_decode": mla,
+        "decode_shard_of_8_gpus": shards,
         "long_prefill": long_prefill,
         "calibration": calibration,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

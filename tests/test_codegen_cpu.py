@@ -53,8 +53,9 @@ def _functions(text, kname):
 
 
 def _gap_pass(mangled):
-    # the last bool template argument is the gap pass, which holds no accumulator
-    return mangled.split("EEEv")[0].endswith("Lb1")
+    # the fourth template argument (a bool) is the gap pass, which holds no accumulator
+    bools = re.findall(r"Lb([01])E", mangled)
+    return len(bools) >= 4 and bools[3] == "1"
 
 
 def test_compiler_emits_no_agpr_access(kasm):

@@ -215,6 +215,30 @@ def _equal_calls(a, b):
     assert (a[3] == b[3]).all()
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_shard_views_equal_contiguous_copies(splits):
+    """One GPU's share of a sharded decode step, passed as a strided view with
+    no copy: a context slice of the GQA cache (tokens 1024..2047 of 3000) and
+    a head slice of the latent queries (16 of 48 heads).  Each call equals
+    the same call on contiguous copies bit for bit, and the GQA slice matches
+    the oracle over that slice."""
+    q, kc, vc, _ = inputs.decode_inputs(3, 8, 2, 3000, 128, n_random=8, device=DEV, seed=150 + splits)
+    ks, vs = kc[:, :, 1024:2048], vc[:, :, 1024:2048]
+    assert not ks.is_contiguous()
+    ls = torch.full((3,), 1024, dtype=torch.int32, device=DEV)
+    _, _, gap0, _ = gpu_decode(q, ks, vs, ls, lam=0.0, num_splits=splits)
+    lam, _ = lambda_for(gap0, 0.6)
+    got = gpu_decode(q, ks, vs, ls, lam=lam, num_splits=splits)
+    _equal_calls(got, gpu_decode(q, ks.contiguous(), vs.contiguous(), ls, lam=lam, num_splits=splits))
+    _run(q, ks, vs, ls, lam=lam, splits=splits, what="GQA context slice view")
+    qm, km, _, lm = inputs.decode_inputs(2, 48, 1, 1500, 576, 512, n_random=16, mla=True, device=DEV,
+                                         seed=160 + splits)
+    qs = qm[:, 16:32]
+    assert not qs.is_contiguous()
+    got = gpu_decode(qs, km, km, lm, lam=lam, num_splits=splits, dv=512)
+    _equal_calls(got, gpu_decode(qs.contiguous(), km, km, lm, lam=lam, num_splits=splits, dv=512))
+
+
 def _gathered(pool, table, lens, Lmax):
     return oracle.gather_pages(f64(pool), table.cpu().numpy(), lens.cpu().numpy(), Lmax)
 
