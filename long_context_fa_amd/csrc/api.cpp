@@ -293,10 +293,13 @@ int choose_splits(const blasst_decode_params *p)
     // and latent decode: one round of 256.  Their workgroups carry more fixed
     // work (the query load, one merge per 16 heads, larger partials), so more
     // splits cost more than the balance they buy (64 x 32K MQA at 70%: 4
-    // splits 184 us, 32 splits 264 us).  Either way keep >= 16 blocks a split.
+    // splits 184 us, 32 splits 264 us).  Splits keep >= 64 blocks each, except
+    // that >= 16 will do while the workgroups do not yet fill one round: a
+    // workgroup's fixed work outweighs the balance that shorter splits buy
+    // (148 x 32/8 x 4096 at 70%: 1 split 250 us, 4 splits 273 us).
     const int64_t want = (decode_kind(p) == KIND_MLA || p->Hq / p->Hkv > 16) ? 256 : 4096;
     int s = 1;
-    while (units * s < want && nkb / (2 * s) >= 16)
+    while (units * s < want && (nkb / (2 * s) >= 64 || (units * s < 256 && nkb / (2 * s) >= 16)))
         s *= 2;
     return s;
 }
